@@ -1,0 +1,10 @@
+"""fp64 CPU oracle for 3D-RoPE full / Skiparse attention.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the
+benchmark's CPU-baseline leg, never by the HIP library or its binding.
+"""
+from .core import (MODES, attn3d, latent_grid, rope3d, skiparse_groups,
+                     skiparse_index, softmax_attention, video_coords)
+
+__all__ = ["MODES", "attn3d", "latent_grid", "rope3d", "skiparse_groups",
+           "skiparse_index", "softmax_attention", "video_coords"]

@@ -1,0 +1,241 @@
+"""Plain fp64 CPU oracle for 3D-RoPE full and Skiparse attention (forward).
+
+TEST INFRASTRUCTURE ONLY.  This module is the independent definition that the
+HIP library is checked against.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it; the library never does, and this
+module shares no code, table or helper with the library.
+
+Every step is the plain definition, written out in float64 with numpy:
+no tiling, no online softmax, no fused loaders.  Each function names the
+passage it follows.  Sources (web pages):
+
+* "Open-Sora Plan: Open-Source Large Video Generation Model" (paper summary
+  page), sections 2.2.1 "Model Overview" and 2.2.2 "Skiparse Attention".
+* "CogVideoX: Text-to-Video Diffusion Models with an Expert Transformer",
+  section 2 (architecture overview), section 2.2 paragraphs "Patchify",
+  "3D-RoPE" and "3D Full Attention", section 3.1 and Appendix A (position
+  extrapolation), reference [14] (RoFormer).
+* "Open Video Models" (book chapter), section "The Mathematics" (latent size
+  of a causal video VAE).
+
+Readings taken where the pages are silent (all listed with reasons in the
+design notes):
+
+1. the latent grid is unfolded row-major over (t, h, w), w fastest;
+2. the head dimension is split into channel chunks [t | h | w];
+3. rotation pairs are adjacent channels (2r, 2r+1), as in RoFormer;
+4. within an axis chunk of size d_a, pair r turns at omega_r = theta^(-2r/d_a);
+5. positions are the integer latent indices (plus optional offsets), used
+   unscaled (extrapolation, not interpolation);
+6. text tokens sit in front of the video tokens and are not rotated;
+7. the softmax scale defaults to 1/sqrt(D);
+8. Single Skip subsequence j = tokens whose index is j mod k;
+9. Group Skip subsequence j = tokens whose group index floor(i/k) is j mod k
+   (groups of k adjacent tokens);
+10. subsequences keep increasing token order and are listed by j;
+11. every token keeps its own (t, h, w) under Skiparse (RoPE acts per token
+    before the regrouping).
+
+Parity status: grid arithmetic, rotation and attention are pinned by closed
+forms, invariants, a library routine and brute force (tests/test_oracle_*.py).
+The two readings that no page value can fix -- the RoPE channel order/pairing
+(readings 2-3) and the Group Skip group size (reading 9) -- are "parity
+unpinned" against any outside implementation: the pages print no example.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+MODES = ("full", "skiparse_single", "skiparse_group")
+
+
+# --------------------------------------------------------------------------
+# Latent grid (row a1)
+# --------------------------------------------------------------------------
+def latent_grid(frames: int, height: int, width: int, c_t: int, c_s: int,
+                p_t: int = 1, p_s: int = 2) -> tuple:
+    """Latent token grid of a clip.
+
+    "Open Video Models", "The Mathematics": a causal video VAE maps T frames
+    of H x W to T' = (T-1)/c_t + 1, H' = H/c_s, W' = W/c_s.  CogVideoX
+    section 2.2 "Patchify": patchify by q in time and p in space gives a
+    sequence of (T/q)(H/p)(W/p) tokens; Open-Sora Plan section 2.2.1 uses a
+    1x2x2 kernel with matching stride.  Non-integral sizes are rejected.
+    """
+    if (frames - 1) % c_t or height % c_s or width % c_s:
+        raise ValueError("clip size not divisible by the VAE compression")
+    t_lat = (frames - 1) // c_t + 1
+    h_lat = height // c_s
+    w_lat = width // c_s
+    if t_lat % p_t or h_lat % p_s or w_lat % p_s:
+        raise ValueError("latent size not divisible by the patch size")
+    return (t_lat // p_t, h_lat // p_s, w_lat // p_s)
+
+
+def video_coords(grid) -> np.ndarray:
+    """(t, h, w) of every video token, in sequence order: shape [T*H*W, 3].
+
+    CogVideoX section 2: the patchified latent is unfolded into one long
+    sequence.  Reading 1: row-major unfold, w fastest.
+    """
+    t, h, w = grid
+    return np.indices((t, h, w)).reshape(3, -1).T.astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# 3D RoPE (row a2)
+# --------------------------------------------------------------------------
+def rope3d(x: np.ndarray, grid, n_text: int, rope_split, theta: float = 1e4,
+           pos_offset=(0, 0, 0)) -> np.ndarray:
+    """Rotate channel pairs of x ([B, N, H, D], float64) by 3D RoPE.
+
+    CogVideoX section 2.2 "3D-RoPE": each latent has a 3D coordinate and 1D
+    RoPE is applied independently per coordinate on its own share of the
+    channels; the three encodings are concatenated along the channel axis.
+    RoFormer (reference [14]): a channel pair (x_a, x_b) at position m is
+    rotated by the angle m * omega_r, giving (x_a cos - x_b sin,
+    x_a sin + x_b cos).  Text tokens (the first ``n_text`` rows, CogVideoX
+    section 2) are returned unchanged.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if sum(rope_split) != d or any(s % 2 for s in rope_split):
+        raise ValueError("rope split must be even chunks summing to head_dim")
+    n_video = int(np.prod(grid))
+    if x.shape[1] != n_text + n_video:
+        raise ValueError("sequence length does not match the grid")
+    coords = video_coords(grid) + np.asarray(pos_offset, dtype=np.int64)[None, :]
+    out = x.copy()
+    c0 = 0
+    for axis, d_a in enumerate(rope_split):
+        if d_a == 0:
+            continue
+        r = np.arange(d_a // 2, dtype=np.float64)
+        omega = theta ** (-2.0 * r / d_a)                       # [d_a/2]
+        phi = coords[:, axis].astype(np.float64)[:, None] * omega[None, :]
+        cos = np.cos(phi)[None, :, None, :]                      # [1, Nv, 1, d_a/2]
+        sin = np.sin(phi)[None, :, None, :]
+        xa = x[:, n_text:, :, c0 + 0:c0 + d_a:2]
+        xb = x[:, n_text:, :, c0 + 1:c0 + d_a:2]
+        out[:, n_text:, :, c0 + 0:c0 + d_a:2] = xa * cos - xb * sin
+        out[:, n_text:, :, c0 + 1:c0 + d_a:2] = xa * sin + xb * cos
+        c0 += d_a
+    return out
+
+
+# --------------------------------------------------------------------------
+# Skiparse regrouping (row a3)
+# --------------------------------------------------------------------------
+def skiparse_groups(mode: str, k: int, n: int) -> list:
+    """Token indices of each subsequence, by membership predicate.
+
+    Open-Sora Plan section 2.2.2: a Skiparse step cuts the attended sequence
+    to 1/k of its length and multiplies the batch by k.  Single Skip takes
+    every k-th token (reading 8); Group Skip gathers groups of adjacent
+    tokens whose groups lie k-1 groups apart (reading 9, group size k).  The
+    section assumes the length divides evenly; we require it.
+    """
+    idx = np.arange(n, dtype=np.int64)
+    if mode == "full":
+        return [idx]
+    if k < 1:
+        raise ValueError("sparse ratio must be >= 1")
+    if mode == "skiparse_single":
+        if n % k:
+            raise ValueError("single skip needs N divisible by k")
+        key = idx % k
+    elif mode == "skiparse_group":
+        if n % (k * k):
+            raise ValueError("group skip needs N divisible by k*k")
+        key = (idx // k) % k
+    else:
+        raise ValueError(f"unknown mode {mode!r}")
+    return [np.nonzero(key == j)[0] for j in range(k)]
+
+
+def skiparse_index(mode: str, k: int, n: int):
+    """perm[r'] = token at regrouped position r' (subsequences by j, each in
+    increasing token order; reading 10); inv is its inverse permutation."""
+    perm = np.concatenate(skiparse_groups(mode, k, n)).astype(np.int64)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(n, dtype=np.int64)
+    return perm.astype(np.int32), inv.astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# Attention (rows a4-a7)
+# --------------------------------------------------------------------------
+def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                      sm_scale: float):
+    """softmax(sm_scale * q k^T) v for one sequence, plus log-sum-exp.
+
+    CogVideoX section 2.2 "3D Full Attention": every token attends to every
+    other token of the (text + video) sequence; FlashAttention computes this
+    exactly.  q: [M, D], k, v: [L, D].  Returns o [M, D], lse [M] (natural
+    log of the softmax denominator of the scaled logits).
+    """
+    s = sm_scale * (q @ k.T)                  # [M, L]
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ v) / l
+    lse = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def attn3d(q, k, v, *, grid, n_text: int = 0, mode: str = "full",
+           sparse_k: int = 1, rope_split, theta: float = 1e4,
+           sm_scale: float | None = None, pos_offset=(0, 0, 0),
+           rope: bool = True, rows=None, block: int = 2048):
+    """3D-RoPE attention over [B, N, H, D] float64 inputs.
+
+    Steps, in the pages' order: rotate Q and K by 3D RoPE (Open-Sora Plan
+    2.2.1, CogVideoX 2.2 "3D-RoPE"); split the sequence into subsequences
+    (one for full attention, k for Skiparse, Open-Sora Plan 2.2.2); attend
+    within each subsequence (CogVideoX 2.2 "3D Full Attention"); write each
+    output row back at its token's original position.
+
+    ``rows``: optional sorted token indices; then only those query rows are
+    computed and o has shape [B, len(rows), H, D], lse [B, H, len(rows)].
+    ``rope=False`` takes q and k as already rotated.
+    Skiparse with text tokens is rejected (reading: Open-Sora Plan feeds text
+    through cross-attention, so its Skiparse self-attention has none).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b_sz, n, h_sz, d = q.shape
+    if n != n_text + int(np.prod(grid)):
+        raise ValueError("sequence length does not match the grid")
+    if mode != "full" and n_text:
+        raise ValueError("Skiparse takes no text tokens")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if rope:
+        q = rope3d(q, grid, n_text, rope_split, theta, pos_offset)
+        k = rope3d(k, grid, n_text, rope_split, theta, pos_offset)
+    groups = skiparse_groups(mode, sparse_k, n)
+    if rows is None:
+        out_rows = np.arange(n, dtype=np.int64)
+    else:
+        out_rows = np.asarray(rows, dtype=np.int64)
+    where = {int(t): i for i, t in enumerate(out_rows)}
+    o = np.full((b_sz, len(out_rows), h_sz, d), np.nan)
+    lse = np.full((b_sz, h_sz, len(out_rows)), np.nan)
+    for g in groups:
+        wanted = g[np.isin(g, out_rows)]
+        if wanted.size == 0:
+            continue
+        dst = np.array([where[int(t)] for t in wanted], dtype=np.int64)
+        for b in range(b_sz):
+            for h in range(h_sz):
+                kk = k[b, g, h, :]
+                vv = v[b, g, h, :]
+                for s0 in range(0, wanted.size, block):
+                    sel = wanted[s0:s0 + block]
+                    ob, lb = softmax_attention(q[b, sel, h, :], kk, vv, sm_scale)
+                    o[b, dst[s0:s0 + block], h, :] = ob
+                    lse[b, h, dst[s0:s0 + block]] = lb
+    return o, lse

@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs for 3D-RoPE full / Skiparse attention.
+
+This module is shared by the test suite, the benchmark and the oracle's
+checks.  It holds no arithmetic of the method itself: it only lists the
+workload shapes (raw clip sizes, compression factors, heads, head_dim, RoPE
+split) and draws seeded Gaussian tensors, rounded to bfloat16.  Turning a clip
+size into a latent grid, rotating, regrouping and attending are done separately
+by the oracle and by the HIP library.
+
+Workloads (clip sizes from the pages; latent-grid arithmetic is done elsewhere):
+
+* ``tiny``   -- a 5x8x8 latent grid (the grid is given directly), 2 heads, D=64.
+* ``osp480`` -- Open-Sora Plan's 93-frame 480p clip (640 wide), 4x8x8 VAE,
+  1x2x2 patchify, 24 heads, D=96, inputs scaled by 1/sqrt(96) before rounding.
+* ``cogvideox`` -- CogVideoX's 49-frame 480x720 clip, 4x8x8 VAE, 2x2 patchify,
+  226 text tokens in front, 48 heads, D=64.
+* ``osp480_skiparse`` -- ``osp480``'s tensors with Skiparse k=4 (single and
+  group).
+* ``osp720`` -- 93-frame 720x1280 clip, 24 heads, D=96, full and k=4; checked
+  on 256 seeded query rows.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    # raw clip (frames, height, width) and compression; ``grid`` set instead
+    # when the workload is specified directly as a latent grid
+    clip: tuple | None
+    c_t: int
+    c_s: int
+    p_t: int
+    p_s: int
+    grid: tuple | None
+    n_text: int
+    batch: int
+    heads: int
+    head_dim: int
+    rope_split: tuple
+    theta: float
+    input_scale: float | None
+    seed: int
+    modes: tuple
+    sparse_k: int
+    sample_rows: int | None = None
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", None, 4, 8, 1, 2, (5, 8, 8), 0, 1, 2, 64,
+                     (16, 24, 24), 1e4, None, 0,
+                     ("full", "skiparse_single", "skiparse_group"), 4),
+    "osp480": Workload("osp480", (93, 480, 640), 4, 8, 1, 2, None, 0, 1, 24, 96,
+                       (32, 32, 32), 1e4, 1.0 / math.sqrt(96.0), 1,
+                       ("full",), 1),
+    "cogvideox": Workload("cogvideox", (49, 480, 720), 4, 8, 1, 2, None, 226, 1,
+                          48, 64, (16, 24, 24), 1e4, None, 2, ("full",), 1),
+    "osp480_skiparse": Workload("osp480_skiparse", (93, 480, 640), 4, 8, 1, 2,
+                                None, 0, 1, 24, 96, (32, 32, 32), 1e4,
+                                1.0 / math.sqrt(96.0), 1,
+                                ("skiparse_single", "skiparse_group"), 4),
+    "osp720": Workload("osp720", (93, 720, 1280), 4, 8, 1, 2, None, 0, 1, 24, 96,
+                       (32, 32, 32), 1e4, None, 4,
+                       ("full", "skiparse_single", "skiparse_group"), 4,
+                       sample_rows=256),
+}
+
+
+def gaussian_bf16(seed, tensor_id: int, shape, scale: float | None = None,
+                  mult: float | None = None) -> torch.Tensor:
+    """Draw N(0,1) fp32 with ``default_rng([seed, tensor_id])``, optionally
+    multiply by ``scale`` and ``mult`` in fp32, round to bfloat16 (RNE).
+
+    ``seed`` may be an int or a tuple of ints (extra entries select variants).
+    Returns a CPU bfloat16 tensor.
+    """
+    key = list(seed) if isinstance(seed, (tuple, list)) else [int(seed)]
+    rng = np.random.default_rng(key + [int(tensor_id)])
+    x = rng.standard_normal(tuple(shape), dtype=np.float32)
+    if scale is not None:
+        x *= np.float32(scale)
+    if mult is not None:
+        x *= np.float32(mult)
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
+def make_qkv(seed, shape, scale: float | None = None, q_mult: float | None = None):
+    """Q, K, V as bf16 CPU tensors of ``shape`` = [B, N, H, D] (tensor ids 0/1/2)."""
+    q = gaussian_bf16(seed, 0, shape, scale, q_mult)
+    k = gaussian_bf16(seed, 1, shape, scale)
+    v = gaussian_bf16(seed, 2, shape, scale)
+    return q, k, v
+
+
+def sample_rows(seed: int, n_tokens: int, count: int) -> np.ndarray:
+    """Sorted, distinct query rows drawn with ``default_rng([seed, 99])``."""
+    rng = np.random.default_rng([int(seed), 99])
+    return np.sort(rng.choice(n_tokens, size=min(count, n_tokens), replace=False)).astype(np.int64)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact upcast of a bf16 tensor to a float64 numpy array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
