@@ -1,0 +1,216 @@
+"""Benchmark: 3D-RoPE attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+latent grid of the clip, 3D RoPE fused into the loaders, full attention over
+all tokens, output scattered back in token order -- one osp_attn3d_fwd call
+on the Open-Sora-Plan-shaped 93x480p workload (grid 24x30x40 = 28,800 tokens,
+batch 1, 24 heads, head_dim 96).  Inputs are resident in HBM before timing.
+
+Prints ONE JSON line.  value = algorithmic attention TFLOP/s
+(4*B*H*N^2*D / k per call).  Also reported: the same kernel on Skiparse k=4
+(single and group skip), the roofline of the attention kernel (MFMA bound,
+dense bf16 peak 2516.6 TFLOP/s), HBM traffic from rocprofv3 counters (when
+taken on the current kernel source) and the fp64 CPU oracle's rate on a
+bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+KERNEL_SRC = os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", "attn3d_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn3d_fwd_osp480_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("attn3d_fwd.hip", "osp_rope.hpp", "osp_common.hpp", "osp_internal.hpp"):
+        with open(os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-skiparse", action="store_true", help="skip the Skiparse k=4 lines")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-heads", type=int, default=2,
+                   help="heads of the workload the oracle times (all query rows each)")
+    p.add_argument("--profile", action="store_true",
+                   help="few launches of the full-attention step only (for rocprofv3)")
+    p.add_argument("--copy", type=int, default=0,
+                   help="instead: time a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(each attention unit (batch, head, subsequence) is independent; "
+              "see the sharding notes in the design document)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import spatiotemporal_attention_amd as osp
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    if args.copy:
+        n = args.copy * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_mib": args.copy, "bytes_read": n * 4, "bytes_written": n * 4}))
+        return
+
+    wl = workloads.WORKLOADS["osp480"]
+    grid = osp.osp_latent_grid(*wl.clip, wl.c_t, wl.c_s, wl.p_t, wl.p_s)      # row a1 on the host
+    n_tok = wl.n_text + grid[0] * grid[1] * grid[2]
+    B, H, D = wl.batch, wl.heads, wl.head_dim
+    shape = (B, n_tok, H, D)
+    q, k, v = (t.to(dev) for t in workloads.make_qkv(wl.seed, shape, wl.input_scale))
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(mode="full", sk=1):
+        osp.osp_attn3d_fwd(q, k, v, grid=grid, n_text=wl.n_text, mode=mode, sparse_k=sk,
+                           rope_split=wl.rope_split, theta=wl.theta, fuse_rope=True, out=o)
+
+    def flops(sk=1):
+        return 4.0 * B * H * float(n_tok) ** 2 * D / sk
+
+    if args.profile:
+        for _ in range(max(args.warmup, 1)):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(max(args.steps, 1)):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_launches": args.steps, "workload": "osp480 full"}))
+        return
+
+    def timed(mode, sk, steps, warmup):
+        for _ in range(warmup):
+            step(mode, sk)
+        torch.cuda.synchronize()
+        # per-launch events on the launch stream (the kernel's own duration)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        t0.record(stream)
+        for e0, e1 in evs:
+            e0.record(stream)
+            step(mode, sk)
+            e1.record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+        total_ms = t0.elapsed_time(t1)
+        per = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+        return total_ms / steps, sum(per) / len(per), per[len(per) // 2], per[0], wall
+
+    ms_step, ms_launch, ms_med, ms_min, wall = timed("full", 1, args.steps, args.warmup)
+    f_full = flops(1)
+    value = f_full / (ms_step * 1e-3) / 1e12
+    achieved = f_full / (ms_launch * 1e-3) / 1e12
+    traffic = load_traffic()
+
+    extra = {}
+    if not args.no_skiparse:
+        for mode in ("skiparse_single", "skiparse_group"):
+            s_step, s_launch, s_med, s_min, _ = timed(mode, 4, max(args.steps, 5), args.warmup)
+            tf = flops(4) / (s_launch * 1e-3) / 1e12
+            extra[mode] = {"k": 4, "ms_per_launch": round(s_launch, 4), "ms_min": round(s_min, 4),
+                           "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                           "dense_equiv_tflops": round(f_full / (s_launch * 1e-3) / 1e12, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nh = max(1, min(args.cpu_heads, H))
+        hs = slice(0, nh)
+        cpu_in = [workloads.to_f64(t[:, :, hs].cpu()) for t in (q, k, v)]
+        t_c = time.perf_counter()
+        oracle.attn3d(*cpu_in, grid=grid, n_text=wl.n_text, rope_split=wl.rope_split,
+                      theta=wl.theta)
+        dt = time.perf_counter() - t_c
+        cores = torch.get_num_threads()
+        try:
+            import threadpoolctl
+            info = threadpoolctl.threadpool_info()
+            cores = max([i.get("num_threads", 0) for i in info if i.get("user_api") == "blas"] or [cores])
+        except Exception:  # noqa: BLE001 -- reporting only
+            pass
+        cpu = {"value": round(4.0 * B * nh * float(n_tok) ** 2 * D / dt / 1e12, 5),
+               "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"fp64 numpy oracle, full attention with 3D RoPE over all {n_tok} query "
+                         f"rows of {nh} of {H} heads ({dt:.1f} s)"}
+
+    line = {
+        "metric": "attention TFLOP/s and % of bf16 MFMA peak at 28,800 tokens, full vs Skiparse k=4",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "osp480 full attention: 93x480x640 clip, 4x8x8 VAE, 1x2x2 patchify "
+                               f"-> grid {grid[0]}x{grid[1]}x{grid[2]} = {n_tok} tokens, batch {B}, "
+                               f"{H} heads, head_dim {D}, fused 3D RoPE {wl.rope_split}",
+                   "global_batch": B, "seq_len": n_tok, "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "attn3d_fwd_kernel<96,...,rope=1>",
+                     "flop_per_launch": f_full, "ms_per_launch": round(ms_launch, 4),
+                     "ms_median": round(ms_med, 4), "ms_min": round(ms_min, 4)},
+        "skiparse": extra,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

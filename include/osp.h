@@ -1,0 +1,152 @@
+/*
+ * osp.h -- C ABI of libosp: 3D-RoPE full and Skiparse attention (forward)
+ * for video diffusion transformers, on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources are web pages; sections named per function):
+ *   - A video clip's latent grid after a causal VAE and patchify
+ *     ("Open Video Models", section "The Mathematics"; CogVideoX section 2.2
+ *     "Patchify"; Open-Sora Plan section 2.2.1).
+ *   - 3D RoPE on the query and key of every video token (CogVideoX section 2.2
+ *     "3D-RoPE"; Open-Sora Plan section 2.2.1; RoFormer, CogVideoX ref. [14]).
+ *   - Attention over the whole [text | video] sequence (CogVideoX section 2.2
+ *     "3D Full Attention"), or within the k subsequences of a Skiparse step
+ *     (Open-Sora Plan section 2.2.2 "Skiparse Attention").
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are bfloat16, logically [B, N, H, D] (batch, token, head,
+ *     channel), channel stride 1; batch/token/head strides are given in
+ *     elements (0 selects the contiguous value).  Token order: n_text text
+ *     tokens first, then the T x H' x W' video tokens unfolded row-major
+ *     (t slowest, w fastest).
+ *   - The head dimension is split into channel chunks [rope_t | rope_h |
+ *     rope_w]; within a chunk of size d_a, channel pair (2r, 2r+1) is
+ *     rotated by the angle pos_a * theta^(-2r/d_a), where pos_a is the
+ *     token's integer latent coordinate on that axis plus pos_*0.  Text
+ *     tokens are not rotated.
+ *   - All memory is owned by the caller; device pointers must stay valid
+ *     until the enqueued work has finished.  The library allocates no device
+ *     memory and keeps no state besides a thread-local error string.
+ *   - Device work is enqueued on the caller's hipStream_t (NULL = the null
+ *     stream) and the call returns without waiting.
+ *   - Every argument is checked on the host before anything is enqueued; on
+ *     error nothing is written or enqueued, the call returns a status code
+ *     and osp_last_error() describes the problem.  No call aborts, asserts or
+ *     throws across this interface.
+ */
+#ifndef OSP_H
+#define OSP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OSP_ABI_VERSION 1
+
+typedef enum {
+  OSP_OK = 0,
+  OSP_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  OSP_ERR_SHAPE = 2,       /* sizes inconsistent or not divisible            */
+  OSP_ERR_PARAM = 3,       /* a scalar parameter is out of range             */
+  OSP_ERR_UNSUPPORTED = 4, /* valid, but not implemented (e.g. head_dim)     */
+  OSP_ERR_DEVICE = 5       /* the HIP runtime reported an error at launch    */
+} osp_status;
+
+typedef enum {
+  OSP_MODE_FULL = 0,             /* every token attends to every token       */
+  OSP_MODE_SKIPARSE_SINGLE = 1,  /* subsequence j = tokens i with i mod k = j */
+  OSP_MODE_SKIPARSE_GROUP = 2    /* subsequence j = tokens i with
+                                    floor(i/k) mod k = j (groups of k
+                                    adjacent tokens, k-1 groups apart)       */
+} osp_mode;
+
+/* flags of osp_attn3d_fwd */
+#define OSP_FUSE_ROPE 1  /* rotate Q and K inside the attention loaders;
+                            without it Q and K are taken as already rotated */
+
+/* Shape, layout and RoPE settings of one attention call. */
+typedef struct {
+  int32_t batch;                    /* B >= 1                                  */
+  int32_t n_text;                   /* text tokens in front, >= 0              */
+  int32_t grid_t, grid_h, grid_w;   /* latent video grid, each >= 1            */
+  int32_t heads;                    /* H >= 1                                  */
+  int32_t head_dim;                 /* D: 64, 96 or 128                        */
+  int32_t rope_t, rope_h, rope_w;   /* channel chunk per axis: even, >= 0,
+                                       sum == head_dim                         */
+  int32_t pos_t0, pos_h0, pos_w0;   /* added to every latent coordinate       */
+  float rope_theta;                 /* RoPE base, finite and > 0               */
+  int64_t stride_b, stride_n, stride_h;    /* Q, K, V (and rope3d input)       */
+  int64_t ostride_b, ostride_n, ostride_h; /* O (and rope3d output)            */
+} osp_attn3d_desc;
+
+/* ABI version compiled into the library (OSP_ABI_VERSION). */
+int32_t osp_abi_version(void);
+
+/* Static text for a status code. */
+const char* osp_status_string(osp_status s);
+
+/* Text describing the last failure on the calling thread ("" if none).
+   The pointer stays valid until the next libosp call on the same thread. */
+const char* osp_last_error(void);
+
+/* Latent token grid of a clip ("Open Video Models", "The Mathematics":
+   T' = (T-1)/c_t + 1, H' = H/c_s, W' = W/c_s; then divided by the patch
+   size p_t x p_s x p_s, CogVideoX section 2.2 "Patchify").  Host only.
+   grid_out[3] receives (T'/p_t, H'/p_s, W'/p_s).  OSP_ERR_SHAPE if a size
+   does not divide exactly, OSP_ERR_PARAM for non-positive arguments. */
+osp_status osp_latent_grid(int32_t frames, int32_t height, int32_t width,
+                           int32_t c_t, int32_t c_s, int32_t p_t, int32_t p_s,
+                           int32_t* grid_out);
+
+/* Host-only check of a call to osp_attn3d_fwd with these settings (no
+   pointers involved): returns what osp_attn3d_fwd would return for valid,
+   aligned pointers. */
+osp_status osp_attn3d_check(const osp_attn3d_desc* desc, int32_t mode,
+                            int32_t sparse_k, int32_t flags);
+
+/* 3D RoPE (CogVideoX section 2.2 "3D-RoPE"): y = rotate(x) for every
+   [b, n, h] row; text rows are copied unchanged.  x is read with the
+   desc stride_*, y is written with ostride_*; y == x (same strides) works in
+   place.  Rotation in fp32, result rounded to bf16 (round to nearest even).
+   Pointers 16-byte aligned, strides multiples of 8. */
+osp_status osp_rope3d(const osp_attn3d_desc* desc, const void* x, void* y,
+                      void* stream);
+
+/* Attention forward.
+   mode: osp_mode.  sparse_k: Skiparse ratio k >= 1 (ignored for FULL);
+   Skiparse (Open-Sora Plan section 2.2.2) needs N divisible by k (single)
+   or by k*k (group), and n_text == 0 (else OSP_ERR_UNSUPPORTED); k == 1
+   equals full attention.  The k subsequences are attended independently
+   and each output row is written back at its token's original position.
+   sm_scale: logit scale; <= 0 selects 1/sqrt(head_dim).
+   flags: OSP_FUSE_ROPE rotates Q and K in the loaders (exactly as
+   osp_rope3d would, then bf16), otherwise Q and K must already be rotated.
+   q, k, v: [B, N, H, D] bf16 read with stride_*; o: written with ostride_*,
+   must not overlap q, k or v.  lse: NULL, or [B, H, N] fp32 contiguous,
+   receives ln(sum_j exp(sm_scale * q_i . k_j)) over the row's subsequence,
+   at the original token position.
+   Arithmetic: bf16 MFMA products with fp32 accumulation, fp32 online
+   softmax; probabilities rounded to bf16 for the second product; output
+   rounded to bf16.  Pointers 16-byte aligned, strides multiples of 8. */
+osp_status osp_attn3d_fwd(const osp_attn3d_desc* desc, int32_t mode,
+                          int32_t sparse_k, float sm_scale, int32_t flags,
+                          const void* q, const void* k, const void* v, void* o,
+                          float* lse, void* stream);
+
+/* Skiparse index maps of an N-token sequence (Open-Sora Plan section 2.2.2).
+   perm[j*L + r] = token at row r of subsequence j (L = N/k; rows in
+   increasing token order); inv[token] = its regrouped position.  FULL (or
+   k == 1) gives the identity.  Either of perm/inv may be NULL, not both.
+   on_device == 0: perm/inv are host arrays, filled before returning
+   (stream ignored).  on_device != 0: they are device arrays, filled by a
+   kernel enqueued on stream.  OSP_ERR_SHAPE if N does not divide. */
+osp_status osp_skiparse_index(int32_t mode, int32_t sparse_k, int64_t n_tokens,
+                              int32_t* perm, int32_t* inv, int32_t on_device,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSP_H */

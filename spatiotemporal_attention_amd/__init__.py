@@ -1,0 +1,208 @@
+"""Python binding of libosp: 3D-RoPE full / Skiparse attention on MI355X.
+
+Argument marshalling only: every step runs in the HIP library
+(``libosp.so``, built by ``python -m spatiotemporal_attention_amd.build``).
+The functions carry the names of the C entry points in include/osp.h.
+Tensors are torch bfloat16 [B, N, H, D] with unit channel stride; device
+work goes on torch's current stream of the tensor's device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libosp.so")
+
+MODES = {"full": 0, "skiparse_single": 1, "skiparse_group": 2}
+OSP_FUSE_ROPE = 1
+ABI_VERSION = 1
+
+
+class OspError(RuntimeError):
+    """A libosp call returned a non-zero status."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"libosp status {code}: {message}")
+        self.code = code
+        self.message = message
+
+
+class OspAttn3dDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_text", ctypes.c_int32),
+        ("grid_t", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+        ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("rope_t", ctypes.c_int32), ("rope_h", ctypes.c_int32), ("rope_w", ctypes.c_int32),
+        ("pos_t0", ctypes.c_int32), ("pos_h0", ctypes.c_int32), ("pos_w0", ctypes.c_int32),
+        ("rope_theta", ctypes.c_float),
+        ("stride_b", ctypes.c_int64), ("stride_n", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+        ("ostride_b", ctypes.c_int64), ("ostride_n", ctypes.c_int64), ("ostride_h", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libosp.so once; raise loudly if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m spatiotemporal_attention_amd.build` (there is no fallback)")
+        h = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        D = ctypes.POINTER(OspAttn3dDesc)
+        sig = {
+            "osp_abi_version": (I32, []),
+            "osp_status_string": (ctypes.c_char_p, [I32]),
+            "osp_last_error": (ctypes.c_char_p, []),
+            "osp_latent_grid": (I32, [I32, I32, I32, I32, I32, I32, I32, ctypes.POINTER(I32)]),
+            "osp_attn3d_check": (I32, [D, I32, I32, I32]),
+            "osp_rope3d": (I32, [D, P, P, P]),
+            "osp_attn3d_fwd": (I32, [D, I32, I32, F32, I32, P, P, P, P, P, P]),
+            "osp_skiparse_index": (I32, [I32, I32, I64, P, P, I32, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        if h.osp_abi_version() != ABI_VERSION:
+            raise RuntimeError("libosp ABI version mismatch; rebuild the library")
+        _lib = h
+    return _lib
+
+
+EXPORTED = ("osp_abi_version", "osp_status_string", "osp_last_error", "osp_latent_grid",
+            "osp_attn3d_check", "osp_rope3d", "osp_attn3d_fwd", "osp_skiparse_index")
+
+
+def _check(status: int):
+    if status != 0:
+        raise OspError(status, lib().osp_last_error().decode())
+
+
+def _mode(mode) -> int:
+    if isinstance(mode, str):
+        if mode not in MODES:
+            raise ValueError(f"unknown mode {mode!r}")
+        return MODES[mode]
+    return int(mode)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def osp_abi_version() -> int:
+    return int(lib().osp_abi_version())
+
+
+def osp_latent_grid(frames: int, height: int, width: int, c_t: int, c_s: int,
+                    p_t: int = 1, p_s: int = 2) -> tuple:
+    """Latent token grid (T, H, W) of a clip after the VAE and patchify."""
+    out = (ctypes.c_int32 * 3)()
+    _check(lib().osp_latent_grid(frames, height, width, c_t, c_s, p_t, p_s, out))
+    return (out[0], out[1], out[2])
+
+
+def make_desc(*, batch: int, n_text: int, grid, heads: int, head_dim: int, rope_split,
+              theta: float = 1e4, pos_offset=(0, 0, 0), strides=(0, 0, 0),
+              ostrides=(0, 0, 0)) -> OspAttn3dDesc:
+    d = OspAttn3dDesc()
+    d.batch, d.n_text = batch, n_text
+    d.grid_t, d.grid_h, d.grid_w = grid
+    d.heads, d.head_dim = heads, head_dim
+    d.rope_t, d.rope_h, d.rope_w = rope_split
+    d.pos_t0, d.pos_h0, d.pos_w0 = pos_offset
+    d.rope_theta = theta
+    d.stride_b, d.stride_n, d.stride_h = strides
+    d.ostride_b, d.ostride_n, d.ostride_h = ostrides
+    return d
+
+
+def _bnhd(t: torch.Tensor, name: str):
+    if t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be a bf16 [B, N, H, D] tensor with unit channel stride")
+    return tuple(t.stride()[:3])
+
+
+def osp_attn3d_check(desc: OspAttn3dDesc, mode="full", sparse_k: int = 1,
+                     flags: int = OSP_FUSE_ROPE) -> None:
+    """Host-only argument check; raises OspError where osp_attn3d_fwd would."""
+    _check(lib().osp_attn3d_check(ctypes.byref(desc), _mode(mode), sparse_k, flags))
+
+
+def osp_rope3d(x: torch.Tensor, *, grid, n_text: int = 0, rope_split, theta: float = 1e4,
+               pos_offset=(0, 0, 0), out: torch.Tensor | None = None) -> torch.Tensor:
+    """3D RoPE of x ([B, N, H, D] bf16 on the GPU); out may be x (in place)."""
+    if out is None:
+        out = torch.empty_like(x)
+    b, n, h, d = x.shape
+    desc = make_desc(batch=b, n_text=n_text, grid=grid, heads=h, head_dim=d,
+                     rope_split=rope_split, theta=theta, pos_offset=pos_offset,
+                     strides=_bnhd(x, "x"), ostrides=_bnhd(out, "out"))
+    if tuple(out.shape) != tuple(x.shape):
+        raise ValueError("out must have the shape of x")
+    _check(lib().osp_rope3d(ctypes.byref(desc), ctypes.c_void_p(x.data_ptr()),
+                            ctypes.c_void_p(out.data_ptr()), _stream(x)))
+    return out
+
+
+def osp_attn3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid,
+                   n_text: int = 0, mode="full", sparse_k: int = 1, rope_split,
+                   theta: float = 1e4, sm_scale: float | None = None,
+                   fuse_rope: bool = True, pos_offset=(0, 0, 0),
+                   out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                   return_lse: bool = False):
+    """Attention forward over [B, N, H, D] bf16 q, k, v on the GPU.
+
+    Returns o (and lse [B, H, N] fp32 when return_lse or lse is given)."""
+    b, n, h, d = q.shape
+    st = _bnhd(q, "q")
+    if _bnhd(k, "k") != st or _bnhd(v, "v") != st or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must share shape and strides")
+    if out is None:
+        out = torch.empty((b, n, h, d), dtype=torch.bfloat16, device=q.device)
+    if tuple(out.shape) != (b, n, h, d):
+        raise ValueError("out must have the shape of q")
+    if lse is None and return_lse:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (b, h, n)
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    desc = make_desc(batch=b, n_text=n_text, grid=grid, heads=h, head_dim=d,
+                     rope_split=rope_split, theta=theta, pos_offset=pos_offset,
+                     strides=st, ostrides=_bnhd(out, "out"))
+    flags = OSP_FUSE_ROPE if fuse_rope else 0
+    _check(lib().osp_attn3d_fwd(
+        ctypes.byref(desc), _mode(mode), int(sparse_k),
+        float(sm_scale) if sm_scale is not None else 0.0, flags,
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+        ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), _stream(q)))
+    return (out, lse) if lse is not None else out
+
+
+def osp_skiparse_index(mode, sparse_k: int, n_tokens: int, device=None):
+    """(perm, inv) int32 maps.  device=None: numpy arrays filled by the
+    library's host path; else torch tensors filled by its device kernel."""
+    m = _mode(mode)
+    if device is None:
+        perm = np.empty(n_tokens, dtype=np.int32)
+        inv = np.empty(n_tokens, dtype=np.int32)
+        _check(lib().osp_skiparse_index(
+            m, int(sparse_k), int(n_tokens), perm.ctypes.data_as(ctypes.c_void_p),
+            inv.ctypes.data_as(ctypes.c_void_p), 0, None))
+        return perm, inv
+    perm = torch.empty(n_tokens, dtype=torch.int32, device=device)
+    inv = torch.empty(n_tokens, dtype=torch.int32, device=device)
+    _check(lib().osp_skiparse_index(
+        m, int(sparse_k), int(n_tokens), ctypes.c_void_p(perm.data_ptr()),
+        ctypes.c_void_p(inv.data_ptr()), 1, _stream(perm)))
+    return perm, inv

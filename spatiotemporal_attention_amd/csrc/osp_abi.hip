@@ -1,0 +1,291 @@
+// osp_abi.hip -- the extern "C" entry points of libosp (declared in
+// include/osp.h): argument checks, descriptor -> kernel arguments, launch.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/osp.h"
+#include "osp_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+osp_status fail(osp_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+osp_status ok() {
+  g_last_error.clear();
+  return OSP_OK;
+}
+
+osp_status device_error(hipError_t e, const char* what) {
+  return fail(OSP_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Resolved geometry of a descriptor.
+struct Shape {
+  int64_t n_tokens;
+  int64_t sb, sn, sh, osb, osn, osh;
+};
+
+// Checks shared by rope3d and attention.  attn: head_dim must be one the
+// attention kernel is built for.
+osp_status check_desc(const osp_attn3d_desc* d, bool attn, Shape* out) {
+  if (!d) return fail(OSP_ERR_NULL, "desc is NULL");
+  if (d->batch < 1 || d->heads < 1)
+    return fail(OSP_ERR_PARAM, "batch (%d) and heads (%d) must be >= 1", d->batch, d->heads);
+  if (d->grid_t < 1 || d->grid_h < 1 || d->grid_w < 1)
+    return fail(OSP_ERR_PARAM, "grid %dx%dx%d: every extent must be >= 1", d->grid_t, d->grid_h,
+                d->grid_w);
+  if (d->n_text < 0) return fail(OSP_ERR_PARAM, "n_text (%d) must be >= 0", d->n_text);
+  const int D = d->head_dim;
+  if (attn) {
+    if (D != 64 && D != 96 && D != 128)
+      return fail(OSP_ERR_UNSUPPORTED, "head_dim %d: attention supports 64, 96 and 128", D);
+  } else if (D < 8 || D > 128 || D % 8) {
+    return fail(OSP_ERR_UNSUPPORTED, "head_dim %d: rope3d supports multiples of 8 up to 128", D);
+  }
+  const int32_t rs[3] = {d->rope_t, d->rope_h, d->rope_w};
+  for (int a = 0; a < 3; ++a)
+    if (rs[a] < 0 || rs[a] % 2)
+      return fail(OSP_ERR_PARAM, "rope chunk %d (%d) must be even and >= 0", a, rs[a]);
+  if (int64_t(rs[0]) + rs[1] + rs[2] != D)
+    return fail(OSP_ERR_PARAM, "rope chunks %d+%d+%d must sum to head_dim %d", rs[0], rs[1],
+                rs[2], D);
+  if (!(d->rope_theta > 0.f) || !isfinite(d->rope_theta))
+    return fail(OSP_ERR_PARAM, "rope_theta must be finite and > 0");
+  const int64_t video = int64_t(d->grid_t) * d->grid_h * d->grid_w;
+  const int64_t n = int64_t(d->n_text) + video;
+  if (n > 0x7fffffffLL)
+    return fail(OSP_ERR_SHAPE, "sequence of %lld tokens exceeds 2^31-1", (long long)n);
+  if (int64_t(d->grid_h) * d->grid_w > 0x7fffffffLL)
+    return fail(OSP_ERR_SHAPE, "grid_h*grid_w exceeds 2^31-1");
+  const int64_t hd = int64_t(d->heads) * D;
+  Shape s;
+  s.n_tokens = n;
+  s.sb = d->stride_b ? d->stride_b : n * hd;
+  s.sn = d->stride_n ? d->stride_n : hd;
+  s.sh = d->stride_h ? d->stride_h : D;
+  s.osb = d->ostride_b ? d->ostride_b : n * hd;
+  s.osn = d->ostride_n ? d->ostride_n : hd;
+  s.osh = d->ostride_h ? d->ostride_h : D;
+  const int64_t st[6] = {s.sb, s.sn, s.sh, s.osb, s.osn, s.osh};
+  for (int i = 0; i < 6; ++i)
+    if (st[i] < 0 || st[i] % 8)
+      return fail(OSP_ERR_PARAM, "stride %lld must be >= 0 and a multiple of 8 elements",
+                  (long long)st[i]);
+  *out = s;
+  return OSP_OK;
+}
+
+void fill_rope(const osp_attn3d_desc* d, osp::RopeGeom* g) {
+  *g = osp::RopeGeom{};
+  g->n_text = d->n_text;
+  const int32_t rs[3] = {d->rope_t, d->rope_h, d->rope_w};
+  const int32_t grid[3] = {d->grid_t, d->grid_h, d->grid_w};
+  g->np0 = rs[0] / 2;
+  g->np1 = rs[1] / 2;
+  g->np2 = rs[2] / 2;
+  g->pos0_t = d->pos_t0;
+  g->pos0_h = d->pos_h0;
+  g->pos0_w = d->pos_w0;
+  const int64_t e0 = int64_t(grid[0]) * g->np0, e1 = int64_t(grid[1]) * g->np1,
+                e2 = int64_t(grid[2]) * g->np2;
+  const bool fits = (e0 + e1 + e2) <= osp::kMaxTableEntries;
+  g->off1 = fits ? int32_t(e0) : 0;
+  g->off2 = fits ? int32_t(e0 + e1) : 0;
+  g->tab_entries = fits ? int32_t(e0 + e1 + e2) : 0;
+  g->aligned8 = (rs[0] % 8 == 0 && rs[1] % 8 == 0 && rs[2] % 8 == 0) ? 1 : 0;
+  int p = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int r = 0; r < rs[a] / 2; ++r)   // omega_r = theta^(-2r/d_a), in double
+      g->omega[p++] = float(pow(double(d->rope_theta), -2.0 * r / double(rs[a])));
+  g->div_hw = osp::make_fastdiv(uint32_t(d->grid_h) * uint32_t(d->grid_w));
+  g->div_w = osp::make_fastdiv(uint32_t(d->grid_w));
+}
+
+osp_status check_mode(const osp_attn3d_desc* d, int64_t n, int32_t mode, int32_t k) {
+  if (mode < OSP_MODE_FULL || mode > OSP_MODE_SKIPARSE_GROUP)
+    return fail(OSP_ERR_PARAM, "unknown mode %d", mode);
+  if (mode == OSP_MODE_FULL) return OSP_OK;
+  if (k < 1) return fail(OSP_ERR_PARAM, "sparse_k (%d) must be >= 1", k);
+  if (d && d->n_text != 0)
+    return fail(OSP_ERR_UNSUPPORTED, "Skiparse takes no text tokens (n_text = %d)", d->n_text);
+  const int64_t div = (mode == OSP_MODE_SKIPARSE_SINGLE) ? int64_t(k) : int64_t(k) * k;
+  if (n % div)
+    return fail(OSP_ERR_SHAPE, "%s skip needs N (%lld) divisible by %lld",
+                mode == OSP_MODE_SKIPARSE_SINGLE ? "single" : "group", (long long)n,
+                (long long)div);
+  return OSP_OK;
+}
+
+osp_status check_attn(const osp_attn3d_desc* d, int32_t mode, int32_t k, int32_t flags,
+                      Shape* s) {
+  osp_status st = check_desc(d, true, s);
+  if (st) return st;
+  if (flags & ~int32_t(OSP_FUSE_ROPE)) return fail(OSP_ERR_PARAM, "unknown flags 0x%x", flags);
+  st = check_mode(d, s->n_tokens, mode, k);
+  if (st) return st;
+  const int64_t groups = (mode == OSP_MODE_FULL) ? 1 : k;
+  const int64_t len = s->n_tokens / groups;
+  const int64_t bm = osp::attn_rows_per_block(d->head_dim);
+  const int64_t tiles = int64_t(d->batch) * d->heads * groups * ((len + bm - 1) / bm);
+  if (tiles > 0x7fffffffLL) return fail(OSP_ERR_SHAPE, "too many tiles (%lld)", (long long)tiles);
+  return OSP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t osp_abi_version(void) { return OSP_ABI_VERSION; }
+
+const char* osp_status_string(osp_status s) {
+  switch (s) {
+    case OSP_OK: return "ok";
+    case OSP_ERR_NULL: return "null pointer";
+    case OSP_ERR_SHAPE: return "inconsistent or indivisible shape";
+    case OSP_ERR_PARAM: return "parameter out of range";
+    case OSP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case OSP_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* osp_last_error(void) { return g_last_error.c_str(); }
+
+osp_status osp_latent_grid(int32_t frames, int32_t height, int32_t width, int32_t c_t,
+                           int32_t c_s, int32_t p_t, int32_t p_s, int32_t* grid_out) {
+  if (!grid_out) return fail(OSP_ERR_NULL, "grid_out is NULL");
+  if (frames < 1 || height < 1 || width < 1 || c_t < 1 || c_s < 1 || p_t < 1 || p_s < 1)
+    return fail(OSP_ERR_PARAM, "sizes and factors must be >= 1");
+  if ((frames - 1) % c_t || height % c_s || width % c_s)
+    return fail(OSP_ERR_SHAPE, "clip %dx%dx%d not divisible by VAE factors %d/%d", frames,
+                height, width, c_t, c_s);
+  const int32_t t = (frames - 1) / c_t + 1, h = height / c_s, w = width / c_s;
+  if (t % p_t || h % p_s || w % p_s)
+    return fail(OSP_ERR_SHAPE, "latent %dx%dx%d not divisible by patch %dx%dx%d", t, h, w, p_t,
+                p_s, p_s);
+  grid_out[0] = t / p_t;
+  grid_out[1] = h / p_s;
+  grid_out[2] = w / p_s;
+  return ok();
+}
+
+osp_status osp_attn3d_check(const osp_attn3d_desc* desc, int32_t mode, int32_t sparse_k,
+                            int32_t flags) {
+  Shape s;
+  osp_status st = check_attn(desc, mode, sparse_k, flags, &s);
+  return st ? st : ok();
+}
+
+osp_status osp_rope3d(const osp_attn3d_desc* desc, const void* x, void* y, void* stream) {
+  Shape s;
+  osp_status st = check_desc(desc, false, &s);
+  if (st) return st;
+  if (!x || !y) return fail(OSP_ERR_NULL, "x and y must be non-NULL");
+  if (!aligned16(x) || !aligned16(y)) return fail(OSP_ERR_PARAM, "x and y must be 16-byte aligned");
+  osp::RopeArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.y = static_cast<uint16_t*>(y);
+  a.sb = s.sb; a.sn = s.sn; a.sh = s.sh;
+  a.osb = s.osb; a.osn = s.osn; a.osh = s.osh;
+  a.batch = desc->batch;
+  a.n_tokens = int32_t(s.n_tokens);
+  a.heads = desc->heads;
+  a.head_dim = desc->head_dim;
+  fill_rope(desc, &a.rope);
+  const uint64_t total = uint64_t(a.batch) * uint64_t(a.n_tokens) * uint64_t(a.heads) *
+                         uint64_t(a.head_dim / 8);
+  if (total > 0xffffffffull - 2048ull * 256ull)
+    return fail(OSP_ERR_SHAPE, "tensor too large for one rope3d call");
+  hipError_t e = osp::launch_rope3d(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "rope3d launch");
+  return ok();
+}
+
+osp_status osp_attn3d_fwd(const osp_attn3d_desc* desc, int32_t mode, int32_t sparse_k,
+                          float sm_scale, int32_t flags, const void* q, const void* k,
+                          const void* v, void* o, float* lse, void* stream) {
+  Shape s;
+  osp_status st = check_attn(desc, mode, sparse_k, flags, &s);
+  if (st) return st;
+  if (!q || !k || !v || !o) return fail(OSP_ERR_NULL, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(OSP_ERR_PARAM, "q, k, v and o must be 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(OSP_ERR_PARAM, "lse must be 4-byte aligned");
+  if (isnan(sm_scale) || isinf(sm_scale)) return fail(OSP_ERR_PARAM, "sm_scale must be finite");
+  const int D = desc->head_dim;
+  const double scale = sm_scale > 0.f ? double(sm_scale) : 1.0 / sqrt(double(D));
+  const int32_t groups = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
+  osp::AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.sb = s.sb; a.sn = s.sn; a.sh = s.sh;
+  a.osb = s.osb; a.osn = s.osn; a.osh = s.osh;
+  a.batch = desc->batch;
+  a.heads = desc->heads;
+  a.n_tokens = int32_t(s.n_tokens);
+  a.groups = groups;
+  a.seq_len = int32_t(s.n_tokens / groups);
+  a.mode = mode;
+  a.divk = osp::make_fastdiv(uint32_t(groups));
+  a.scale_log2 = float(scale * 1.4426950408889634);
+  const int bm = osp::attn_rows_per_block(D);
+  a.q_tiles = (a.seq_len + bm - 1) / bm;
+  a.total_tiles = a.batch * a.heads * groups * a.q_tiles;
+  fill_rope(desc, &a.rope);
+  if (a.total_tiles == 0) return ok();
+  // rotation in the loaders: fast path when every axis chunk is a multiple
+  // of 8 channels and the cos/sin table fits in LDS, else the general path
+  const int rope_kind = !(flags & OSP_FUSE_ROPE) ? 0
+                        : (a.rope.aligned8 && a.rope.tab_entries) ? 1 : 2;
+  hipError_t e = osp::launch_attn3d(a, D, rope_kind, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "attn3d_fwd launch");
+  return ok();
+}
+
+osp_status osp_skiparse_index(int32_t mode, int32_t sparse_k, int64_t n_tokens, int32_t* perm,
+                              int32_t* inv, int32_t on_device, void* stream) {
+  if (!perm && !inv) return fail(OSP_ERR_NULL, "perm and inv are both NULL");
+  if (n_tokens < 0 || n_tokens > 0x7fffffffLL)
+    return fail(OSP_ERR_SHAPE, "n_tokens %lld out of range", (long long)n_tokens);
+  osp_status st = check_mode(nullptr, n_tokens, mode, sparse_k);
+  if (st) return st;
+  const int32_t n = int32_t(n_tokens);
+  const int32_t k = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
+  if (on_device) {
+    hipError_t e = osp::launch_skiparse_index(mode, k, n, perm, inv,
+                                              static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_error(e, "skiparse_index launch");
+    return ok();
+  }
+  const osp::FastDiv divk = osp::make_fastdiv(uint32_t(k));
+  const uint32_t len = uint32_t(n / k);
+  for (uint32_t j = 0; j < uint32_t(k); ++j)
+    for (uint32_t r = 0; r < len; ++r) {
+      const uint32_t pos = j * len + r;
+      const uint32_t i = osp::skiparse_token(mode, r, j, divk);
+      if (perm) perm[pos] = int32_t(i);
+      if (inv) inv[i] = int32_t(pos);
+    }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+"""libosp loads without a GPU, exports every symbol include/osp.h declares,
+and rejects bad arguments on the host before any device work.  CPU only:
+no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import spatiotemporal_attention_amd as osp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, PARAM, UNSUP, DEVICE = range(6)
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "osp.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(osp_[a-z_0-9]+)\(",
+                                 text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = osp.lib()
+    names = header_functions()
+    assert "osp_attn3d_fwd" in names and len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(osp.EXPORTED) == names
+    assert osp.osp_abi_version() == 1
+
+
+def test_status_strings():
+    lib = osp.lib()
+    for code in range(6):
+        assert lib.osp_status_string(code)
+    assert b"unknown" in lib.osp_status_string(99)
+
+
+def test_latent_grid_matches_oracle_and_rejects():
+    cases = [((93, 480, 640), 4, 8, 1, 2), ((49, 480, 720), 4, 8, 1, 2),
+             ((93, 720, 1280), 4, 8, 1, 2), ((121, 576, 1024), 8, 8, 1, 2),
+             ((1, 256, 256), 4, 8, 1, 2), ((21, 64, 64), 4, 8, 2, 1)]
+    for clip, ct, cs, pt, ps in cases:
+        assert osp.osp_latent_grid(*clip, ct, cs, pt, ps) == oracle.latent_grid(*clip, ct, cs, pt, ps)
+    for clip in ((94, 480, 640), (93, 484, 640), (93, 488, 640)):
+        with pytest.raises(osp.OspError) as e:
+            osp.osp_latent_grid(*clip, 4, 8)
+        assert e.value.code == SHAPE
+    with pytest.raises(osp.OspError) as e:
+        osp.osp_latent_grid(0, 480, 640, 4, 8)
+    assert e.value.code == PARAM
+
+
+def _desc(**kw):
+    base = dict(batch=1, n_text=0, grid=(5, 8, 8), heads=2, head_dim=64, rope_split=(16, 24, 24))
+    base.update(kw)
+    return osp.make_desc(**base)
+
+
+def _code(desc, mode="full", k=1, flags=1):
+    try:
+        osp.osp_attn3d_check(desc, mode, k, flags)
+        return OK
+    except osp.OspError as e:
+        assert e.message  # every failure carries a description
+        return e.code
+
+
+@pytest.mark.parametrize("kw,mode,k,flags,want", [
+    ({}, "full", 1, 1, OK),
+    ({}, "skiparse_single", 4, 1, OK),
+    ({}, "skiparse_group", 4, 1, OK),              # 320 = 20 * 16
+    ({}, "skiparse_group", 8, 1, OK),              # 320 = 5 * 64
+    ({}, "skiparse_group", 16, 1, SHAPE),          # 320 % 256 != 0
+    ({}, "skiparse_single", 3, 1, SHAPE),          # 320 % 3 != 0
+    ({}, "skiparse_single", 0, 1, PARAM),
+    ({}, 7, 1, 1, PARAM),
+    ({}, "full", 1, 4, PARAM),                     # unknown flag bit
+    ({"n_text": 2, "grid": (2, 3, 53)}, "skiparse_single", 2, 1, UNSUP),
+    ({"n_text": 226, "grid": (13, 30, 45), "heads": 48}, "full", 1, 1, OK),
+    ({"head_dim": 80, "rope_split": (16, 32, 32)}, "full", 1, 1, UNSUP),
+    ({"head_dim": 96, "rope_split": (32, 32, 32)}, "full", 1, 1, OK),
+    ({"head_dim": 96, "rope_split": (36, 36, 24)}, "full", 1, 1, OK),
+    ({"head_dim": 128, "rope_split": (32, 48, 48)}, "full", 1, 1, OK),
+    ({"rope_split": (15, 25, 24)}, "full", 1, 1, PARAM),   # odd chunk
+    ({"rope_split": (16, 24, 26)}, "full", 1, 1, PARAM),   # sum != D
+    ({"rope_split": (-2, 40, 26)}, "full", 1, 1, PARAM),
+    ({"theta": 0.0}, "full", 1, 1, PARAM),
+    ({"theta": float("inf")}, "full", 1, 1, PARAM),
+    ({"batch": 0}, "full", 1, 1, PARAM),
+    ({"heads": 0}, "full", 1, 1, PARAM),
+    ({"grid": (0, 8, 8)}, "full", 1, 1, PARAM),
+    ({"n_text": -1}, "full", 1, 1, PARAM),
+    ({"grid": (2000, 2000, 1000)}, "full", 1, 1, SHAPE),   # N > 2^31 - 1
+    ({"strides": (0, 132, 0)}, "full", 1, 1, PARAM),       # not a multiple of 8
+    ({"ostrides": (0, 0, -64)}, "full", 1, 1, PARAM),
+])
+def test_attn_check_codes(kw, mode, k, flags, want):
+    assert _code(_desc(**kw), mode, k, flags) == want
+
+
+def test_null_and_alignment_errors_before_launch():
+    lib = osp.lib()
+    d = _desc()
+    fake = ctypes.c_void_p(4096)
+    assert lib.osp_attn3d_fwd(None, 0, 1, 0.0, 1, fake, fake, fake, fake, None, None) == NULL
+    assert lib.osp_attn3d_fwd(ctypes.byref(d), 0, 1, 0.0, 1, None, fake, fake, fake, None, None) == NULL
+    assert lib.osp_attn3d_fwd(ctypes.byref(d), 0, 1, 0.0, 1, ctypes.c_void_p(4098), fake, fake,
+                              fake, None, None) == PARAM
+    assert lib.osp_attn3d_fwd(ctypes.byref(d), 0, 1, 0.0, 1, fake, fake, fake, fake,
+                              ctypes.c_void_p(4098), None) == PARAM
+    assert lib.osp_attn3d_fwd(ctypes.byref(d), 0, 1, float("nan"), 1, fake, fake, fake, fake,
+                              None, None) == PARAM
+    assert b"NULL" in lib.osp_last_error() or b"finite" in lib.osp_last_error()
+    assert lib.osp_rope3d(ctypes.byref(d), None, fake, None) == NULL
+    assert lib.osp_rope3d(ctypes.byref(d), fake, ctypes.c_void_p(4104), None) == PARAM
+    d2 = _desc(head_dim=12, rope_split=(4, 4, 4))
+    assert lib.osp_rope3d(ctypes.byref(d2), fake, fake, None) == UNSUP
+    assert lib.osp_skiparse_index(1, 4, 64, None, None, 0, None) == NULL
+    buf = np.zeros(64, dtype=np.int32)
+    assert lib.osp_skiparse_index(1, 4, 66, buf.ctypes.data_as(ctypes.c_void_p), None, 0, None) == SHAPE
+    assert lib.osp_skiparse_index(2, 4, 72, buf.ctypes.data_as(ctypes.c_void_p), None, 0, None) == SHAPE
+    assert lib.osp_skiparse_index(1, 0, 64, buf.ctypes.data_as(ctypes.c_void_p), None, 0, None) == PARAM
+    assert lib.osp_skiparse_index(5, 2, 64, buf.ctypes.data_as(ctypes.c_void_p), None, 0, None) == PARAM
+    assert lib.osp_skiparse_index(1, 2, -1, buf.ctypes.data_as(ctypes.c_void_p), None, 0, None) == SHAPE
+
+
+def test_success_clears_last_error():
+    lib = osp.lib()
+    osp.osp_attn3d_check(_desc())
+    assert lib.osp_last_error() == b""

@@ -1,0 +1,220 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle,
+element by element, at sizes that span several tiles and a ragged tail;
+plus bit-exact device index maps, fused == unfused RoPE, determinism and
+fully-written outputs.  Needs an MI355X."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import spatiotemporal_attention_amd as osp
+import workloads
+from parity_util import (LSE_ABS, MAX_ABS, REL_L2, assert_parity, note, oracle_attn, qkv_for,
+                         to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    osp.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_case(seed, *, grid, n_text, heads, head_dim, rope_split, mode="full", sparse_k=1,
+             scale=None, q_mult=None, theta=1e4, sm_scale=None, pos_offset=(0, 0, 0),
+             batch=1, lse=True, fuse_rope=True, tag="", tol=1.0):
+    n = n_text + int(np.prod(grid))
+    shape = (batch, n, heads, head_dim)
+    note(f"case {tag} seed={seed} shape={shape} grid={grid} n_text={n_text} mode={mode} "
+         f"k={sparse_k} rope={rope_split} fuse={fuse_rope}")
+    cpu, (q, k, v) = qkv_for(seed, shape, scale, q_mult)
+    if not fuse_rope:
+        q = osp.osp_rope3d(q, grid=grid, n_text=n_text, rope_split=rope_split, theta=theta,
+                           pos_offset=pos_offset)
+        k = osp.osp_rope3d(k, grid=grid, n_text=n_text, rope_split=rope_split, theta=theta,
+                           pos_offset=pos_offset)
+    o, l = osp.osp_attn3d_fwd(q, k, v, grid=grid, n_text=n_text, mode=mode, sparse_k=sparse_k,
+                              rope_split=rope_split, theta=theta, sm_scale=sm_scale,
+                              pos_offset=pos_offset, fuse_rope=fuse_rope, return_lse=True)
+    torch.cuda.synchronize()
+    want_o, want_l = oracle_attn(cpu, grid=grid, n_text=n_text, mode=mode, sparse_k=sparse_k,
+                                 rope_split=rope_split, theta=theta, sm_scale=sm_scale,
+                                 pos_offset=pos_offset)
+    assert_parity(to_np(o), want_o, f"O {tag}", MAX_ABS * tol, REL_L2 * tol)
+    if lse:
+        got_l = to_np(l)
+        assert np.isfinite(got_l).all()
+        assert np.abs(got_l - want_l).max() <= LSE_ABS * tol, np.abs(got_l - want_l).max()
+    return o, l
+
+
+# ---------------------------------------------------------------- RoPE pass
+@pytest.mark.parametrize("grid,n_text,heads,d,split,offset", [
+    ((5, 8, 8), 0, 2, 64, (16, 24, 24), (0, 0, 0)),
+    ((4, 12, 15), 0, 3, 96, (32, 32, 32), (0, 0, 0)),
+    ((3, 10, 12), 37, 2, 64, (16, 24, 24), (2, -1, 5)),
+    ((3, 7, 9), 5, 2, 96, (36, 36, 24), (0, 0, 0)),      # chunks straddle 8-channel blocks
+    ((2, 6, 7), 0, 2, 128, (32, 48, 48), (0, 0, 0)),
+    ((200, 4, 80), 0, 1, 96, (32, 32, 32), (0, 0, 0)),   # cos/sin table too big: direct path
+])
+def test_rope3d_matches_oracle(grid, n_text, heads, d, split, offset):
+    n = n_text + int(np.prod(grid))
+    note(f"rope3d grid={grid} n_text={n_text} d={d} split={split}")
+    x = workloads.gaussian_bf16(5, 0, (2, n, heads, d))
+    y = osp.osp_rope3d(x.cuda(), grid=grid, n_text=n_text, rope_split=split, pos_offset=offset)
+    torch.cuda.synchronize()
+    xw = workloads.to_f64(x)
+    want = oracle.rope3d(xw, grid, n_text, split, 1e4, offset)
+    got = to_np(y)
+    bound = 2.0 ** -8 * np.abs(want) + 1e-5 * np.abs(xw).max()
+    assert (np.abs(got - want) <= bound).all(), np.abs(got - want).max()
+    assert np.array_equal(got[:, :n_text], xw[:, :n_text])    # text rows copied
+
+
+def test_rope3d_in_place_and_strided():
+    grid, split = (4, 6, 8), (16, 24, 24)
+    n = 192
+    x = workloads.gaussian_bf16(6, 0, (1, n, 3, 2, 64))    # packed [B, N, (q,k,v), H, D]
+    xd = x.cuda()
+    ref = osp.osp_rope3d(xd[:, :, 0].contiguous(), grid=grid, rope_split=split)
+    view = xd[:, :, 0]
+    osp.osp_rope3d(view, grid=grid, rope_split=split, out=view)
+    torch.cuda.synchronize()
+    assert torch.equal(xd[:, :, 0], ref)
+    assert torch.equal(xd[:, :, 1:].cpu(), x[:, :, 1:])      # neighbours untouched
+
+
+# ---------------------------------------------------------- attention, small
+def test_tiny_full():
+    run_case(0, grid=(5, 8, 8), n_text=0, heads=2, head_dim=64, rope_split=(16, 24, 24),
+             tag="tiny-full")
+
+
+@pytest.mark.parametrize("mode", ["skiparse_single", "skiparse_group"])
+@pytest.mark.parametrize("k", [1, 2, 4, 8])
+def test_tiny_skiparse(mode, k):
+    run_case(0, grid=(5, 8, 8), n_text=0, heads=2, head_dim=64, rope_split=(16, 24, 24),
+             mode=mode, sparse_k=k, tag=f"tiny-{mode}-{k}")
+
+
+@pytest.mark.parametrize("variant", ["unscaled", "literal", "sharp"])
+@pytest.mark.parametrize("mode,k", [("full", 1), ("skiparse_single", 4), ("skiparse_group", 4),
+                                    ("skiparse_group", 2)])
+def test_multitile_d96(variant, mode, k):
+    # 720 tokens: several 256-row query tiles and 64-key tiles, ragged tails.
+    # "sharp" multiplies Q by 4 (logit std ~4 instead of ~1).  The kernel
+    # rounds rotated Q and K to bf16 before the MFMA, so its logit error, and
+    # with it the output error, grows in proportion to the logit scale: the
+    # bound is the unit-scale bound times 4.
+    scale = 1 / math.sqrt(96) if variant == "literal" else None
+    q_mult = 4.0 if variant == "sharp" else None
+    run_case(10, grid=(4, 12, 15), n_text=0, heads=3, head_dim=96, rope_split=(32, 32, 32),
+             mode=mode, sparse_k=k, scale=scale, q_mult=q_mult, tag=f"mt96-{variant}-{mode}{k}",
+             tol=4.0 if variant == "sharp" else 1.0)
+
+
+def test_text_tokens_d64():
+    run_case(11, grid=(3, 10, 12), n_text=37, heads=2, head_dim=64, rope_split=(16, 24, 24),
+             tag="text-d64")
+
+
+def test_d128_and_batch2():
+    run_case(12, grid=(3, 8, 11), n_text=0, heads=2, head_dim=128, rope_split=(32, 48, 48),
+             batch=2, tag="d128-b2")
+    run_case(12, grid=(3, 8, 12), n_text=0, heads=2, head_dim=128, rope_split=(32, 48, 48),
+             mode="skiparse_single", sparse_k=3, tag="d128-single3")
+
+
+def test_unaligned_rope_split_and_offsets():
+    run_case(13, grid=(3, 7, 9), n_text=5, heads=2, head_dim=96, rope_split=(36, 36, 24),
+             pos_offset=(3, 1, -2), theta=500.0, tag="split36")
+
+
+def test_sm_scale_override():
+    run_case(14, grid=(2, 9, 10), n_text=0, heads=2, head_dim=64, rope_split=(16, 24, 24),
+             sm_scale=0.3, tag="scale0.3")
+
+
+def test_single_token_and_singleton_groups():
+    # N = 1: the output is V.  single skip with k = N: every group is one token.
+    o, _ = run_case(15, grid=(1, 1, 1), n_text=0, heads=2, head_dim=64, rope_split=(16, 24, 24),
+                    tag="n1")
+    run_case(15, grid=(1, 4, 4), n_text=0, heads=2, head_dim=64, rope_split=(16, 24, 24),
+             mode="skiparse_single", sparse_k=16, tag="k=N")
+
+
+def test_fused_equals_unfused_bitwise():
+    args = dict(grid=(4, 12, 15), n_text=0, heads=3, head_dim=96, rope_split=(32, 32, 32))
+    a, la = run_case(16, **args, tag="fused")
+    b, lb = run_case(16, **args, fuse_rope=False, tag="unfused")
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    args = dict(grid=(3, 10, 12), n_text=37, heads=2, head_dim=64, rope_split=(16, 24, 24))
+    a, _ = run_case(17, **args, tag="fused-text")
+    b, _ = run_case(17, **args, fuse_rope=False, tag="unfused-text")
+    assert torch.equal(a, b)
+
+
+def test_deterministic_and_fully_written():
+    grid, split = (4, 12, 15), (32, 32, 32)
+    _, (q, k, v) = qkv_for(18, (1, 720, 3, 96))
+    outs = []
+    for rep in range(2):
+        for mode, kk in (("full", 1), ("skiparse_group", 4)):
+            o = torch.full_like(q, float("nan"))
+            lse = torch.full((1, 3, 720), float("nan"), device=q.device)
+            note(f"determinism rep={rep} mode={mode}")
+            osp.osp_attn3d_fwd(q, k, v, grid=grid, rope_split=split, mode=mode, sparse_k=kk,
+                               out=o, lse=lse)
+            torch.cuda.synchronize()
+            assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+            outs.append((o.clone(), lse.clone()))
+    assert torch.equal(outs[0][0], outs[2][0]) and torch.equal(outs[1][0], outs[3][0])
+    assert torch.equal(outs[0][1], outs[2][1])
+
+
+def test_strided_packed_qkv():
+    grid, split = (3, 8, 10), (16, 24, 24)
+    n = 240
+    cpu = workloads.gaussian_bf16(19, 0, (1, n, 3, 2, 64))
+    qkv = cpu.cuda()
+    note("strided packed qkv")
+    o = torch.empty((1, n, 2, 64), dtype=torch.bfloat16, device="cuda")
+    osp.osp_attn3d_fwd(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], grid=grid, rope_split=split,
+                       out=o)
+    torch.cuda.synchronize()
+    f = workloads.to_f64(cpu)
+    want, _ = oracle.attn3d(f[:, :, 0], f[:, :, 1], f[:, :, 2], grid=grid, rope_split=split)
+    assert_parity(to_np(o), want, "O strided")
+
+
+def test_output_strides():
+    grid, split = (3, 8, 10), (16, 24, 24)
+    cpu, (q, k, v) = qkv_for(20, (1, 240, 2, 64))
+    big = torch.zeros((1, 240, 4, 64), dtype=torch.bfloat16, device="cuda")
+    note("output strides")
+    osp.osp_attn3d_fwd(q, k, v, grid=grid, rope_split=split, out=big[:, :, 1:3])
+    torch.cuda.synchronize()
+    want, _ = oracle_attn(cpu, grid=grid, n_text=0, mode="full", sparse_k=1, rope_split=split)
+    assert_parity(to_np(big[:, :, 1:3]), want, "O into a strided view")
+    assert not big[:, :, 0].any() and not big[:, :, 3].any()
+
+
+# ------------------------------------------------------------ index maps
+@pytest.mark.parametrize("n,k", [(320, 4), (28800, 4), (86400, 4), (720, 2), (4096, 8),
+                                 (1 << 20, 16), (17550, 3), (1, 1)])
+def test_device_index_maps_bitexact(n, k):
+    for mode in ("full", "skiparse_single", "skiparse_group"):
+        div = {"full": 1, "skiparse_single": k, "skiparse_group": k * k}[mode]
+        if n % div:
+            continue
+        note(f"device index map mode={mode} n={n} k={k}")
+        perm, inv = osp.osp_skiparse_index(mode, k, n, device="cuda")
+        torch.cuda.synchronize()
+        want_perm, want_inv = oracle.skiparse_index(mode, k, n)
+        assert np.array_equal(perm.cpu().numpy(), want_perm)
+        assert np.array_equal(inv.cpu().numpy(), want_inv)

@@ -1,0 +1,37 @@
+"""Skiparse index maps from the library's host path equal the oracle's
+membership-predicate maps bit for bit.  CPU only."""
+import numpy as np
+import pytest
+
+import oracle
+import spatiotemporal_attention_amd as osp
+
+CASES = [
+    (n, k) for n in (16, 48, 64, 320, 720, 4096, 28800) for k in (1, 2, 3, 4, 8)
+] + [(86400, 4), (17550, 3), (1 << 20, 16), (9, 3), (1, 1)]
+
+
+@pytest.mark.parametrize("n,k", CASES)
+def test_host_maps_bitexact(n, k):
+    for mode in ("full", "skiparse_single", "skiparse_group"):
+        div = k if mode == "skiparse_single" else (k * k if mode == "skiparse_group" else 1)
+        if n % div:
+            with pytest.raises(osp.OspError):
+                osp.osp_skiparse_index(mode, k, n)
+            continue
+        perm, inv = osp.osp_skiparse_index(mode, k, n)
+        want_perm, want_inv = oracle.skiparse_index(mode, k, n)
+        assert perm.dtype == np.int32 and inv.dtype == np.int32
+        assert np.array_equal(perm, want_perm), (mode, n, k)
+        assert np.array_equal(inv, want_inv), (mode, n, k)
+
+
+def test_large_ratio_division_paths():
+    # the library divides by k with multiply-high; exercise many divisors
+    for k in list(range(1, 40)) + [63, 64, 65, 127, 255, 256]:
+        n = k * k * (3 if k < 64 else 1)
+        perm, _ = osp.osp_skiparse_index("skiparse_group", k, n)
+        assert np.array_equal(perm, oracle.skiparse_index("skiparse_group", k, n)[0]), k
+    for k in list(range(1, 40)) + [63, 64, 65, 127, 255, 256, 1000, 4096]:
+        perm, _ = osp.osp_skiparse_index("skiparse_single", k, k * 7)
+        assert np.array_equal(perm, oracle.skiparse_index("skiparse_single", k, k * 7)[0]), k
