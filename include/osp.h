@@ -62,8 +62,11 @@ typedef enum {
 } osp_mode;
 
 /* flags of osp_attn3d_fwd */
-#define OSP_FUSE_ROPE 1  /* rotate Q and K inside the attention loaders;
-                            without it Q and K are taken as already rotated */
+#define OSP_FUSE_ROPE_Q 1  /* rotate Q inside the attention loader; without it
+                              Q is taken as already rotated                  */
+#define OSP_FUSE_ROPE_K 2  /* rotate K inside the attention loader; without it
+                              K is taken as already rotated                  */
+#define OSP_FUSE_ROPE 3    /* both                                           */
 
 /* Shape, layout and RoPE settings of one attention call. */
 typedef struct {
@@ -120,8 +123,12 @@ osp_status osp_rope3d(const osp_attn3d_desc* desc, const void* x, void* y,
    equals full attention.  The k subsequences are attended independently
    and each output row is written back at its token's original position.
    sm_scale: logit scale; <= 0 selects 1/sqrt(head_dim).
-   flags: OSP_FUSE_ROPE rotates Q and K in the loaders (exactly as
-   osp_rope3d would, then bf16), otherwise Q and K must already be rotated.
+   flags: OSP_FUSE_ROPE_Q / OSP_FUSE_ROPE_K rotate Q / K in the loaders
+   (exactly as osp_rope3d would, then bf16); a tensor whose flag is clear
+   must already be rotated.  Every combination gives bit-identical results
+   for the same rotated values.  OSP_FUSE_ROPE_K needs the per-axis cos/sin
+   table in LDS: grid_t*rope_t + grid_h*rope_h + grid_w*rope_w <= 6144
+   (else OSP_ERR_UNSUPPORTED; rotate K with osp_rope3d instead).
    q, k, v: [B, N, H, D] bf16 read with stride_*; o: written with ostride_*,
    must not overlap q, k or v.  lse: NULL, or [B, H, N] fp32 contiguous,
    receives ln(sum_j exp(sm_scale * q_i . k_j)) over the row's subsequence,

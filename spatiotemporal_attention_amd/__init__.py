@@ -18,7 +18,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libosp.so")
 
 MODES = {"full": 0, "skiparse_single": 1, "skiparse_group": 2}
-OSP_FUSE_ROPE = 1
+OSP_FUSE_ROPE_Q = 1
+OSP_FUSE_ROPE_K = 2
+OSP_FUSE_ROPE = 3
 ABI_VERSION = 1
 
 
@@ -157,11 +159,13 @@ def osp_rope3d(x: torch.Tensor, *, grid, n_text: int = 0, rope_split, theta: flo
 def osp_attn3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid,
                    n_text: int = 0, mode="full", sparse_k: int = 1, rope_split,
                    theta: float = 1e4, sm_scale: float | None = None,
-                   fuse_rope: bool = True, pos_offset=(0, 0, 0),
+                   fuse_rope=True, pos_offset=(0, 0, 0),
                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                    return_lse: bool = False):
     """Attention forward over [B, N, H, D] bf16 q, k, v on the GPU.
 
+    fuse_rope: True (rotate Q and K in the loaders), False (both already
+    rotated), "q" or "k" (rotate only that one in its loader).
     Returns o (and lse [B, H, N] fp32 when return_lse or lse is given)."""
     b, n, h, d = q.shape
     st = _bnhd(q, "q")
@@ -179,7 +183,12 @@ def osp_attn3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid,
     desc = make_desc(batch=b, n_text=n_text, grid=grid, heads=h, head_dim=d,
                      rope_split=rope_split, theta=theta, pos_offset=pos_offset,
                      strides=st, ostrides=_bnhd(out, "out"))
-    flags = OSP_FUSE_ROPE if fuse_rope else 0
+    if fuse_rope is True:
+        flags = OSP_FUSE_ROPE
+    elif fuse_rope is False or fuse_rope is None:
+        flags = 0
+    else:
+        flags = {"q": OSP_FUSE_ROPE_Q, "k": OSP_FUSE_ROPE_K, "qk": OSP_FUSE_ROPE}[fuse_rope]
     _check(lib().osp_attn3d_fwd(
         ctypes.byref(desc), _mode(mode), int(sparse_k),
         float(sm_scale) if sm_scale is not None else 0.0, flags,

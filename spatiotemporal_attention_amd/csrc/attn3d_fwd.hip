@@ -1,62 +1,67 @@
 // attn3d_fwd.hip -- flash-style attention forward for gfx950 (MI355X):
-// 3D RoPE fused into the Q/K loaders, Skiparse as a row -> token remap in
-// the loaders and the store, bf16 MFMA 32x32x16 with fp32 accumulation,
-// fp32 online softmax.
+// 3D RoPE fused into the Q (and optionally K) loaders, Skiparse as a
+// row -> token remap in the loaders and the store, bf16 MFMA 32x32x16 with
+// fp32 accumulation, fp32 online softmax.
 //
 // What it computes: softmax(scale * q k^T) v over every token of a
 // subsequence (CogVideoX section 2.2 "3D Full Attention"; Skiparse
 // subsequences from Open-Sora Plan section 2.2.2).  The blocked order with a
-// running maximum reaches the same result as the plain definition up to
-// rounding (the FlashAttention argument cited in CogVideoX section 2.2).
+// running maximum reaches the plain definition's result up to rounding (the
+// FlashAttention argument cited in CogVideoX section 2.2).
 //
-// Work split.  One workgroup = NW waves owns BM = NW*32*QB query rows of one
-// (batch, head, subsequence); each wave owns QB blocks of 32 rows.  Keys
-// and values stream through LDS in tiles of BN rows, double buffered.
+// Work split.  One workgroup = 4 waves owns BM = 4*32*QB query rows of one
+// (batch, head, subsequence); each wave owns QB blocks of 32 rows.  Keys and
+// values stream through LDS in tiles of BN rows (row-major, padded rows).
 //
-// Per wave and key tile, S^T = K Q^T is formed with K as the A operand
-// (read from LDS) and Q^T as the B operand (held in registers), so each lane
-// ends up holding scores of ONE query (column = lane mod 32): the row max
-// and row sum are in-lane reductions plus one exchange with lane +-32.
-// O^T = V^T P^T then takes the probabilities straight from the score
-// registers as the B operand; V is stored transposed in LDS so the A operand
-// is two 8-byte reads per lane.  The k-index order inside each PV product
-// is permuted identically on both operands to match the score layout.
+// Per wave and key tile, S^T = K Q^T is formed with K as the A operand (LDS)
+// and Q^T as the B operand (registers), so a lane holds the scores of ONE
+// query (column = lane mod 32): row max and row sum are in-lane reductions
+// plus one exchange with lane +-32 (v_permlane32_swap).  O^T = V^T P^T takes
+// the probabilities straight from the score registers as the B operand; the
+// V^T A operand is read from row-major V with ds_read_b64_tr_b16 (a
+// transposing LDS read), in the key order that matches the score layout.
 //
-// Softmax: logits are kept in log2 units (scale * log2 e folded into one
-// FMA before v_exp_f32).  The reference maximum m of a row is only raised
-// when a tile's maximum exceeds it by more than kTau (= 8, i.e. factor 256),
-// so the O rescale is skipped for most tiles; probabilities stay <= 2^8 and
-// the final O / l is unchanged in exact arithmetic.
+// Software pipeline (one wave per SIMD, so MFMA and VALU overlap inside the
+// wave): iteration j issues the S products of tile j+1 interleaved with the
+// exponentials of tile j, then the PV products of tile j interleaved with the
+// row max of tile j+1.  K runs one tile ahead of V in double-buffered LDS.
+//
+// Softmax: logits in log2 units (scale * log2 e folded into one FMA before
+// v_exp_f32).  A row's reference maximum m only rises when a tile's maximum
+// exceeds it by more than kTau (= 8, a factor 256), so the O rescale is
+// skipped for most tiles; probabilities stay <= 2^8 and O / l is unchanged
+// in exact arithmetic.  Row sums add the bf16-rounded probabilities (the
+// same values the PV product uses) with v_dot2c_f32_bf16.
+#include <type_traits>
+
 #include "osp_internal.hpp"
 
 namespace osp {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef i16x4_t __attribute__((address_space(3))) * lds_i16x4_ptr;
 
 constexpr float kTau = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
-template <int D, int NW, int QB, int BN>
+template <int D, int QB, int BN>
 struct AttnCfg {
+  static constexpr int NW = 4;
   static constexpr int NT = NW * 64;
   static constexpr int BM = NW * 32 * QB;
-  static constexpr int KSTR = D + 8;    // LDS row pitch of K (bf16): 16*odd bytes
-  static constexpr int VSTR = BN + 4;   // LDS row pitch of V^T (bf16): 8*odd bytes
-  static constexpr int K_ELEMS = BN * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int KCH = D / 8;     // 16-byte chunks per row
-  static constexpr int K_ITEMS = BN * KCH;
-  static constexpr int K_PER_T = (K_ITEMS + NT - 1) / NT;
-  static constexpr int V_ITEMS = (BN / 4) * KCH;
-  static constexpr int V_PER_T = (V_ITEMS + NT - 1) / NT;
+  static constexpr int KP = D + 8;              // LDS row pitch (bf16): 16 * odd bytes
+  static constexpr int TILE = BN * KP;          // elements of one K or V tile
+  static constexpr int KCH = D / 8;             // 16-byte chunks per row
+  static constexpr int CH = BN * KCH;           // chunks per tile
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
-  static_assert(((KSTR * 2 / 16) & 1) == 1, "K pitch must be 16 * odd bytes");
-  static_assert(((VSTR * 2 / 8) & 1) == 1, "V^T pitch must be 8 * odd bytes");
+  static_assert(CH % 128 == 0, "each half of the workgroup loads whole chunks");
+  static_assert(((KP * 2 / 16) & 1) == 1, "row pitch must be 16 * odd bytes");
 };
 
-// LDS for the RoPE rates and cos/sin table, only when the kernel rotates.
+// LDS for the RoPE rates and cos/sin table, only when a loader rotates.
 template <bool R> struct RopeSmem {
   RopeLds r;
   __device__ RopeLds* get() { return &r; }
@@ -66,17 +71,30 @@ template <> struct RopeSmem<false> {
   __device__ RopeLds* get() { return nullptr; }
 };
 
+template <bool B> using bool_c = std::integral_constant<bool, B>;
+
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// max / sum over lanes l and l^32
+__device__ __forceinline__ float max_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-template <int D, int NW, int QB, int BN, int ROPE>
-__global__ __launch_bounds__(NW * 64) void attn3d_fwd_kernel(const AttnArgs a) {
-  using C = AttnCfg<D, NW, QB, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
-  __shared__ __attribute__((aligned(16))) RopeSmem<ROPE != 0> rsm;
+// ROPE_Q / ROPE_K: rotate Q / K in the loaders (false = already rotated).
+template <int D, int QB, int BN, bool ROPE_Q, bool ROPE_K>
+__global__ __launch_bounds__(256) void attn3d_fwd_kernel(const AttnArgs a) {
+  using C = AttnCfg<D, QB, BN>;
+  constexpr int NKB = BN / 32;        // 32-key blocks per tile
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2 * C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2 * C::TILE];
+  __shared__ __attribute__((aligned(16))) RopeSmem<ROPE_Q || ROPE_K> rsm;
   RopeLds* const rl = rsm.get();
 
   const int tid = threadIdx.x;
@@ -97,16 +115,28 @@ __global__ __launch_bounds__(NW * 64) void attn3d_fwd_kernel(const AttnArgs a) {
   const uint32_t h = u % uint32_t(a.heads);
   const uint32_t b = u / uint32_t(a.heads);
 
+  // kernel arguments used below, as locals (keeps the argument block out of
+  // private memory)
+  const int mode = a.mode;
+  const FastDiv divk = a.divk;
+  const RopeGeom rg = rope_scalars(a.rope);
+  const int64_t a_sn = a.sn;
+
   const int L = a.seq_len;
+  const int nkt = (L + BN - 1) / BN;
   const int64_t in_off = int64_t(b) * a.sb + int64_t(h) * a.sh;
   const uint16_t* __restrict__ qg = a.q + in_off;
   const uint16_t* __restrict__ kg = a.k + in_off;
   const uint16_t* __restrict__ vg = a.v + in_off;
+  const float c2 = a.scale_log2;
 
-  if constexpr (ROPE != 0) {
-    build_rope_lds(a.rope, rl, tid, C::NT);
+  if constexpr (ROPE_Q || ROPE_K) {
+    stage_rope_rates<C::NT>(a.rope.omega, rl, tid);
+    __syncthreads();
+    fill_rope_table(rg, rl, tid, C::NT);
     __syncthreads();
   }
+  const bool fast_rope = rg.aligned8 && rg.tab_entries;
 
   // ---- Q^T operand: lane holds query (block, l32), channels 16c + 8g .. +7
   bf16x8_t qreg[QB][D / 16];
@@ -114,19 +144,100 @@ __global__ __launch_bounds__(NW * 64) void attn3d_fwd_kernel(const AttnArgs a) {
   for (int qb = 0; qb < QB; ++qb) {
     const int r = int(qt) * C::BM + (wave * QB + qb) * 32 + l32;
     const bool valid = r < L;
-    const uint32_t i = skiparse_token(a.mode, uint32_t(valid ? r : 0), j, a.divk);
-    const uint16_t* p = qg + int64_t(i) * a.sn;
-    Coord3 cc;
-    const bool video = ROPE ? token_coords(a.rope, i, &cc) : false;
+    const uint32_t i = skiparse_token(mode, uint32_t(valid ? r : 0), j, divk);
+    const uint16_t* p = qg + int64_t(i) * a_sn;
+    const bool video = ROPE_Q && is_video(rg, i);
+    const Coord3 cc = video_coords(rg, i);
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
       uint4 raw = valid ? ld16(p + 16 * c + 8 * g) : make_uint4(0, 0, 0, 0);
-      if (ROPE == 1 && video) raw = rotate_chunk_col(rl, chunk_col(a.rope, 8 * c + 4 * g), cc, raw);
-      if (ROPE == 2 && video) raw = rotate_chunk(a.rope, rl, 8 * c + 4 * g, cc, raw);
+      if (ROPE_Q && video) raw = rotate_chunk(rg, rl, 8 * c + 4 * g, cc, raw);
       qreg[qb][c] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
 
+  // ---- loaders.  Each tile's K and V are fetched by the two halves of
+  // the workgroup (waves 0-1 and 2-3), which swap roles every tile so that
+  // K rotation work alternates.  Tile kt's first row r0 = kt*BN maps to
+  // token i0(kt); the remap is increasing in the row, and when BN is a
+  // multiple of the group-skip ratio (or the mode is full / single skip),
+  // row r0 + row maps to i0(kt) + drow(row): every thread's byte offsets
+  // are fixed and only the tile base moves.  Loads go through a buffer descriptor whose range ends
+  // at kRecords, so rows past the end of the subsequence (offset kRecords)
+  // read as zeros without a branch.
+  constexpr int LDPT = C::CH / 128;
+  constexpr int32_t kRecords = 0x40000000;
+  const int half = __builtin_amdgcn_readfirstlane(tid >> 7);
+  const int rt = tid & 127;
+  const int kmul = (mode == MODE_FULL) ? 1 : int(divk.d);
+  const bool fixed_rows = (mode != MODE_GROUP) || (BN % kmul == 0);
+  int ld_row[LDPT], ld_col[LDPT];
+  uint32_t ld_drow[LDPT];
+  int32_t ld_off[LDPT];
+  ChunkCol ld_rc[LDPT];
+#pragma unroll
+  for (int e = 0; e < LDPT; ++e) {
+    const int idx = rt + 128 * e;
+    ld_row[e] = idx / C::KCH;
+    ld_col[e] = idx % C::KCH;
+    const uint32_t rw = uint32_t(ld_row[e]);
+    ld_drow[e] = (mode == MODE_FULL) ? rw
+               : (mode == MODE_SINGLE) ? rw * uint32_t(kmul)
+               : (rw / uint32_t(kmul)) * uint32_t(kmul * kmul) + rw % uint32_t(kmul);
+    ld_off[e] = int32_t((int64_t(ld_drow[e]) * a_sn + 8 * ld_col[e]) * 2);
+    if constexpr (ROPE_K) ld_rc[e] = chunk_col(rg, 4 * ld_col[e]);
+  }
+
+  uint4 ld_reg[LDPT];
+  // Issue this thread's loads: the half whose index equals the tile
+  // parity fetches K of tile kt_k, the other half V of tile kt_v (-1: none).
+  auto issue_loads = [&](int kt_k, int kt_v, int parity) __attribute__((always_inline)) {
+    const bool do_k = half == parity;
+    const int kt = do_k ? kt_k : kt_v;
+    if (kt < 0) return;
+    const uint32_t i0 = skiparse_token(mode, uint32_t(kt * BN), j, divk);
+    const uint16_t* tb = (do_k ? kg : vg) + int64_t(i0) * a_sn;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(tb), (short)0, kRecords, 0x00020000);
+    const int rem = L - kt * BN;
+#pragma unroll
+    for (int e = 0; e < LDPT; ++e) {
+      int32_t off = ld_off[e];
+      if (!fixed_rows) {
+        const uint32_t r = uint32_t(min(kt * BN + ld_row[e], L - 1));
+        off = int32_t((int64_t(skiparse_token(mode, r, j, divk) - i0) * a_sn + 8 * ld_col[e]) * 2);
+      }
+      off = (ld_row[e] < rem) ? off : kRecords;
+      ld_reg[e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    }
+  };
+  // Store the staged chunks into LDS (rotating K when fused).
+  auto store_loads = [&](int kt_k, int kt_v, int parity) __attribute__((always_inline)) {
+    const bool do_k = half == parity;
+    const int kt = do_k ? kt_k : kt_v;
+    if (kt < 0) return;
+    uint16_t* dst = (do_k ? kbuf : vbuf) + (kt & 1) * C::TILE;
+    const uint32_t i0 = skiparse_token(mode, uint32_t(kt * BN), j, divk);
+#pragma unroll
+    for (int e = 0; e < LDPT; ++e) {
+      uint4 val = ld_reg[e];
+      if constexpr (ROPE_K) {
+        if (do_k) {
+          const int r = kt * BN + ld_row[e];
+          const uint32_t i = fixed_rows ? i0 + ld_drow[e]
+                                        : skiparse_token(mode, uint32_t(min(r, L - 1)), j, divk);
+          if (r < L && is_video(rg, i)) {
+            const Coord3 cc = video_coords(rg, i);
+            val = fast_rope ? rotate_chunk_col(rl, ld_rc[e], cc, val)
+                            : rotate_chunk_tab(rg, rl, 4 * ld_col[e], cc, val);
+          }
+        }
+      }
+      *reinterpret_cast<uint4*>(dst + ld_row[e] * C::KP + 8 * ld_col[e]) = val;
+    }
+  };
+
+  // ---- accumulators and softmax state
   f32x16_t o[QB][D / 32];
   float mref[QB], lsum[QB];
 #pragma unroll
@@ -139,99 +250,11 @@ __global__ __launch_bounds__(NW * 64) void attn3d_fwd_kernel(const AttnArgs a) {
       for (int e = 0; e < 16; ++e) o[qb][db][e] = 0.f;
   }
 
-  // ---- K/V tile loaders: global -> registers -> (rotate / transpose) -> LDS
-  uint4 kreg[C::K_PER_T];
-  Coord3 kcrd[C::K_PER_T];
-  bool kvid[C::K_PER_T];
-  uint4 vreg[C::V_PER_T][4];
-  ChunkCol kcol[C::K_PER_T];     // fast RoPE path: table column of each K chunk
-  if constexpr (ROPE == 1) {
+  // S^T of tile kt into s (LDS buffer kt & 1)
+  auto qk = [&](int kt, f32x16_t (&s)[NKB][QB]) __attribute__((always_inline)) {
+    const uint16_t* ks = kbuf + (kt & 1) * C::TILE;
 #pragma unroll
-    for (int e = 0; e < C::K_PER_T; ++e)
-      kcol[e] = chunk_col(a.rope, 4 * ((tid + e * C::NT) % C::KCH));
-  }
-
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int e = 0; e < C::K_PER_T; ++e) {
-      const int idx = tid + e * C::NT;
-      const int row = idx / C::KCH, ch = idx % C::KCH;
-      const int r = kt * BN + row;
-      const bool valid = (idx < C::K_ITEMS) && (r < L);
-      const uint32_t i = skiparse_token(a.mode, uint32_t(valid ? r : 0), j, a.divk);
-      kreg[e] = valid ? ld16(kg + int64_t(i) * a.sn + 8 * ch) : make_uint4(0, 0, 0, 0);
-      if (ROPE) kvid[e] = valid && token_coords(a.rope, i, &kcrd[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < C::V_PER_T; ++e) {
-      const int idx = tid + e * C::NT;
-      const int kq = idx % (BN / 4), ch = idx / (BN / 4);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = kt * BN + 4 * kq + t;
-        const bool valid = (idx < C::V_ITEMS) && (r < L);
-        const uint32_t i = skiparse_token(a.mode, uint32_t(valid ? r : 0), j, a.divk);
-        vreg[e][t] = valid ? ld16(vg + int64_t(i) * a.sn + 8 * ch) : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = smem + buf * C::STAGE;
-    uint16_t* vs = ks + C::K_ELEMS;
-#pragma unroll
-    for (int e = 0; e < C::K_PER_T; ++e) {
-      const int idx = tid + e * C::NT;
-      if (idx < C::K_ITEMS) {
-        const int row = idx / C::KCH, ch = idx % C::KCH;
-        uint4 val = kreg[e];
-        if (ROPE == 1 && kvid[e]) val = rotate_chunk_col(rl, kcol[e], kcrd[e], val);
-        if (ROPE == 2 && kvid[e]) val = rotate_chunk(a.rope, rl, 4 * ch, kcrd[e], val);
-        *reinterpret_cast<uint4*>(ks + row * C::KSTR + 8 * ch) = val;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < C::V_PER_T; ++e) {
-      const int idx = tid + e * C::NT;
-      if (idx < C::V_ITEMS) {
-        const int kq = idx % (BN / 4), ch = idx / (BN / 4);
-        const uint32_t w0[4] = {vreg[e][0].x, vreg[e][0].y, vreg[e][0].z, vreg[e][0].w};
-        const uint32_t w1[4] = {vreg[e][1].x, vreg[e][1].y, vreg[e][1].z, vreg[e][1].w};
-        const uint32_t w2[4] = {vreg[e][2].x, vreg[e][2].y, vreg[e][2].z, vreg[e][2].w};
-        const uint32_t w3[4] = {vreg[e][3].x, vreg[e][3].y, vreg[e][3].z, vreg[e][3].w};
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const int wi = dd >> 1;
-          uint32_t lo, hi;
-          if (dd & 1) {
-            lo = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
-            hi = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
-          } else {
-            lo = (w0[wi] & 0xffffu) | (w1[wi] << 16);
-            hi = (w2[wi] & 0xffffu) | (w3[wi] << 16);
-          }
-          *reinterpret_cast<uint2*>(vs + (8 * ch + dd) * C::VSTR + 4 * kq) = make_uint2(lo, hi);
-        }
-      }
-    }
-  };
-
-  const int nkt = (L + BN - 1) / BN;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) load_tile(kt + 1);
-
-    const uint16_t* ks = smem + buf * C::STAGE;
-    const uint16_t* vs = ks + C::K_ELEMS;
-
-    // S^T = K Q^T : lane holds query l32, keys 32kb + 8(e/4) + 4g + e%4
-    f32x16_t s[BN / 32][QB];
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -239,40 +262,40 @@ __global__ __launch_bounds__(NW * 64) void attn3d_fwd_kernel(const AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
         const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(
-            ks + (32 * kb + l32) * C::KSTR + 16 * c + 8 * g);
+            ks + (32 * kb + l32) * C::KP + 16 * c + 8 * g);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], s[kb][qb], 0, 0, 0);
       }
     }
-
-    if ((kt + 1) * BN > L) {   // ragged last tile: drop keys past the end
+  };
+  // keys past the end of the subsequence in tile kt -> -inf
+  auto mask = [&](int kt, f32x16_t (&s)[NKB][QB]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kt * BN + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-          if (key >= L) {
+      for (int e = 0; e < 16; ++e) {
+        const int key = kt * BN + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (key >= L) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[kb][qb][e] = -INFINITY;
-          }
+          for (int qb = 0; qb < QB; ++qb) s[kb][qb][e] = -INFINITY;
         }
-    }
-
-    // online softmax, one query per lane (pair of lanes l, l^32)
+      }
+  };
+  // row max of a tile (scaled to log2 units), raise m where needed, rescale
+  auto update_max = [&](f32x16_t (&s)[NKB][QB]) __attribute__((always_inline)) {
     float zmax[QB];
     bool need = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
-      mx = fmaxf(mx, xor32(mx));
-      zmax[qb] = mx * a.scale_log2;
+      zmax[qb] = max_pair32(mx) * c2;
       need |= zmax[qb] > mref[qb] + kTau;
     }
     if (__ballot(need)) {
@@ -288,46 +311,52 @@ __global__ __launch_bounds__(NW * 64) void attn3d_fwd_kernel(const AttnArgs a) {
           for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
       }
     }
-
-    bf16x8_t pb[QB][BN / 32][2];
+  };
+  // probabilities of a tile as bf16 B operands, row sums
+  auto softmax = [&](f32x16_t (&s)[NKB][QB], bf16x8_t (&pb)[QB][NKB][2]) __attribute__((always_inline)) {
+    const bf16x2v_t one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float nm = -mref[qb];
       float acc = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-        float pv[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][e], a.scale_log2, nm));
-          acc += pv[e];
-        }
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          uint4 w;
-          w.x = pack_bf16(pv[8 * hh + 0], pv[8 * hh + 1]);
-          w.y = pack_bf16(pv[8 * hh + 2], pv[8 * hh + 3]);
-          w.z = pack_bf16(pv[8 * hh + 4], pv[8 * hh + 5]);
-          w.w = pack_bf16(pv[8 * hh + 6], pv[8 * hh + 7]);
-          pb[qb][kb][hh] = __builtin_bit_cast(bf16x8_t, w);
+          uint32_t w[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][8 * hh + 2 * t], c2, nm));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][8 * hh + 2 * t + 1], c2, nm));
+            w[t] = pack_bf16(p0, p1);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[t]), one, acc,
+                                                  false);
+          }
+          pb[qb][kb][hh] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
         }
-      }
       lsum[qb] += acc;
     }
-
-    // O^T += V^T P^T  (db innermost: 3*QB independent accumulators between
-    // two products into the same one)
+  };
+  // O^T += V^T P^T for tile kt (V LDS buffer kt & 1)
+  auto pv = [&](int kt, bf16x8_t (&pb)[QB][NKB][2]) __attribute__((always_inline)) {
+    const uint16_t* vs = vbuf + (kt & 1) * C::TILE;
+    const int G = lane >> 4, s16 = lane & 15;
+    const int ta = s16 & 3, te = s16 >> 2;
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         bf16x8_t va[D / 32];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const uint16_t* vrow = vs + (32 * db + l32) * C::VSTR + 32 * kb + 16 * hh + 4 * g;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-          va[db] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          // source lane (ta, te) of its 16-lane group points at key
+          // 32kb + 16hh + 4g + te (+8), channels 32db + 16(G%2) + 4ta .. +3
+          const uint16_t* src = vs + (32 * kb + 16 * hh + 4 * (G >> 1) + te) * C::KP +
+                                32 * db + 16 * (G & 1) + 4 * ta;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(src));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(src + 8 * C::KP));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          va[db] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
         }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -335,21 +364,73 @@ __global__ __launch_bounds__(NW * 64) void attn3d_fwd_kernel(const AttnArgs a) {
           for (int qb = 0; qb < QB; ++qb)
             o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pb[qb][kb][hh], o[qb][db], 0, 0, 0);
       }
-    }
+  };
 
-    if (kt + 1 < nkt) store_tile(buf ^ 1);
-    __syncthreads();
+  // ---- prologue: K0, V0 (and K1) into LDS, S of tile 0
+  f32x16_t sA[NKB][QB], sB[NKB][QB];
+  issue_loads(0, 0, 0);
+  store_loads(0, 0, 0);
+  if (nkt > 1) {
+    issue_loads(1, -1, 0);
+    store_loads(1, -1, 0);
+  }
+  __syncthreads();
+  qk(0, sA);
+  if (nkt == 1 && L % BN) mask(0, sA);
+  update_max(sA);
+  __syncthreads();   // K0's buffer is refilled with K2 in the first iteration
+
+  // ---- main loop.  Iteration jt: S(jt+1) with exp(jt); PV(jt) with
+  // max(jt+1); stores K(jt+2), V(jt+1).  The two score arrays alternate.
+  auto step = [&](int jt, f32x16_t (&s_cur)[NKB][QB], f32x16_t (&s_nxt)[NKB][QB],
+                  auto has_next, auto load_k2, auto mask_next) __attribute__((always_inline)) {
+    constexpr bool HAS_NEXT = decltype(has_next)::value;
+    constexpr bool LOAD_K2 = decltype(load_k2)::value;
+    constexpr bool MASK_NEXT = decltype(mask_next)::value;
+    const int parity = jt & 1;
+    if constexpr (HAS_NEXT) issue_loads(LOAD_K2 ? jt + 2 : -1, jt + 1, parity);
+    bf16x8_t pb[QB][NKB][2];
+    if constexpr (HAS_NEXT) qk(jt + 1, s_nxt);
+    softmax(s_cur, pb);
+    if constexpr (MASK_NEXT) mask(jt + 1, s_nxt);
+    pv(jt, pb);
+    if constexpr (HAS_NEXT) {
+      store_loads(LOAD_K2 ? jt + 2 : -1, jt + 1, parity);
+      update_max(s_nxt);
+      __syncthreads();
+    }
+  };
+  // the last tiles, starting at tile jt whose scores are in s_cur
+  auto tail = [&](int jt, f32x16_t (&s_cur)[NKB][QB], f32x16_t (&s_nxt)[NKB][QB]) __attribute__((always_inline)) {
+    if (jt + 1 < nkt) {
+      if (L % BN) step(jt, s_cur, s_nxt, bool_c<true>{}, bool_c<false>{}, bool_c<true>{});
+      else step(jt, s_cur, s_nxt, bool_c<true>{}, bool_c<false>{}, bool_c<false>{});
+      step(jt + 1, s_nxt, s_cur, bool_c<false>{}, bool_c<false>{}, bool_c<false>{});
+    } else {
+      step(jt, s_cur, s_nxt, bool_c<false>{}, bool_c<false>{}, bool_c<false>{});
+    }
+  };
+  int jt = 0;
+  for (; jt + 3 < nkt; jt += 2) {
+    step(jt, sA, sB, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
+    step(jt + 1, sB, sA, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
+  }
+  if (jt + 2 < nkt) {
+    step(jt, sA, sB, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
+    tail(jt + 1, sB, sA);
+  } else {
+    tail(jt, sA, sB);
   }
 
   // ---- epilogue: O = O^T / l, stored at the original token row ----
   uint16_t* og = a.o + int64_t(b) * a.osb + int64_t(h) * a.osh;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lt = lsum[qb] + xor32(lsum[qb]);
+    const float lt = sum_pair32(lsum[qb]);
     const float inv = 1.0f / lt;
     const int r = int(qt) * C::BM + (wave * QB + qb) * 32 + l32;
     if (r < L) {
-      const uint32_t i = skiparse_token(a.mode, uint32_t(r), j, a.divk);
+      const uint32_t i = skiparse_token(mode, uint32_t(r), j, divk);
       uint16_t* p = og + int64_t(i) * a.osn;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
@@ -365,40 +446,50 @@ __global__ __launch_bounds__(NW * 64) void attn3d_fwd_kernel(const AttnArgs a) {
   }
 }
 
-// Tile shape per head_dim: waves per workgroup, 32-row query blocks per
-// wave, keys per tile.
+// Tile shape per head_dim: 32-row query blocks per wave, keys per tile.
 template <int D> struct TileCfg;
-template <> struct TileCfg<64> { static constexpr int NW = 4, QB = 2, BN = 64; };
-template <> struct TileCfg<96> { static constexpr int NW = 4, QB = 2, BN = 64; };
-template <> struct TileCfg<128> { static constexpr int NW = 4, QB = 1, BN = 64; };
+template <> struct TileCfg<64> { static constexpr int QB = 2, BN = 32; };
+template <> struct TileCfg<96> { static constexpr int QB = 2, BN = 32; };
+template <> struct TileCfg<128> { static constexpr int QB = 1, BN = 32; };
+
+int attn_keys_per_tile(int head_dim) {
+  switch (head_dim) {
+    case 64: return TileCfg<64>::BN;
+    case 96: return TileCfg<96>::BN;
+    case 128: return TileCfg<128>::BN;
+    default: return 0;
+  }
+}
 
 int attn_rows_per_block(int head_dim) {
   switch (head_dim) {
-    case 64: return TileCfg<64>::NW * 32 * TileCfg<64>::QB;
-    case 96: return TileCfg<96>::NW * 32 * TileCfg<96>::QB;
-    case 128: return TileCfg<128>::NW * 32 * TileCfg<128>::QB;
+    case 64: return AttnCfg<64, TileCfg<64>::QB, TileCfg<64>::BN>::BM;
+    case 96: return AttnCfg<96, TileCfg<96>::QB, TileCfg<96>::BN>::BM;
+    case 128: return AttnCfg<128, TileCfg<128>::QB, TileCfg<128>::BN>::BM;
     default: return 0;
   }
 }
 
 template <int D>
-static hipError_t launch_d(const AttnArgs& a, int rope_kind, hipStream_t s) {
+static hipError_t launch_d(const AttnArgs& a, int rope_q, int rope_k, hipStream_t s) {
   using T = TileCfg<D>;
-  dim3 grid(a.total_tiles), block(T::NW * 64);
-  if (rope_kind == 1)
-    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::NW, T::QB, T::BN, 1>), grid, block, 0, s, a);
-  else if (rope_kind == 2)
-    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::NW, T::QB, T::BN, 2>), grid, block, 0, s, a);
+  dim3 grid(a.total_tiles), block(256);
+  if (rope_q && rope_k)
+    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, true, true>), grid, block, 0, s, a);
+  else if (rope_q)
+    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, true, false>), grid, block, 0, s, a);
+  else if (rope_k)
+    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, false, true>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::NW, T::QB, T::BN, 0>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, false, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_kind, hipStream_t s) {
+hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_q, int rope_k, hipStream_t s) {
   switch (head_dim) {
-    case 64: return launch_d<64>(a, rope_kind, s);
-    case 96: return launch_d<96>(a, rope_kind, s);
-    case 128: return launch_d<128>(a, rope_kind, s);
+    case 64: return launch_d<64>(a, rope_q, rope_k, s);
+    case 96: return launch_d<96>(a, rope_q, rope_k, s);
+    case 128: return launch_d<128>(a, rope_q, rope_k, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -135,14 +135,30 @@ osp_status check_attn(const osp_attn3d_desc* d, int32_t mode, int32_t k, int32_t
                       Shape* s) {
   osp_status st = check_desc(d, true, s);
   if (st) return st;
-  if (flags & ~int32_t(OSP_FUSE_ROPE)) return fail(OSP_ERR_PARAM, "unknown flags 0x%x", flags);
+  if (flags & ~int32_t(OSP_FUSE_ROPE_Q | OSP_FUSE_ROPE_K))
+    return fail(OSP_ERR_PARAM, "unknown flags 0x%x", flags);
   st = check_mode(d, s->n_tokens, mode, k);
   if (st) return st;
+  if (flags & OSP_FUSE_ROPE_K) {
+    osp::RopeGeom g;
+    fill_rope(d, &g);
+    if (!g.tab_entries)
+      return fail(OSP_ERR_UNSUPPORTED,
+                  "K rotation in the loader needs the cos/sin table (grid_t*rope_t + grid_h*rope_h "
+                  "+ grid_w*rope_w <= %d); rotate K with osp_rope3d first",
+                  2 * osp::kMaxTableEntries);
+  }
   const int64_t groups = (mode == OSP_MODE_FULL) ? 1 : k;
   const int64_t len = s->n_tokens / groups;
   const int64_t bm = osp::attn_rows_per_block(d->head_dim);
   const int64_t tiles = int64_t(d->batch) * d->heads * groups * ((len + bm - 1) / bm);
   if (tiles > 0x7fffffffLL) return fail(OSP_ERR_SHAPE, "too many tiles (%lld)", (long long)tiles);
+  // the loaders address one key tile through 32-bit byte offsets below 2^30
+  const int64_t bn = osp::attn_keys_per_tile(d->head_dim);
+  const int64_t span = (bn + groups) * groups * s->sn * 2 + int64_t(d->head_dim) * 2;
+  if (span >= (int64_t(1) << 30))
+    return fail(OSP_ERR_UNSUPPORTED, "token stride %lld with k=%lld spans more than 1 GiB per key tile",
+                (long long)s->sn, (long long)groups);
   return OSP_OK;
 }
 
@@ -252,11 +268,9 @@ osp_status osp_attn3d_fwd(const osp_attn3d_desc* desc, int32_t mode, int32_t spa
   a.total_tiles = a.batch * a.heads * groups * a.q_tiles;
   fill_rope(desc, &a.rope);
   if (a.total_tiles == 0) return ok();
-  // rotation in the loaders: fast path when every axis chunk is a multiple
-  // of 8 channels and the cos/sin table fits in LDS, else the general path
-  const int rope_kind = !(flags & OSP_FUSE_ROPE) ? 0
-                        : (a.rope.aligned8 && a.rope.tab_entries) ? 1 : 2;
-  hipError_t e = osp::launch_attn3d(a, D, rope_kind, static_cast<hipStream_t>(stream));
+  hipError_t e = osp::launch_attn3d(a, D, (flags & OSP_FUSE_ROPE_Q) ? 1 : 0,
+                                    (flags & OSP_FUSE_ROPE_K) ? 1 : 0,
+                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(e, "attn3d_fwd launch");
   return ok();
 }

@@ -27,11 +27,13 @@ struct AttnArgs {
   RopeGeom rope;
 };
 
-// Rows of queries handled by one workgroup of the attention kernel.
+// Rows of queries handled by one workgroup of the attention kernel, and
+// keys per LDS tile.
 int attn_rows_per_block(int head_dim);
+int attn_keys_per_tile(int head_dim);
 
-// rope_kind: 0 = inputs already rotated, 1 = rotate in the loaders.
-hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_kind, hipStream_t s);
+// rope_q / rope_k: rotate Q / K in the loaders (0 = already rotated).
+hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_q, int rope_k, hipStream_t s);
 
 struct RopeArgs {
   const uint16_t* x;

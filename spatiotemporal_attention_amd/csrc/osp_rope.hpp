@@ -78,14 +78,18 @@ __device__ __forceinline__ int pair_axis(const RopeGeom& g, int p, int* r) {
   return a;
 }
 
-// Copy the rates to LDS, then fill the table.  Every thread of the block
-// must call this; the caller synchronises again before reading the table.
-__device__ __forceinline__ void build_rope_lds(const RopeGeom& g, RopeLds* s, int tid,
-                                               int nthreads) {
+// Stage the rates in LDS (all threads), then -- after the caller's barrier
+// -- fill the table with fill_rope_table.
+template <int NT>
+__device__ __forceinline__ void stage_rope_rates(const float (&omega)[kMaxPairs], RopeLds* s,
+                                                 int tid) {
 #pragma unroll
   for (int p = 0; p < kMaxPairs; ++p)
-    if ((p % nthreads) == tid) s->omega[p] = g.omega[p];
-  __syncthreads();
+    if ((p % NT) == tid) s->omega[p] = omega[p];
+}
+
+__device__ __forceinline__ void fill_rope_table(const RopeGeom& g, RopeLds* s, int tid,
+                                                int nthreads) {
   for (int e = tid; e < g.tab_entries; e += nthreads) {
     const int a = (e >= g.off2) ? 2 : (e >= g.off1 ? 1 : 0);
     const int np = sel3(a, g.np0, g.np1, g.np2);
@@ -95,6 +99,19 @@ __device__ __forceinline__ void build_rope_lds(const RopeGeom& g, RopeLds* s, in
     const int p = r + sel3(a, 0, g.np0, g.np0 + g.np1);
     s->tab[e] = rope_cs(x + sel3(a, g.pos0_t, g.pos0_h, g.pos0_w), s->omega[p]);
   }
+}
+
+// The geometry without the rates (small enough for scalar registers).
+__device__ __forceinline__ RopeGeom rope_scalars(const RopeGeom& g) {
+  RopeGeom r;
+  r.n_text = g.n_text;
+  r.np0 = g.np0; r.np1 = g.np1; r.np2 = g.np2;
+  r.pos0_t = g.pos0_t; r.pos0_h = g.pos0_h; r.pos0_w = g.pos0_w;
+  r.off1 = g.off1; r.off2 = g.off2;
+  r.tab_entries = g.tab_entries;
+  r.aligned8 = g.aligned8;
+  r.div_hw = g.div_hw; r.div_w = g.div_w;
+  return r;
 }
 
 // (cos, sin) of pair p for a token at coordinates c (general path).
@@ -116,6 +133,20 @@ __device__ __forceinline__ uint4 rotate_chunk(const RopeGeom& g, const RopeLds* 
   x.y = rotate_pair(x.y, pair_cs(g, s, p0 + 1, c));
   x.z = rotate_pair(x.z, pair_cs(g, s, p0 + 2, c));
   x.w = rotate_pair(x.w, pair_cs(g, s, p0 + 3, c));
+  return x;
+}
+
+// Same as rotate_chunk, table only (requires tab_entries != 0).
+__device__ __forceinline__ uint4 rotate_chunk_tab(const RopeGeom& g, const RopeLds* s, int p0,
+                                                  const Coord3& c, uint4 x) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(&x);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    int r;
+    const int a = pair_axis(g, p0 + t, &r);
+    const int pos = int(sel3(a, c.t, c.h, c.w));
+    w[t] = rotate_pair(w[t], s->tab[sel3(a, 0, g.off1, g.off2) + pos * sel3(a, g.np0, g.np1, g.np2) + r]);
+  }
   return x;
 }
 
@@ -148,11 +179,14 @@ __device__ __forceinline__ uint4 rotate_chunk_col(const RopeLds* s, const ChunkC
   return x;
 }
 
-// Is token i a video token, and if so its coordinates.
-__device__ __forceinline__ bool token_coords(const RopeGeom& g, uint32_t i, Coord3* c) {
-  if (int32_t(i) < g.n_text) return false;
-  *c = decode_video(i - uint32_t(g.n_text), g.div_hw, g.div_w);
-  return true;
+// Is token i a video token (text tokens come first and are not rotated).
+__device__ __forceinline__ bool is_video(const RopeGeom& g, uint32_t i) {
+  return int32_t(i) >= g.n_text;
+}
+
+// Latent coordinates of video token i.
+__device__ __forceinline__ Coord3 video_coords(const RopeGeom& g, uint32_t i) {
+  return decode_video(i - uint32_t(g.n_text), g.div_hw, g.div_w);
 }
 
 }  // namespace osp

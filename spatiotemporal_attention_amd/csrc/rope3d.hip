@@ -18,7 +18,9 @@ __global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(const RopeArgs a,
                                                                FastDiv div_heads,
                                                                FastDiv div_tokens) {
   __shared__ __attribute__((aligned(16))) RopeLds rl;
-  build_rope_lds(a.rope, &rl, threadIdx.x, kRopeThreads);
+  stage_rope_rates<kRopeThreads>(a.rope.omega, &rl, threadIdx.x);
+  __syncthreads();
+  fill_rope_table(a.rope, &rl, threadIdx.x, kRopeThreads);
   __syncthreads();
   const uint32_t kch = uint32_t(a.head_dim / 8);
   for (uint32_t idx = blockIdx.x * kRopeThreads + threadIdx.x; idx < total;
@@ -33,8 +35,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(const RopeArgs a,
     const uint16_t* src = a.x + int64_t(b) * a.sb + int64_t(n) * a.sn + int64_t(h) * a.sh + 8 * ch;
     uint16_t* dst = a.y + int64_t(b) * a.osb + int64_t(n) * a.osn + int64_t(h) * a.osh + 8 * ch;
     uint4 v = *reinterpret_cast<const uint4*>(src);
-    Coord3 c;
-    if (token_coords(a.rope, n, &c)) v = rotate_chunk(a.rope, &rl, 4 * int(ch), c, v);
+    if (is_video(a.rope, n)) v = rotate_chunk(a.rope, &rl, 4 * int(ch), video_coords(a.rope, n), v);
     *reinterpret_cast<uint4*>(dst) = v;
   }
 }

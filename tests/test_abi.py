@@ -97,6 +97,14 @@ def _code(desc, mode="full", k=1, flags=1):
     ({"grid": (2000, 2000, 1000)}, "full", 1, 1, SHAPE),   # N > 2^31 - 1
     ({"strides": (0, 132, 0)}, "full", 1, 1, PARAM),       # not a multiple of 8
     ({"ostrides": (0, 0, -64)}, "full", 1, 1, PARAM),
+    # rotating K in the loader needs the cos/sin table in LDS (6144 pair-rows)
+    ({"grid": (200, 100, 100), "head_dim": 96, "rope_split": (32, 32, 32)}, "full", 1, 3, UNSUP),
+    ({"grid": (200, 100, 100), "head_dim": 96, "rope_split": (32, 32, 32)}, "full", 1, 2, UNSUP),
+    ({"grid": (200, 100, 100), "head_dim": 96, "rope_split": (32, 32, 32)}, "full", 1, 1, OK),
+    ({"grid": (200, 100, 100), "head_dim": 96, "rope_split": (32, 32, 32)}, "full", 1, 0, OK),
+    ({}, "full", 1, 0, OK),
+    ({}, "full", 1, 2, OK),
+    ({}, "full", 1, 8, PARAM),
 ])
 def test_attn_check_codes(kw, mode, k, flags, want):
     assert _code(_desc(**kw), mode, k, flags) == want

@@ -33,9 +33,10 @@ def run_case(seed, *, grid, n_text, heads, head_dim, rope_split, mode="full", sp
     note(f"case {tag} seed={seed} shape={shape} grid={grid} n_text={n_text} mode={mode} "
          f"k={sparse_k} rope={rope_split} fuse={fuse_rope}")
     cpu, (q, k, v) = qkv_for(seed, shape, scale, q_mult)
-    if not fuse_rope:
+    if fuse_rope in (False, "k"):
         q = osp.osp_rope3d(q, grid=grid, n_text=n_text, rope_split=rope_split, theta=theta,
                            pos_offset=pos_offset)
+    if fuse_rope in (False, "q"):
         k = osp.osp_rope3d(k, grid=grid, n_text=n_text, rope_split=rope_split, theta=theta,
                            pos_offset=pos_offset)
     o, l = osp.osp_attn3d_fwd(q, k, v, grid=grid, n_text=n_text, mode=mode, sparse_k=sparse_k,
@@ -148,15 +149,17 @@ def test_single_token_and_singleton_groups():
              mode="skiparse_single", sparse_k=16, tag="k=N")
 
 
-def test_fused_equals_unfused_bitwise():
-    args = dict(grid=(4, 12, 15), n_text=0, heads=3, head_dim=96, rope_split=(32, 32, 32))
+@pytest.mark.parametrize("args", [
+    dict(grid=(4, 12, 15), n_text=0, heads=3, head_dim=96, rope_split=(32, 32, 32)),
+    dict(grid=(3, 10, 12), n_text=37, heads=2, head_dim=64, rope_split=(16, 24, 24)),
+    dict(grid=(3, 7, 9), n_text=5, heads=2, head_dim=96, rope_split=(36, 36, 24)),
+], ids=["d96", "d64-text", "d96-split36"])
+def test_fused_equals_unfused_bitwise(args):
+    # rotating in the loaders gives the same bf16 operands as osp_rope3d
     a, la = run_case(16, **args, tag="fused")
-    b, lb = run_case(16, **args, fuse_rope=False, tag="unfused")
-    assert torch.equal(a, b) and torch.equal(la, lb)
-    args = dict(grid=(3, 10, 12), n_text=37, heads=2, head_dim=64, rope_split=(16, 24, 24))
-    a, _ = run_case(17, **args, tag="fused-text")
-    b, _ = run_case(17, **args, fuse_rope=False, tag="unfused-text")
-    assert torch.equal(a, b)
+    for mode in (False, "q", "k"):
+        b, lb = run_case(16, **args, fuse_rope=mode, tag=f"fuse={mode}")
+        assert torch.equal(a, b) and torch.equal(la, lb), mode
 
 
 def test_deterministic_and_fully_written():
