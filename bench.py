@@ -2,11 +2,13 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-A step is one pass of the whole hot path over one batch of synthetic input:
-latent grid of the clip, 3D RoPE fused into the loaders, full attention over
-all tokens, output scattered back in token order -- one osp_attn3d_fwd call
-on the Open-Sora-Plan-shaped 93x480p workload (grid 24x30x40 = 28,800 tokens,
-batch 1, 24 heads, head_dim 96).  Inputs are resident in HBM before timing.
+A step is one pass of the whole hot path over one batch of synthetic input
+on the Open-Sora-Plan-shaped 93x480p workload (grid 24x30x40 = 28,800
+tokens, batch 1, 24 heads, head_dim 96): latent grid of the clip on the
+host, 3D RoPE of K in one memory-bound pass (osp_rope3d), then attention
+with the rotation of Q fused into its loader, full attention over all
+tokens and the output written back in token order (osp_attn3d_fwd).
+Inputs are resident in HBM before timing.
 
 Prints ONE JSON line.  value = algorithmic attention TFLOP/s
 (4*B*H*N^2*D / k per call).  Also reported: the same kernel on Skiparse k=4
@@ -64,7 +66,7 @@ def parse():
     p.add_argument("--cpu-heads", type=int, default=2,
                    help="heads of the workload the oracle times (all query rows each)")
     p.add_argument("--profile", action="store_true",
-                   help="few launches of the full-attention step only (for rocprofv3)")
+                   help="few steps of the full-attention workload only (for rocprofv3)")
     p.add_argument("--copy", type=int, default=0,
                    help="instead: time a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -104,11 +106,18 @@ def main():
     shape = (B, n_tok, H, D)
     q, k, v = (t.to(dev) for t in workloads.make_qkv(wl.seed, shape, wl.input_scale))
     o = torch.empty_like(q)
+    k_rot = torch.empty_like(k)
     stream = torch.cuda.current_stream(dev)
 
-    def step(mode="full", sk=1):
-        osp.osp_attn3d_fwd(q, k, v, grid=grid, n_text=wl.n_text, mode=mode, sparse_k=sk,
-                           rope_split=wl.rope_split, theta=wl.theta, fuse_rope=True, out=o)
+    def step(mode="full", sk=1, marks=None):
+        osp.osp_rope3d(k, grid=grid, n_text=wl.n_text, rope_split=wl.rope_split,
+                       theta=wl.theta, out=k_rot)
+        if marks:
+            marks[0].record(stream)
+        osp.osp_attn3d_fwd(q, k_rot, v, grid=grid, n_text=wl.n_text, mode=mode, sparse_k=sk,
+                           rope_split=wl.rope_split, theta=wl.theta, fuse_rope="q", out=o)
+        if marks:
+            marks[1].record(stream)
 
     def flops(sk=1):
         return 4.0 * B * H * float(n_tok) ** 2 * D / sk
@@ -135,10 +144,8 @@ def main():
         torch.cuda.synchronize()
         t_wall = time.perf_counter()
         t0.record(stream)
-        for e0, e1 in evs:
-            e0.record(stream)
-            step(mode, sk)
-            e1.record(stream)
+        for marks in evs:
+            step(mode, sk, marks)     # events bracket the attention launch
         t1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_wall
@@ -203,7 +210,8 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn3d_fwd_kernel<96,...,rope=1>",
+                     "traffic": traffic,
+                     "kernel": "attn3d_fwd_kernel<96, QB=2, BN=32, rope_q, fixed_rows>",
                      "flop_per_launch": f_full, "ms_per_launch": round(ms_launch, 4),
                      "ms_median": round(ms_med, 4), "ms_min": round(ms_min, 4)},
         "skiparse": extra,

@@ -9,9 +9,17 @@
 // running maximum reaches the plain definition's result up to rounding (the
 // FlashAttention argument cited in CogVideoX section 2.2).
 //
-// Work split.  One workgroup = 4 waves owns BM = 4*32*QB query rows of one
+// Work split.  One workgroup = NW waves owns BM = NW*32*QB query rows of one
 // (batch, head, subsequence); each wave owns QB blocks of 32 rows.  Keys and
-// values stream through LDS in tiles of BN rows (row-major, padded rows).
+// values stream through LDS in tiles of BN rows.
+//
+// LDS tiles are unpadded rows of D bf16; the 16-byte chunks of row r are
+// XOR-swizzled (chunk_swz) so that the operand reads below hit distinct
+// banks.  Tiles arrive by LDS DMA (buffer_load ... lds): each wave issues a
+// few 64-lane loads that write 1 KiB of a tile directly, with no registers
+// and no LDS store instructions; rows past the end of a subsequence are
+// fetched out of the buffer range and land as zeros.  When K is rotated in
+// the loader, chunks go through registers instead.
 //
 // Per wave and key tile, S^T = K Q^T is formed with K as the A operand (LDS)
 // and Q^T as the B operand (registers), so a lane holds the scores of ONE
@@ -21,10 +29,11 @@
 // V^T A operand is read from row-major V with ds_read_b64_tr_b16 (a
 // transposing LDS read), in the key order that matches the score layout.
 //
-// Software pipeline (one wave per SIMD, so MFMA and VALU overlap inside the
-// wave): iteration j issues the S products of tile j+1 interleaved with the
-// exponentials of tile j, then the PV products of tile j interleaved with the
-// row max of tile j+1.  K runs one tile ahead of V in double-buffered LDS.
+// Pipeline: iteration j issues the S products of tile j+1 interleaved with
+// the exponentials of tile j, then the PV products of tile j interleaved
+// with the row max of tile j+1.  K runs one tile ahead of V in
+// double-buffered LDS; the loop is unrolled by two so buffer slots are
+// compile-time constants.
 //
 // Softmax: logits in log2 units (scale * log2 e folded into one FMA before
 // v_exp_f32).  A row's reference maximum m only rises when a tile's maximum
@@ -43,22 +52,31 @@ typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef i16x4_t __attribute__((address_space(3))) * lds_i16x4_ptr;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 constexpr float kTau = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int32_t kRecords = 0x40000000;   // buffer range of one key tile (bytes)
 
-template <int D, int QB, int BN>
+// XOR swizzle of the 16-byte chunks of LDS row r: a permutation of the
+// row's chunks.  It is the same for rows r, r + 16 and r + 32, which keeps
+// the operand addresses of different 16/32-key blocks a constant apart.
+template <int D> __device__ __forceinline__ int chunk_swz(int r);
+template <> __device__ __forceinline__ int chunk_swz<64>(int r) { return (5 * (r >> 1)) & 7; }
+template <> __device__ __forceinline__ int chunk_swz<96>(int r) { return (r >> 2) & 3; }
+template <> __device__ __forceinline__ int chunk_swz<128>(int r) { return (5 * r) & 15; }
+
+template <int D, int QB, int BN, int NW>
 struct AttnCfg {
-  static constexpr int NW = 4;
   static constexpr int NT = NW * 64;
   static constexpr int BM = NW * 32 * QB;
-  static constexpr int KP = D + 8;              // LDS row pitch (bf16): 16 * odd bytes
-  static constexpr int TILE = BN * KP;          // elements of one K or V tile
-  static constexpr int KCH = D / 8;             // 16-byte chunks per row
-  static constexpr int CH = BN * KCH;           // chunks per tile
-  static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
-  static_assert(CH % 128 == 0, "each half of the workgroup loads whole chunks");
-  static_assert(((KP * 2 / 16) & 1) == 1, "row pitch must be 16 * odd bytes");
+  static constexpr int KCH = D / 8;               // 16-byte chunks per row
+  static constexpr int CH = BN * KCH;             // chunks per tile
+  static constexpr int TILE = BN * D;             // bf16 elements of one K or V tile
+  static constexpr int DPT = CH / 64;             // 64-lane DMA loads per tile
+  static constexpr int DPW = (2 * DPT + NW - 1) / NW;   // per wave, K and V together
+  static constexpr int SPT = (2 * CH + NT - 1) / NT;    // staged chunks per thread
+  static_assert(D % 32 == 0 && BN % 32 == 0 && CH % 64 == 0, "tile shape");
 };
 
 // LDS for the RoPE rates and cos/sin table, only when a loader rotates.
@@ -72,6 +90,7 @@ template <> struct RopeSmem<false> {
 };
 
 template <bool B> using bool_c = std::integral_constant<bool, B>;
+template <int I> using int_c = std::integral_constant<int, I>;
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
@@ -88,18 +107,31 @@ __device__ __forceinline__ float sum_pair32(float x) {
 }
 
 // ROPE_Q / ROPE_K: rotate Q / K in the loaders (false = already rotated).
-template <int D, int QB, int BN, bool ROPE_Q, bool ROPE_K>
-__global__ __launch_bounds__(256) void attn3d_fwd_kernel(const AttnArgs a) {
-  using C = AttnCfg<D, QB, BN>;
+// FIXED_ROWS: the row -> token offsets inside a key tile are the same for
+// every tile (full, single skip, or group skip with BN a multiple of k).
+// OCC: waves per SIMD the register budget is sized for.
+template <int D, int QB, int BN, int NW, int OCC, bool ROPE_Q, bool ROPE_K, bool FIXED_ROWS>
+__global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs a) {
+  using C = AttnCfg<D, QB, BN, NW>;
   constexpr int NKB = BN / 32;        // 32-key blocks per tile
-  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2 * C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2 * C::TILE];
+  // K and V tiles, two slots each; separate arrays so that the compiler can
+  // see that an LDS DMA into one slot does not touch the slot being read
+  __shared__ __attribute__((aligned(1024))) uint16_t k_s0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_s1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_s0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_s1[C::TILE];
+  auto kslot = [&](auto sl) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (decltype(sl)::value == 0) return k_s0; else return k_s1;
+  };
+  auto vslot = [&](auto sl) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (decltype(sl)::value == 0) return v_s0; else return v_s1;
+  };
   __shared__ __attribute__((aligned(16))) RopeSmem<ROPE_Q || ROPE_K> rsm;
   RopeLds* const rl = rsm.get();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;      // half of the wave
   const int l32 = lane & 31;
 
@@ -156,84 +188,107 @@ __global__ __launch_bounds__(256) void attn3d_fwd_kernel(const AttnArgs a) {
     }
   }
 
-  // ---- loaders.  Each tile's K and V are fetched by the two halves of
-  // the workgroup (waves 0-1 and 2-3), which swap roles every tile so that
-  // K rotation work alternates.  Tile kt's first row r0 = kt*BN maps to
-  // token i0(kt); the remap is increasing in the row, and when BN is a
-  // multiple of the group-skip ratio (or the mode is full / single skip),
-  // row r0 + row maps to i0(kt) + drow(row): every thread's byte offsets
-  // are fixed and only the tile base moves.  Loads go through a buffer descriptor whose range ends
-  // at kRecords, so rows past the end of the subsequence (offset kRecords)
-  // read as zeros without a branch.
-  constexpr int LDPT = C::CH / 128;
-  constexpr int32_t kRecords = 0x40000000;
-  const int half = __builtin_amdgcn_readfirstlane(tid >> 7);
-  const int rt = tid & 127;
+  // ---- loaders.  Tile kt's first row r0 = kt*BN maps to token i0(kt); the
+  // remap is increasing in the row, and with FIXED_ROWS row r0 + row maps
+  // to i0(kt) + drow(row), so per-lane byte offsets are fixed and only the
+  // tile base moves.  K of tile kt goes to K slot kt&1, V to V slot kt&1.
   const int kmul = (mode == MODE_FULL) ? 1 : int(divk.d);
-  const bool fixed_rows = (mode != MODE_GROUP) || (BN % kmul == 0);
-  int ld_row[LDPT], ld_col[LDPT];
-  uint32_t ld_drow[LDPT];
-  int32_t ld_off[LDPT];
-  ChunkCol ld_rc[LDPT];
-#pragma unroll
-  for (int e = 0; e < LDPT; ++e) {
-    const int idx = rt + 128 * e;
-    ld_row[e] = idx / C::KCH;
-    ld_col[e] = idx % C::KCH;
-    const uint32_t rw = uint32_t(ld_row[e]);
-    ld_drow[e] = (mode == MODE_FULL) ? rw
-               : (mode == MODE_SINGLE) ? rw * uint32_t(kmul)
-               : (rw / uint32_t(kmul)) * uint32_t(kmul * kmul) + rw % uint32_t(kmul);
-    ld_off[e] = int32_t((int64_t(ld_drow[e]) * a_sn + 8 * ld_col[e]) * 2);
-    if constexpr (ROPE_K) ld_rc[e] = chunk_col(rg, 4 * ld_col[e]);
-  }
+  auto drow_of = [&](int rw) __attribute__((always_inline)) -> uint32_t {
+    const uint32_t r = uint32_t(rw);
+    return (mode == MODE_FULL) ? r
+         : (mode == MODE_SINGLE) ? r * uint32_t(kmul)
+         : (r / uint32_t(kmul)) * uint32_t(kmul * kmul) + r % uint32_t(kmul);
+  };
 
-  uint4 ld_reg[LDPT];
-  // Issue this thread's loads: the half whose index equals the tile
-  // parity fetches K of tile kt_k, the other half V of tile kt_v (-1: none).
-  auto issue_loads = [&](int kt_k, int kt_v, int parity) __attribute__((always_inline)) {
-    const bool do_k = half == parity;
-    const int kt = do_k ? kt_k : kt_v;
-    if (kt < 0) return;
-    const uint32_t i0 = skiparse_token(mode, uint32_t(kt * BN), j, divk);
-    const uint16_t* tb = (do_k ? kg : vg) + int64_t(i0) * a_sn;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(tb), (short)0, kRecords, 0x00020000);
-    const int rem = L - kt * BN;
+  // DMA path: wave w issues loads t = 0..DPW-1 with index i = w + NW*t
+  // (K tile block i if i < DPT, else V tile block i - DPT).
+  int32_t dm_off[C::DPW];
+  int dm_row[C::DPW], dm_col[C::DPW];
 #pragma unroll
-    for (int e = 0; e < LDPT; ++e) {
-      int32_t off = ld_off[e];
-      if (!fixed_rows) {
-        const uint32_t r = uint32_t(min(kt * BN + ld_row[e], L - 1));
-        off = int32_t((int64_t(skiparse_token(mode, r, j, divk) - i0) * a_sn + 8 * ld_col[e]) * 2);
+  for (int t = 0; t < C::DPW; ++t) {
+    const int i = wave + NW * t;
+    const int blk = (i < C::DPT) ? i : i - C::DPT;
+    const int p = 64 * blk + lane;
+    dm_row[t] = p / C::KCH;
+    dm_col[t] = (p % C::KCH) ^ chunk_swz<D>(dm_row[t]);    // logical chunk
+    dm_off[t] = int32_t((int64_t(drow_of(dm_row[t])) * a_sn + 8 * dm_col[t]) * 2);
+  }
+  // first token of tile kt: with FIXED_ROWS, i0(kt) = kt*BN*kmul + c_j
+  const int64_t tile_c0 = (mode == MODE_SINGLE) ? int64_t(j)
+                        : (mode == MODE_GROUP) ? int64_t(j) * kmul : 0;
+  auto tile_first = [&](int kt) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (FIXED_ROWS) return uint32_t(int64_t(kt) * BN * kmul + tile_c0);
+    else return skiparse_token(mode, uint32_t(kt * BN), j, divk);
+  };
+  auto dma_issue = [&](int kt_k, int kt_v, auto slot_k, auto slot_v, auto hk, auto hv)
+      __attribute__((always_inline)) {
+    constexpr bool HK = decltype(hk)::value, HV = decltype(hv)::value;
+    const uint32_t i0k = HK ? tile_first(kt_k) : 0u, i0v = HV ? tile_first(kt_v) : 0u;
+    const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kg + int64_t(i0k) * a_sn), (short)0, kRecords, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vg + int64_t(i0v) * a_sn), (short)0, kRecords, 0x00020000);
+#pragma unroll
+    for (int t = 0; t < C::DPW; ++t) {
+      const int i = wave + NW * t;
+      if (i >= 2 * C::DPT) continue;
+      const bool is_k = i < C::DPT;
+      if (is_k ? !HK : !HV) continue;
+      const int kt = is_k ? kt_k : kt_v;
+      const int blk = is_k ? i : i - C::DPT;
+      int32_t off = dm_off[t];
+      if constexpr (!FIXED_ROWS) {
+        const uint32_t r = uint32_t(min(kt * BN + dm_row[t], L - 1));
+        off = int32_t((int64_t(skiparse_token(mode, r, j, divk) - (is_k ? i0k : i0v)) * a_sn +
+                       8 * dm_col[t]) * 2);
       }
-      off = (ld_row[e] < rem) ? off : kRecords;
-      ld_reg[e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+      off = (dm_row[t] < L - kt * BN) ? off : kRecords;
+      uint16_t* dst = (is_k ? kslot(slot_k) : vslot(slot_v)) + 512 * blk;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_k ? rsk : rsv, (lds_void_ptr)dst, 16, off, 0, 0, 0);
     }
   };
-  // Store the staged chunks into LDS (rotating K when fused).
-  auto store_loads = [&](int kt_k, int kt_v, int parity) __attribute__((always_inline)) {
-    const bool do_k = half == parity;
-    const int kt = do_k ? kt_k : kt_v;
-    if (kt < 0) return;
-    uint16_t* dst = (do_k ? kbuf : vbuf) + (kt & 1) * C::TILE;
-    const uint32_t i0 = skiparse_token(mode, uint32_t(kt * BN), j, divk);
+
+  // Staged path (K rotated in the loader): thread chunks idx = tid + NT*e,
+  // K chunk idx if idx < CH, else V chunk idx - CH.
+  uint4 st_reg[ROPE_K ? C::SPT : 1];
+  auto staged_issue = [&](int kt_k, int kt_v, auto hk, auto hv) __attribute__((always_inline)) {
+    constexpr bool HK = decltype(hk)::value, HV = decltype(hv)::value;
 #pragma unroll
-    for (int e = 0; e < LDPT; ++e) {
-      uint4 val = ld_reg[e];
-      if constexpr (ROPE_K) {
-        if (do_k) {
-          const int r = kt * BN + ld_row[e];
-          const uint32_t i = fixed_rows ? i0 + ld_drow[e]
-                                        : skiparse_token(mode, uint32_t(min(r, L - 1)), j, divk);
-          if (r < L && is_video(rg, i)) {
-            const Coord3 cc = video_coords(rg, i);
-            val = fast_rope ? rotate_chunk_col(rl, ld_rc[e], cc, val)
-                            : rotate_chunk_tab(rg, rl, 4 * ld_col[e], cc, val);
-          }
+    for (int e = 0; e < C::SPT; ++e) {
+      const int idx = tid + C::NT * e;
+      const bool is_k = idx < C::CH;
+      const int ci = is_k ? idx : idx - C::CH;
+      const int row = ci / C::KCH, col = ci % C::KCH;
+      const int kt = is_k ? kt_k : kt_v;
+      const bool on = idx < 2 * C::CH && (is_k ? HK : HV) && kt * BN + row < L;
+      const uint32_t r = uint32_t(min(kt * BN + row, L - 1));
+      const uint32_t i = skiparse_token(mode, on ? r : 0u, j, divk);
+      st_reg[e] = on ? ld16((is_k ? kg : vg) + int64_t(i) * a_sn + 8 * col) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto staged_store = [&](int kt_k, int kt_v, auto slot_k, auto slot_v, auto hk, auto hv)
+      __attribute__((always_inline)) {
+    constexpr bool HK = decltype(hk)::value, HV = decltype(hv)::value;
+#pragma unroll
+    for (int e = 0; e < C::SPT; ++e) {
+      const int idx = tid + C::NT * e;
+      const bool is_k = idx < C::CH;
+      const int ci = is_k ? idx : idx - C::CH;
+      const int row = ci / C::KCH, col = ci % C::KCH;
+      if (idx >= 2 * C::CH || !(is_k ? HK : HV)) continue;
+      const int kt = is_k ? kt_k : kt_v;
+      uint4 val = st_reg[e];
+      if (is_k) {
+        const int r = kt * BN + row;
+        const uint32_t i = skiparse_token(mode, uint32_t(min(r, L - 1)), j, divk);
+        if (r < L && is_video(rg, i)) {
+          const Coord3 cc = video_coords(rg, i);
+          val = fast_rope ? rotate_chunk_col(rl, chunk_col(rg, 4 * col), cc, val)
+                          : rotate_chunk_tab(rg, rl, 4 * col, cc, val);
         }
       }
-      *reinterpret_cast<uint4*>(dst + ld_row[e] * C::KP + 8 * ld_col[e]) = val;
+      uint16_t* dst = is_k ? kslot(slot_k) : vslot(slot_v);
+      *reinterpret_cast<uint4*>(dst + 8 * (row * C::KCH + (col ^ chunk_swz<D>(row)))) = val;
     }
   };
 
@@ -250,9 +305,30 @@ __global__ __launch_bounds__(256) void attn3d_fwd_kernel(const AttnArgs a) {
       for (int e = 0; e < 16; ++e) o[qb][db][e] = 0.f;
   }
 
-  // S^T of tile kt into s (LDS buffer kt & 1)
-  auto qk = [&](int kt, f32x16_t (&s)[NKB][QB]) __attribute__((always_inline)) {
-    const uint16_t* ks = kbuf + (kt & 1) * C::TILE;
+  // per-lane LDS byte offsets of the operand reads (swizzle folded in)
+  int k_off[D / 16];
+  {
+    const int hsw = g ^ chunk_swz<D>(l32);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) k_off[c] = (l32 * C::KCH + ((2 * c) ^ hsw)) * 16;
+  }
+  int v_off[2][D / 32];
+  {
+    const int G = lane >> 4, s16 = lane & 15;
+    const int ta = s16 & 3, te = s16 >> 2;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int key = 4 * (G >> 1) + te + 8 * s;
+        const int chunk = 4 * db + 2 * (G & 1) + (ta >> 1);
+        v_off[s][db] = (key * C::KCH + (chunk ^ chunk_swz<D>(key))) * 16 + 8 * (ta & 1);
+      }
+  }
+
+  // S^T of the K tile in slot SK into s
+  auto qk = [&](auto slot, f32x16_t (&s)[NKB][QB]) __attribute__((always_inline)) {
+    const char* ks = reinterpret_cast<const char*>(kslot(slot));
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -263,8 +339,7 @@ __global__ __launch_bounds__(256) void attn3d_fwd_kernel(const AttnArgs a) {
     for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(
-            ks + (32 * kb + l32) * C::KP + 16 * c + 8 * g);
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(ks + 32 * kb * C::KCH * 16 + k_off[c]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], s[kb][qb], 0, 0, 0);
@@ -298,7 +373,9 @@ __global__ __launch_bounds__(256) void attn3d_fwd_kernel(const AttnArgs a) {
       zmax[qb] = max_pair32(mx) * c2;
       need |= zmax[qb] > mref[qb] + kTau;
     }
-    if (__ballot(need)) {
+    if (__builtin_expect(__ballot(need) != 0, 0)) {
+      // rare after the first tiles; keep it a branch (no speculation)
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float mnew = (zmax[qb] > mref[qb] + kTau) ? zmax[qb] : mref[qb];
@@ -337,24 +414,22 @@ __global__ __launch_bounds__(256) void attn3d_fwd_kernel(const AttnArgs a) {
       lsum[qb] += acc;
     }
   };
-  // O^T += V^T P^T for tile kt (V LDS buffer kt & 1)
-  auto pv = [&](int kt, bf16x8_t (&pb)[QB][NKB][2]) __attribute__((always_inline)) {
-    const uint16_t* vs = vbuf + (kt & 1) * C::TILE;
-    const int G = lane >> 4, s16 = lane & 15;
-    const int ta = s16 & 3, te = s16 >> 2;
+  // O^T += V^T P^T for the V tile in slot SV.  Source lane (ta, te) of its
+  // 16-lane group G points at key 32kb + 16hh + 4(G/2) + te (+8), channels
+  // 32db + 16(G%2) + 4ta .. +3; the transposing read hands each lane 4 keys
+  // of one channel.
+  auto pv = [&](auto slot, bf16x8_t (&pb)[QB][NKB][2]) __attribute__((always_inline)) {
+    const char* vs = reinterpret_cast<const char*>(vslot(slot));
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         bf16x8_t va[D / 32];
+        const char* blk = vs + (32 * kb + 16 * hh) * C::KCH * 16;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          // source lane (ta, te) of its 16-lane group points at key
-          // 32kb + 16hh + 4g + te (+8), channels 32db + 16(G%2) + 4ta .. +3
-          const uint16_t* src = vs + (32 * kb + 16 * hh + 4 * (G >> 1) + te) * C::KP +
-                                32 * db + 16 * (G & 1) + 4 * ta;
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(src));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(src + 8 * C::KP));
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(blk + v_off[0][db]));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(blk + v_off[1][db]));
           const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
           va[db] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
         }
@@ -366,60 +441,75 @@ __global__ __launch_bounds__(256) void attn3d_fwd_kernel(const AttnArgs a) {
       }
   };
 
-  // ---- prologue: K0, V0 (and K1) into LDS, S of tile 0
+  // issue / complete the loads of K tile kt_k into K slot SK and V tile kt_v
+  // into V slot SV (HK / HV: whether those tiles exist)
+  auto load_issue = [&](int kt_k, int kt_v, auto sk, auto sv, auto hk, auto hv) __attribute__((always_inline)) {
+    if constexpr (ROPE_K) staged_issue(kt_k, kt_v, hk, hv);
+    else dma_issue(kt_k, kt_v, sk, sv, hk, hv);
+  };
+  auto load_finish = [&](int kt_k, int kt_v, auto sk, auto sv, auto hk, auto hv) __attribute__((always_inline)) {
+    if constexpr (ROPE_K) staged_store(kt_k, kt_v, sk, sv, hk, hv);
+  };
+
+  // ---- prologue: K0, V0 and K1 into LDS, S of tile 0
   f32x16_t sA[NKB][QB], sB[NKB][QB];
-  issue_loads(0, 0, 0);
-  store_loads(0, 0, 0);
+  load_issue(0, 0, int_c<0>{}, int_c<0>{}, bool_c<true>{}, bool_c<true>{});
+  load_finish(0, 0, int_c<0>{}, int_c<0>{}, bool_c<true>{}, bool_c<true>{});
   if (nkt > 1) {
-    issue_loads(1, -1, 0);
-    store_loads(1, -1, 0);
+    load_issue(1, 0, int_c<1>{}, int_c<0>{}, bool_c<true>{}, bool_c<false>{});
+    load_finish(1, 0, int_c<1>{}, int_c<0>{}, bool_c<true>{}, bool_c<false>{});
   }
   __syncthreads();
-  qk(0, sA);
+  qk(int_c<0>{}, sA);
   if (nkt == 1 && L % BN) mask(0, sA);
   update_max(sA);
-  __syncthreads();   // K0's buffer is refilled with K2 in the first iteration
+  __syncthreads();   // K slot 0 is refilled with K2 in the first iteration
 
-  // ---- main loop.  Iteration jt: S(jt+1) with exp(jt); PV(jt) with
-  // max(jt+1); stores K(jt+2), V(jt+1).  The two score arrays alternate.
-  auto step = [&](int jt, f32x16_t (&s_cur)[NKB][QB], f32x16_t (&s_nxt)[NKB][QB],
+  // ---- main loop.  Iteration jt (slot P = jt & 1): S(jt+1) from K slot
+  // P^1 with exp(jt); PV(jt) from V slot P with max(jt+1); loads K(jt+2)
+  // into K slot P and V(jt+1) into V slot P^1.
+  auto step = [&](int jt, f32x16_t (&s_cur)[NKB][QB], f32x16_t (&s_nxt)[NKB][QB], auto slot,
                   auto has_next, auto load_k2, auto mask_next) __attribute__((always_inline)) {
+    constexpr int P = decltype(slot)::value;
     constexpr bool HAS_NEXT = decltype(has_next)::value;
-    constexpr bool LOAD_K2 = decltype(load_k2)::value;
     constexpr bool MASK_NEXT = decltype(mask_next)::value;
-    const int parity = jt & 1;
-    if constexpr (HAS_NEXT) issue_loads(LOAD_K2 ? jt + 2 : -1, jt + 1, parity);
+    if constexpr (HAS_NEXT)
+      load_issue(jt + 2, jt + 1, int_c<P>{}, int_c<P ^ 1>{}, load_k2, bool_c<true>{});
     bf16x8_t pb[QB][NKB][2];
-    if constexpr (HAS_NEXT) qk(jt + 1, s_nxt);
+    if constexpr (HAS_NEXT) qk(int_c<P ^ 1>{}, s_nxt);
     softmax(s_cur, pb);
     if constexpr (MASK_NEXT) mask(jt + 1, s_nxt);
-    pv(jt, pb);
+    pv(int_c<P>{}, pb);
     if constexpr (HAS_NEXT) {
-      store_loads(LOAD_K2 ? jt + 2 : -1, jt + 1, parity);
+      load_finish(jt + 2, jt + 1, int_c<P>{}, int_c<P ^ 1>{}, load_k2, bool_c<true>{});
       update_max(s_nxt);
       __syncthreads();
     }
   };
-  // the last tiles, starting at tile jt whose scores are in s_cur
-  auto tail = [&](int jt, f32x16_t (&s_cur)[NKB][QB], f32x16_t (&s_nxt)[NKB][QB]) __attribute__((always_inline)) {
+  // the last tiles, starting at tile jt (slot P) whose scores are in s_cur
+  auto tail = [&](int jt, f32x16_t (&s_cur)[NKB][QB], f32x16_t (&s_nxt)[NKB][QB], auto slot)
+      __attribute__((always_inline)) {
+    constexpr int P = decltype(slot)::value;
     if (jt + 1 < nkt) {
-      if (L % BN) step(jt, s_cur, s_nxt, bool_c<true>{}, bool_c<false>{}, bool_c<true>{});
-      else step(jt, s_cur, s_nxt, bool_c<true>{}, bool_c<false>{}, bool_c<false>{});
-      step(jt + 1, s_nxt, s_cur, bool_c<false>{}, bool_c<false>{}, bool_c<false>{});
+      if (L % BN)
+        step(jt, s_cur, s_nxt, int_c<P>{}, bool_c<true>{}, bool_c<false>{}, bool_c<true>{});
+      else
+        step(jt, s_cur, s_nxt, int_c<P>{}, bool_c<true>{}, bool_c<false>{}, bool_c<false>{});
+      step(jt + 1, s_nxt, s_cur, int_c<P ^ 1>{}, bool_c<false>{}, bool_c<false>{}, bool_c<false>{});
     } else {
-      step(jt, s_cur, s_nxt, bool_c<false>{}, bool_c<false>{}, bool_c<false>{});
+      step(jt, s_cur, s_nxt, int_c<P>{}, bool_c<false>{}, bool_c<false>{}, bool_c<false>{});
     }
   };
   int jt = 0;
   for (; jt + 3 < nkt; jt += 2) {
-    step(jt, sA, sB, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
-    step(jt + 1, sB, sA, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
+    step(jt, sA, sB, int_c<0>{}, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
+    step(jt + 1, sB, sA, int_c<1>{}, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
   }
   if (jt + 2 < nkt) {
-    step(jt, sA, sB, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
-    tail(jt + 1, sB, sA);
+    step(jt, sA, sB, int_c<0>{}, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
+    tail(jt + 1, sB, sA, int_c<1>{});
   } else {
-    tail(jt, sA, sB);
+    tail(jt, sA, sB, int_c<0>{});
   }
 
   // ---- epilogue: O = O^T / l, stored at the original token row ----
@@ -446,11 +536,25 @@ __global__ __launch_bounds__(256) void attn3d_fwd_kernel(const AttnArgs a) {
   }
 }
 
-// Tile shape per head_dim: 32-row query blocks per wave, keys per tile.
+// Tile shape per head_dim: 32-row query blocks per wave (QB), keys per
+// tile (BN), waves per workgroup (NW), waves per SIMD (OCC).  Build-time
+// overridable for tuning.
+#ifndef OSP_D64_TILE
+#define OSP_D64_TILE 1, 32, 8, 2
+#endif
+#ifndef OSP_D96_TILE
+#define OSP_D96_TILE 1, 32, 8, 2
+#endif
+#ifndef OSP_D128_TILE
+#define OSP_D128_TILE 1, 32, 8, 2
+#endif
+template <int QB_, int BN_, int NW_, int OCC_> struct TileShape {
+  static constexpr int QB = QB_, BN = BN_, NW = NW_, OCC = OCC_;
+};
 template <int D> struct TileCfg;
-template <> struct TileCfg<64> { static constexpr int QB = 2, BN = 32; };
-template <> struct TileCfg<96> { static constexpr int QB = 2, BN = 32; };
-template <> struct TileCfg<128> { static constexpr int QB = 1, BN = 32; };
+template <> struct TileCfg<64> : TileShape<OSP_D64_TILE> {};
+template <> struct TileCfg<96> : TileShape<OSP_D96_TILE> {};
+template <> struct TileCfg<128> : TileShape<OSP_D128_TILE> {};
 
 int attn_keys_per_tile(int head_dim) {
   switch (head_dim) {
@@ -463,26 +567,31 @@ int attn_keys_per_tile(int head_dim) {
 
 int attn_rows_per_block(int head_dim) {
   switch (head_dim) {
-    case 64: return AttnCfg<64, TileCfg<64>::QB, TileCfg<64>::BN>::BM;
-    case 96: return AttnCfg<96, TileCfg<96>::QB, TileCfg<96>::BN>::BM;
-    case 128: return AttnCfg<128, TileCfg<128>::QB, TileCfg<128>::BN>::BM;
+    case 64: return TileCfg<64>::NW * 32 * TileCfg<64>::QB;
+    case 96: return TileCfg<96>::NW * 32 * TileCfg<96>::QB;
+    case 128: return TileCfg<128>::NW * 32 * TileCfg<128>::QB;
     default: return 0;
   }
 }
 
+template <int D, bool FIXED>
+static hipError_t launch_df(const AttnArgs& a, int rope_q, int rope_k, hipStream_t s) {
+  using T = TileCfg<D>;
+  dim3 grid(a.total_tiles), block(T::NW * 64);
+#define OSP_LAUNCH(RQ, RK) \
+  hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, RQ, RK, FIXED>), grid, block, 0, s, a)
+  if (rope_q && rope_k) OSP_LAUNCH(true, true);
+  else if (rope_q) OSP_LAUNCH(true, false);
+  else if (rope_k) OSP_LAUNCH(false, true);
+  else OSP_LAUNCH(false, false);
+#undef OSP_LAUNCH
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_d(const AttnArgs& a, int rope_q, int rope_k, hipStream_t s) {
-  using T = TileCfg<D>;
-  dim3 grid(a.total_tiles), block(256);
-  if (rope_q && rope_k)
-    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, true, true>), grid, block, 0, s, a);
-  else if (rope_q)
-    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, true, false>), grid, block, 0, s, a);
-  else if (rope_k)
-    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, false, true>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, false, false>), grid, block, 0, s, a);
-  return hipGetLastError();
+  const bool fixed = a.mode != MODE_GROUP || TileCfg<D>::BN % int(a.divk.d) == 0;
+  return fixed ? launch_df<D, true>(a, rope_q, rope_k, s) : launch_df<D, false>(a, rope_q, rope_k, s);
 }
 
 hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_q, int rope_k, hipStream_t s) {
