@@ -63,7 +63,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-skiparse", action="store_true", help="skip the Skiparse k=4 lines")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=2,
+    p.add_argument("--cpu-heads", type=int, default=6,
                    help="heads of the workload the oracle times (all query rows each)")
     p.add_argument("--profile", action="store_true",
                    help="few steps of the full-attention workload only (for rocprofv3)")
@@ -211,7 +211,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": "attn3d_fwd_kernel<96, QB=2, BN=32, rope_q, fixed_rows>",
+                     "kernel": "attn3d_fwd_kernel<D=96, QB=1, BN=64, NW=8, OCC=2, rope_q, fixed_rows>",
                      "flop_per_launch": f_full, "ms_per_launch": round(ms_launch, 4),
                      "ms_median": round(ms_med, 4), "ms_min": round(ms_min, 4)},
         "skiparse": extra,

@@ -123,10 +123,13 @@ osp_status osp_rope3d(const osp_attn3d_desc* desc, const void* x, void* y,
    equals full attention.  The k subsequences are attended independently
    and each output row is written back at its token's original position.
    sm_scale: logit scale; <= 0 selects 1/sqrt(head_dim).
-   flags: OSP_FUSE_ROPE_Q / OSP_FUSE_ROPE_K rotate Q / K in the loaders
-   (exactly as osp_rope3d would, then bf16); a tensor whose flag is clear
-   must already be rotated.  Every combination gives bit-identical results
-   for the same rotated values.  OSP_FUSE_ROPE_K needs the per-axis cos/sin
+   flags: OSP_FUSE_ROPE_Q / OSP_FUSE_ROPE_K rotate Q / K in the loaders; a
+   tensor whose flag is clear must already be rotated.  K is rotated
+   exactly as osp_rope3d would (then bf16), so results do not depend on
+   OSP_FUSE_ROPE_K.  Q is multiplied by sm_scale * log2(e) in the loader
+   and rounded to bf16: with OSP_FUSE_ROPE_Q the rotation and the scaling
+   share that one rounding, without it the already rotated bf16 Q is
+   rounded a second time.  OSP_FUSE_ROPE_K needs the per-axis cos/sin
    table in LDS: grid_t*rope_t + grid_h*rope_h + grid_w*rope_w <= 6144
    (else OSP_ERR_UNSUPPORTED; rotate K with osp_rope3d instead).
    q, k, v: [B, N, H, D] bf16 read with stride_*; o: written with ostride_*,

@@ -35,12 +35,16 @@
 // double-buffered LDS; the loop is unrolled by two so buffer slots are
 // compile-time constants.
 //
-// Softmax: logits in log2 units (scale * log2 e folded into one FMA before
-// v_exp_f32).  A row's reference maximum m only rises when a tile's maximum
-// exceeds it by more than kTau (= 8, a factor 256), so the O rescale is
-// skipped for most tiles; probabilities stay <= 2^8 and O / l is unchanged
-// in exact arithmetic.  Row sums add the bf16-rounded probabilities (the
-// same values the PV product uses) with v_dot2c_f32_bf16.
+// Softmax: Q is multiplied by scale * log2(e) once (then bf16 again), so
+// scores come out in log2 units, and the first product of each score block
+// starts from -m instead of 0: the MFMA delivers z - m and v_exp_f32 takes
+// it as is (keys past the end of the last tile start from -inf).  A row's
+// reference maximum m is set by its first tile and afterwards only rises
+// when a tile's maximum exceeds it by more than kTau (= 8, a factor 256),
+// so the O rescale is skipped for most tiles; probabilities stay <= 2^8 and
+// O / l is unchanged in exact arithmetic.  Row sums add the bf16-rounded
+// probabilities (the same values the PV product uses) with
+// v_dot2c_f32_bf16.
 #include <type_traits>
 
 #include "osp_internal.hpp"
@@ -183,7 +187,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
       uint4 raw = valid ? ld16(p + 16 * c + 8 * g) : make_uint4(0, 0, 0, 0);
-      if (ROPE_Q && video) raw = rotate_chunk(rg, rl, 8 * c + 4 * g, cc, raw);
+      // times scale * log2(e) so that the score products come out in log2
+      // units; a rotated row is rotated and scaled in fp32, rounded once
+      if (ROPE_Q && video) {
+        raw = rotate_chunk_scaled(rg, rl, 8 * c + 4 * g, cc, raw, c2);
+      } else {
+        raw.x = pack_bf16(bf16lo(raw.x) * c2, bf16hi(raw.x) * c2);
+        raw.y = pack_bf16(bf16lo(raw.y) * c2, bf16hi(raw.y) * c2);
+        raw.z = pack_bf16(bf16lo(raw.z) * c2, bf16hi(raw.z) * c2);
+        raw.w = pack_bf16(bf16lo(raw.w) * c2, bf16hi(raw.w) * c2);
+      }
       qreg[qb][c] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
@@ -292,13 +305,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     }
   };
 
-  // ---- accumulators and softmax state
+  // ---- accumulators and softmax state.  Scores are kept relative to the
+  // row's reference maximum m (log2 units): the first product of each score
+  // block starts from negm = -m instead of 0.
   f32x16_t o[QB][D / 32];
+  f32x16_t negm[QB];
   float mref[QB], lsum[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    mref[qb] = -INFINITY;
+    mref[qb] = 0.f;
     lsum[qb] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) negm[qb][e] = 0.f;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -326,15 +344,25 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       }
   }
 
-  // S^T of the K tile in slot SK into s
-  auto qk = [&](auto slot, f32x16_t (&s)[NKB][QB]) __attribute__((always_inline)) {
+  // S^T - m of the K tile in slot SK into s; MASKED: keys of tile kt past
+  // the end of the subsequence start from -inf instead
+  auto qk = [&](auto slot, f32x16_t (&s)[NKB][QB], int kt, auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
     const char* ks = reinterpret_cast<const char*>(kslot(slot));
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int qb = 0; qb < QB; ++qb) {
+        if constexpr (MASKED) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[kb][qb][e] = 0.f;
+          for (int e = 0; e < 16; ++e) {
+            const int key = kt * BN + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+            s[kb][qb][e] = (key < L) ? negm[qb][e] : -INFINITY;
+          }
+        } else {
+          s[kb][qb] = negm[qb];
+        }
+      }
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
@@ -346,23 +374,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       }
     }
   };
-  // keys past the end of the subsequence in tile kt -> -inf
-  auto mask = [&](int kt, f32x16_t (&s)[NKB][QB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kt * BN + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-        if (key >= L) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[kb][qb][e] = -INFINITY;
-        }
-      }
-  };
-  // row max of a tile (scaled to log2 units), raise m where needed, rescale
-  auto update_max = [&](f32x16_t (&s)[NKB][QB]) __attribute__((always_inline)) {
-    float zmax[QB];
-    bool need = false;
+  // row max t of a tile's shifted scores; where t > kTau raise m by t and
+  // rescale (O, l, and this tile's scores).  FIRST: set m to the first
+  // tile's maximum whatever its sign.
+  auto update_max = [&](f32x16_t (&s)[NKB][QB], auto first) __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first)::value;
+    float tmax[QB];
+    bool need = FIRST;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
@@ -370,22 +388,30 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
-      zmax[qb] = max_pair32(mx) * c2;
-      need |= zmax[qb] > mref[qb] + kTau;
+      tmax[qb] = max_pair32(mx);
+      need |= tmax[qb] > kTau;
     }
-    if (__builtin_expect(__ballot(need) != 0, 0)) {
+    if (FIRST || __builtin_expect(__ballot(need) != 0, 0)) {
       // rare after the first tiles; keep it a branch (no speculation)
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float mnew = (zmax[qb] > mref[qb] + kTau) ? zmax[qb] : mref[qb];
-        const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mnew);
-        mref[qb] = mnew;
-        lsum[qb] *= alpha;
+        const float dm = (FIRST || tmax[qb] > kTau) ? tmax[qb] : 0.f;
+        mref[qb] += dm;
+        if constexpr (!FIRST) {
+          const float alpha = __builtin_amdgcn_exp2f(-dm);
+          lsum[qb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+          for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
+            for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[kb][qb][e] -= dm;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) negm[qb][e] = -mref[qb];
       }
     }
   };
@@ -394,7 +420,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     const bf16x2v_t one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float nm = -mref[qb];
       float acc = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -403,8 +428,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
           uint32_t w[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][8 * hh + 2 * t], c2, nm));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][8 * hh + 2 * t + 1], c2, nm));
+            const float p0 = __builtin_amdgcn_exp2f(s[kb][qb][8 * hh + 2 * t]);
+            const float p1 = __builtin_amdgcn_exp2f(s[kb][qb][8 * hh + 2 * t + 1]);
             w[t] = pack_bf16(p0, p1);
             acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[t]), one, acc,
                                                   false);
@@ -460,9 +485,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     load_finish(1, 0, int_c<1>{}, int_c<0>{}, bool_c<true>{}, bool_c<false>{});
   }
   __syncthreads();
-  qk(int_c<0>{}, sA);
-  if (nkt == 1 && L % BN) mask(0, sA);
-  update_max(sA);
+  if (nkt == 1 && L % BN) qk(int_c<0>{}, sA, 0, bool_c<true>{});
+  else qk(int_c<0>{}, sA, 0, bool_c<false>{});
+  update_max(sA, bool_c<true>{});
   __syncthreads();   // K slot 0 is refilled with K2 in the first iteration
 
   // ---- main loop.  Iteration jt (slot P = jt & 1): S(jt+1) from K slot
@@ -472,17 +497,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
                   auto has_next, auto load_k2, auto mask_next) __attribute__((always_inline)) {
     constexpr int P = decltype(slot)::value;
     constexpr bool HAS_NEXT = decltype(has_next)::value;
-    constexpr bool MASK_NEXT = decltype(mask_next)::value;
     if constexpr (HAS_NEXT)
       load_issue(jt + 2, jt + 1, int_c<P>{}, int_c<P ^ 1>{}, load_k2, bool_c<true>{});
     bf16x8_t pb[QB][NKB][2];
-    if constexpr (HAS_NEXT) qk(int_c<P ^ 1>{}, s_nxt);
+    if constexpr (HAS_NEXT) qk(int_c<P ^ 1>{}, s_nxt, jt + 1, mask_next);
     softmax(s_cur, pb);
-    if constexpr (MASK_NEXT) mask(jt + 1, s_nxt);
     pv(int_c<P>{}, pb);
     if constexpr (HAS_NEXT) {
       load_finish(jt + 2, jt + 1, int_c<P>{}, int_c<P ^ 1>{}, load_k2, bool_c<true>{});
-      update_max(s_nxt);
+      update_max(s_nxt, bool_c<false>{});
       __syncthreads();
     }
   };
@@ -540,13 +563,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
 // tile (BN), waves per workgroup (NW), waves per SIMD (OCC).  Build-time
 // overridable for tuning.
 #ifndef OSP_D64_TILE
-#define OSP_D64_TILE 1, 32, 8, 2
+#define OSP_D64_TILE 1, 64, 8, 2
 #endif
 #ifndef OSP_D96_TILE
-#define OSP_D96_TILE 1, 32, 8, 2
+#define OSP_D96_TILE 1, 64, 8, 2
 #endif
 #ifndef OSP_D128_TILE
-#define OSP_D128_TILE 1, 32, 8, 2
+#define OSP_D128_TILE 1, 32, 4, 1
 #endif
 template <int QB_, int BN_, int NW_, int OCC_> struct TileShape {
   static constexpr int QB = QB_, BN = BN_, NW = NW_, OCC = OCC_;

@@ -71,6 +71,15 @@ __device__ __forceinline__ uint32_t rotate_pair(uint32_t xy, float2 cs) {
   return pack_bf16(y0, y1);
 }
 
+// Rotate one packed bf16 pair, multiply by `scale` in fp32, repack (one
+// rounding).
+__device__ __forceinline__ uint32_t rotate_pair_scaled(uint32_t xy, float2 cs, float scale) {
+  float x0 = bf16lo(xy), x1 = bf16hi(xy);
+  float y0 = fmaf(x0, cs.x, -(x1 * cs.y));
+  float y1 = fmaf(x0, cs.y, x1 * cs.x);
+  return pack_bf16(y0 * scale, y1 * scale);
+}
+
 // Axis of head-dim pair p, its index r inside the axis chunk.
 __device__ __forceinline__ int pair_axis(const RopeGeom& g, int p, int* r) {
   const int a = (p < g.np0) ? 0 : (p < g.np0 + g.np1 ? 1 : 2);
@@ -133,6 +142,16 @@ __device__ __forceinline__ uint4 rotate_chunk(const RopeGeom& g, const RopeLds* 
   x.y = rotate_pair(x.y, pair_cs(g, s, p0 + 1, c));
   x.z = rotate_pair(x.z, pair_cs(g, s, p0 + 2, c));
   x.w = rotate_pair(x.w, pair_cs(g, s, p0 + 3, c));
+  return x;
+}
+
+// rotate_chunk with the result multiplied by `scale` before rounding.
+__device__ __forceinline__ uint4 rotate_chunk_scaled(const RopeGeom& g, const RopeLds* s, int p0,
+                                                     const Coord3& c, uint4 x, float scale) {
+  x.x = rotate_pair_scaled(x.x, pair_cs(g, s, p0 + 0, c), scale);
+  x.y = rotate_pair_scaled(x.y, pair_cs(g, s, p0 + 1, c), scale);
+  x.z = rotate_pair_scaled(x.z, pair_cs(g, s, p0 + 2, c), scale);
+  x.w = rotate_pair_scaled(x.w, pair_cs(g, s, p0 + 3, c), scale);
   return x;
 }
 
