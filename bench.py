@@ -66,7 +66,10 @@ def parse():
     p.add_argument("--cpu-heads", type=int, default=6,
                    help="heads of the workload the oracle times (all query rows each)")
     p.add_argument("--profile", action="store_true",
-                   help="few steps of the full-attention workload only (for rocprofv3)")
+                   help="few steps of one attention mode only (for rocprofv3)")
+    p.add_argument("--profile-mode", default="full",
+                   choices=("full", "skiparse_single", "skiparse_group"),
+                   help="attention mode of --profile (Skiparse with k=4)")
     p.add_argument("--copy", type=int, default=0,
                    help="instead: time a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -123,13 +126,15 @@ def main():
         return 4.0 * B * H * float(n_tok) ** 2 * D / sk
 
     if args.profile:
+        pm = args.profile_mode
+        pk = 1 if pm == "full" else 4
         for _ in range(max(args.warmup, 1)):
-            step()
+            step(pm, pk)
         torch.cuda.synchronize()
         for _ in range(max(args.steps, 1)):
-            step()
+            step(pm, pk)
         torch.cuda.synchronize()
-        print(json.dumps({"profile_launches": args.steps, "workload": "osp480 full"}))
+        print(json.dumps({"profile_launches": args.steps, "workload": f"osp480 {pm} k={pk}"}))
         return
 
     def timed(mode, sk, steps, warmup):
