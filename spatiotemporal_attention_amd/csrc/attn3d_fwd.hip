@@ -77,10 +77,12 @@ struct AttnCfg {
   static constexpr int KCH = D / 8;               // 16-byte chunks per row
   static constexpr int CH = BN * KCH;             // chunks per tile
   static constexpr int TILE = BN * D;             // bf16 elements of one K or V tile
+  static constexpr int LW = NW / 2;               // loading waves (the leading half)
+  static constexpr int LT = LW * 64;
   static constexpr int DPT = CH / 64;             // 64-lane DMA loads per tile
-  static constexpr int DPW = (2 * DPT + NW - 1) / NW;   // per wave, K and V together
-  static constexpr int SPT = (2 * CH + NT - 1) / NT;    // staged chunks per thread
-  static_assert(D % 32 == 0 && BN % 32 == 0 && CH % 64 == 0, "tile shape");
+  static constexpr int DPW = (2 * DPT + LW - 1) / LW;   // per loading wave, K and V together
+  static constexpr int SPT = (2 * CH + LT - 1) / LT;    // staged chunks per loading thread
+  static_assert(D % 32 == 0 && BN % 32 == 0 && CH % 64 == 0 && NW % 8 == 0, "tile shape");
 };
 
 // LDS for the RoPE rates and cos/sin table, only when a loader rotates.
@@ -114,6 +116,37 @@ __device__ __forceinline__ float sum_pair32(float x) {
 // FIXED_ROWS: the row -> token offsets inside a key tile are the same for
 // every tile (full, single skip, or group skip with BN a multiple of k).
 // OCC: waves per SIMD the register budget is sized for.
+// Scheduling groups of a matrix phase: NMK QK MFMAs (one LDS read each)
+// then NMV PV MFMAs (two reads each), in the program order of their reads
+// (the transposing V reads are not moved above other LDS reads).  The
+// reads of the first L MFMAs come first; after MFMA i come the reads of
+// MFMA i + L.
+template <int NMK, int NMV> __device__ constexpr int m_reads(int m) {
+  return m < NMK ? 1 : (m < NMK + NMV ? 2 : 0);
+}
+template <int NMK, int NMV, int L> __device__ constexpr int m_first_reads() {
+  int r = 0;
+  for (int m = 0; m < L; ++m) r += m_reads<NMK, NMV>(m);
+  return r;
+}
+template <int NMK, int NMV, int L, int I = 0>
+__device__ __forceinline__ void m_phase_order() {
+  if constexpr (I < NMK + NMV) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+    constexpr int r = m_reads<NMK, NMV>(I + L);
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);   // DS read
+    m_phase_order<NMK, NMV, L, I + 1>();
+  }
+}
+
+#ifndef OSP_M_LEAD
+#define OSP_M_LEAD 4
+#endif
+#ifndef OSP_LEAD_EXPR
+#define OSP_LEAD_EXPR (wave < NW / 2)
+#define OSP_LEAD_RANK (wave % (NW / 2))
+#endif
+
 template <int D, int QB, int BN, int NW, int OCC, bool ROPE_Q, bool ROPE_K, bool FIXED_ROWS>
 __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs a) {
   using C = AttnCfg<D, QB, BN, NW>;
@@ -136,6 +169,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool lead = OSP_LEAD_EXPR;   // leading half of the waves (they load)
+  const int lw = OSP_LEAD_RANK;      // rank inside the half
   const int g = lane >> 5;      // half of the wave
   const int l32 = lane & 31;
 
@@ -213,13 +248,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
          : (r / uint32_t(kmul)) * uint32_t(kmul * kmul) + r % uint32_t(kmul);
   };
 
-  // DMA path: wave w issues loads t = 0..DPW-1 with index i = w + NW*t
-  // (K tile block i if i < DPT, else V tile block i - DPT).
+  // DMA path: loading wave w issues loads t = 0..DPW-1 with index
+  // i = w + LW*t (K tile block i if i < DPT, else V tile block i - DPT).
   int32_t dm_off[C::DPW];
   int dm_row[C::DPW], dm_col[C::DPW];
 #pragma unroll
   for (int t = 0; t < C::DPW; ++t) {
-    const int i = wave + NW * t;
+    const int i = lw + C::LW * t;
     const int blk = (i < C::DPT) ? i : i - C::DPT;
     const int p = 64 * blk + lane;
     dm_row[t] = p / C::KCH;
@@ -243,7 +278,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
         const_cast<uint16_t*>(vg + int64_t(i0v) * a_sn), (short)0, kRecords, 0x00020000);
 #pragma unroll
     for (int t = 0; t < C::DPW; ++t) {
-      const int i = wave + NW * t;
+      const int i = lw + C::LW * t;
       if (i >= 2 * C::DPT) continue;
       const bool is_k = i < C::DPT;
       if (is_k ? !HK : !HV) continue;
@@ -261,14 +296,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     }
   };
 
-  // Staged path (K rotated in the loader): thread chunks idx = tid + NT*e,
-  // K chunk idx if idx < CH, else V chunk idx - CH.
+  // Staged path (K rotated in the loader): loading thread chunks
+  // idx = tid + LT*e, K chunk idx if idx < CH, else V chunk idx - CH.
   uint4 st_reg[ROPE_K ? C::SPT : 1];
   auto staged_issue = [&](int kt_k, int kt_v, auto hk, auto hv) __attribute__((always_inline)) {
     constexpr bool HK = decltype(hk)::value, HV = decltype(hv)::value;
 #pragma unroll
     for (int e = 0; e < C::SPT; ++e) {
-      const int idx = tid + C::NT * e;
+      const int idx = lw * 64 + lane + C::LT * e;
       const bool is_k = idx < C::CH;
       const int ci = is_k ? idx : idx - C::CH;
       const int row = ci / C::KCH, col = ci % C::KCH;
@@ -284,7 +319,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     constexpr bool HK = decltype(hk)::value, HV = decltype(hv)::value;
 #pragma unroll
     for (int e = 0; e < C::SPT; ++e) {
-      const int idx = tid + C::NT * e;
+      const int idx = lw * 64 + lane + C::LT * e;
       const bool is_k = idx < C::CH;
       const int ci = is_k ? idx : idx - C::CH;
       const int row = ci / C::KCH, col = ci % C::KCH;
@@ -374,13 +409,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       }
     }
   };
-  // row max t of a tile's shifted scores; where t > kTau raise m by t and
-  // rescale (O, l, and this tile's scores).  FIRST: set m to the first
-  // tile's maximum whatever its sign.
-  auto update_max = [&](f32x16_t (&s)[NKB][QB], auto first) __attribute__((always_inline)) {
-    constexpr bool FIRST = decltype(first)::value;
+  // Row max t of a tile's shifted scores; where t > kTau raise m by t and
+  // rescale (O, l, and this tile's scores).  first: the row's first tile,
+  // which sets m to its maximum whatever its sign.
+  auto update_max = [&](f32x16_t (&s)[NKB][QB], bool first) __attribute__((always_inline)) {
     float tmax[QB];
-    bool need = FIRST;
+    bool need = first;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
@@ -391,21 +425,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       tmax[qb] = max_pair32(mx);
       need |= tmax[qb] > kTau;
     }
-    if (FIRST || __builtin_expect(__ballot(need) != 0, 0)) {
-      // rare after the first tiles; keep it a branch (no speculation)
+    if (__builtin_expect(__ballot(need) != 0, 0)) {
+      // rare after the first tile; keep it a branch (no speculation)
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float dm = (FIRST || tmax[qb] > kTau) ? tmax[qb] : 0.f;
+        const float dm = (first || tmax[qb] > kTau) ? tmax[qb] : 0.f;
         mref[qb] += dm;
-        if constexpr (!FIRST) {
-          const float alpha = __builtin_amdgcn_exp2f(-dm);
-          lsum[qb] *= alpha;
+        const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-dm);
+        lsum[qb] *= alpha;
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
-        }
+          for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -476,64 +508,98 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     if constexpr (ROPE_K) staged_store(kt_k, kt_v, sk, sv, hk, hv);
   };
 
-  // ---- prologue: K0, V0 and K1 into LDS, S of tile 0
-  f32x16_t sA[NKB][QB], sB[NKB][QB];
-  load_issue(0, 0, int_c<0>{}, int_c<0>{}, bool_c<true>{}, bool_c<true>{});
-  load_finish(0, 0, int_c<0>{}, int_c<0>{}, bool_c<true>{}, bool_c<true>{});
-  if (nkt > 1) {
-    load_issue(1, 0, int_c<1>{}, int_c<0>{}, bool_c<true>{}, bool_c<false>{});
-    load_finish(1, 0, int_c<1>{}, int_c<0>{}, bool_c<true>{}, bool_c<false>{});
+  // ---- ping-pong schedule.  The waves form two halves, one wave of each
+  // on every SIMD.  Per key tile t a wave runs a matrix phase M(t) (S(t) =
+  // K(t) Q^T from K slot t&1, then O += PV(t-1) from V slot (t-1)&1) and a
+  // softmax phase V(t) (max, rescale, exp2, row sums of S(t) into P), each
+  // ended by a workgroup barrier.  The trailing half passes one barrier
+  // first and so runs one phase behind: on each SIMD one wave's MFMAs
+  // overlap the other wave's softmax.  Only the leading half loads.  At the
+  // start of its iteration t it issues K(t+1) into K slot (t+1)&1 and V(t)
+  // into V slot t&1 (their previous tiles were last read by the trailing
+  // half in the phase just ended) and waits for them at the iteration's
+  // end, one phase before their first reader.
+  const bool ragged = (L % BN) != 0;
+  f32x16_t s[NKB][QB];
+  bf16x8_t pb[QB][NKB][2];
+
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // the compiler tracks this wait (vmcnt(0) lgkmcnt(0)), so it knows the
+  // loaded tiles are complete when they are read in later phases
+  auto loads_done = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0070);
+  };
+  // matrix phase of tile t: QK(t) (QK) and PV(t-1) (PV); slot P = t & 1
+  // Instruction order inside it: the LDS reads run OSP_M_LEAD MFMAs ahead
+  // of the MFMAs that use them.
+  auto m_phase = [&](int t, auto slot, auto do_qk, auto do_pv, auto masked) __attribute__((always_inline)) {
+    constexpr int P = decltype(slot)::value;
+    constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (QK) qk(int_c<P>{}, s, t, masked);
+    if constexpr (PV) pv(int_c<P ^ 1>{}, pb);
+    if constexpr (QB == 1) {
+      constexpr int NMV = PV ? NKB * 2 * (D / 32) : 0, NMK = QK ? NKB * (D / 16) : 0;
+      __builtin_amdgcn_sched_group_barrier(0x100, m_first_reads<NMK, NMV, OSP_M_LEAD>(), 0);
+      m_phase_order<NMK, NMV, OSP_M_LEAD>();
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // one iteration (two phases) for tile t; HK: K(t+1) exists
+  auto iter = [&](int t, auto slot, auto do_pv, auto masked, auto hk) __attribute__((always_inline)) {
+    constexpr int P = decltype(slot)::value;
+    if (lead) load_issue(t + 1, t, int_c<P ^ 1>{}, int_c<P>{}, hk, bool_c<true>{});
+    m_phase(t, slot, bool_c<true>{}, do_pv, masked);
+    barrier();
+    update_max(s, t == 0);
+    softmax(s, pb);
+    if (lead) load_finish(t + 1, t, int_c<P ^ 1>{}, int_c<P>{}, hk, bool_c<true>{});
+    loads_done();   // a no-op for the trailing half, which loads nothing
+    barrier();
+  };
+  // the last tile t = nkt - 1 >= 1: masked when the subsequence is ragged
+  auto last = [&](int t, auto slot) __attribute__((always_inline)) {
+    if (ragged) iter(t, slot, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
+    else iter(t, slot, bool_c<true>{}, bool_c<false>{}, bool_c<false>{});
+  };
+  // the last matrix phase, PV of tile nkt - 1 (slot P = nkt & 1)
+  auto fin = [&](auto slot) __attribute__((always_inline)) {
+    m_phase(nkt, slot, bool_c<false>{}, bool_c<true>{}, bool_c<false>{});
+  };
+
+  // prologue: K(0) into K slot 0
+  if (lead) {
+    load_issue(0, 0, int_c<0>{}, int_c<0>{}, bool_c<true>{}, bool_c<false>{});
+    load_finish(0, 0, int_c<0>{}, int_c<0>{}, bool_c<true>{}, bool_c<false>{});
   }
   __syncthreads();
-  if (nkt == 1 && L % BN) qk(int_c<0>{}, sA, 0, bool_c<true>{});
-  else qk(int_c<0>{}, sA, 0, bool_c<false>{});
-  update_max(sA, bool_c<true>{});
-  __syncthreads();   // K slot 0 is refilled with K2 in the first iteration
-
-  // ---- main loop.  Iteration jt (slot P = jt & 1): S(jt+1) from K slot
-  // P^1 with exp(jt); PV(jt) from V slot P with max(jt+1); loads K(jt+2)
-  // into K slot P and V(jt+1) into V slot P^1.
-  auto step = [&](int jt, f32x16_t (&s_cur)[NKB][QB], f32x16_t (&s_nxt)[NKB][QB], auto slot,
-                  auto has_next, auto load_k2, auto mask_next) __attribute__((always_inline)) {
-    constexpr int P = decltype(slot)::value;
-    constexpr bool HAS_NEXT = decltype(has_next)::value;
-    if constexpr (HAS_NEXT)
-      load_issue(jt + 2, jt + 1, int_c<P>{}, int_c<P ^ 1>{}, load_k2, bool_c<true>{});
-    bf16x8_t pb[QB][NKB][2];
-    if constexpr (HAS_NEXT) qk(int_c<P ^ 1>{}, s_nxt, jt + 1, mask_next);
-    softmax(s_cur, pb);
-    pv(int_c<P>{}, pb);
-    if constexpr (HAS_NEXT) {
-      load_finish(jt + 2, jt + 1, int_c<P>{}, int_c<P ^ 1>{}, load_k2, bool_c<true>{});
-      update_max(s_nxt, bool_c<false>{});
-      __syncthreads();
-    }
-  };
-  // the last tiles, starting at tile jt (slot P) whose scores are in s_cur
-  auto tail = [&](int jt, f32x16_t (&s_cur)[NKB][QB], f32x16_t (&s_nxt)[NKB][QB], auto slot)
-      __attribute__((always_inline)) {
-    constexpr int P = decltype(slot)::value;
-    if (jt + 1 < nkt) {
-      if (L % BN)
-        step(jt, s_cur, s_nxt, int_c<P>{}, bool_c<true>{}, bool_c<false>{}, bool_c<true>{});
-      else
-        step(jt, s_cur, s_nxt, int_c<P>{}, bool_c<true>{}, bool_c<false>{}, bool_c<false>{});
-      step(jt + 1, s_nxt, s_cur, int_c<P ^ 1>{}, bool_c<false>{}, bool_c<false>{}, bool_c<false>{});
-    } else {
-      step(jt, s_cur, s_nxt, int_c<P>{}, bool_c<false>{}, bool_c<false>{}, bool_c<false>{});
-    }
-  };
-  int jt = 0;
-  for (; jt + 3 < nkt; jt += 2) {
-    step(jt, sA, sB, int_c<0>{}, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
-    step(jt + 1, sB, sA, int_c<1>{}, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
-  }
-  if (jt + 2 < nkt) {
-    step(jt, sA, sB, int_c<0>{}, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
-    tail(jt + 1, sB, sA, int_c<1>{});
+  if (!lead) barrier();
+  if (nkt == 1) {
+    if (ragged) iter(0, int_c<0>{}, bool_c<false>{}, bool_c<true>{}, bool_c<false>{});
+    else iter(0, int_c<0>{}, bool_c<false>{}, bool_c<false>{}, bool_c<false>{});
+    fin(int_c<1>{});
   } else {
-    tail(jt, sA, sB, int_c<0>{});
+    iter(0, int_c<0>{}, bool_c<false>{}, bool_c<false>{}, bool_c<true>{});
+    int t = 1;
+    for (; t + 2 < nkt; t += 2) {
+      iter(t, int_c<1>{}, bool_c<true>{}, bool_c<false>{}, bool_c<true>{});
+      iter(t + 1, int_c<0>{}, bool_c<true>{}, bool_c<false>{}, bool_c<true>{});
+    }
+    if (t + 1 < nkt) {
+      iter(t, int_c<1>{}, bool_c<true>{}, bool_c<false>{}, bool_c<true>{});
+      last(t + 1, int_c<0>{});
+      fin(int_c<1>{});
+    } else {
+      last(t, int_c<1>{});
+      fin(int_c<0>{});
+    }
   }
+  if (lead) barrier();   // the trailing half's last barrier
 
   // ---- epilogue: O = O^T / l, stored at the original token row ----
   uint16_t* og = a.o + int64_t(b) * a.osb + int64_t(h) * a.osh;
@@ -569,7 +635,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
 #define OSP_D96_TILE 1, 64, 8, 2
 #endif
 #ifndef OSP_D128_TILE
-#define OSP_D128_TILE 1, 32, 4, 1
+#define OSP_D128_TILE 1, 32, 8, 2
 #endif
 template <int QB_, int BN_, int NW_, int OCC_> struct TileShape {
   static constexpr int QB = QB_, BN = BN_, NW = NW_, OCC = OCC_;
