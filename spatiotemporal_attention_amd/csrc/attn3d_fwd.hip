@@ -515,10 +515,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   // ended by a workgroup barrier.  The trailing half passes one barrier
   // first and so runs one phase behind: on each SIMD one wave's MFMAs
   // overlap the other wave's softmax.  Only the leading half loads.  At the
-  // start of its iteration t it issues K(t+1) into K slot (t+1)&1 and V(t)
-  // into V slot t&1 (their previous tiles were last read by the trailing
-  // half in the phase just ended) and waits for them at the iteration's
-  // end, one phase before their first reader.
+  // start of its softmax phase t it issues K(t+1) into K slot (t+1)&1 and
+  // V(t) into V slot t&1 (their previous tiles were last read by the
+  // trailing half in the phase before) and waits for them at the phase's
+  // end, one phase before their first reader; the loads stay out of its
+  // matrix phases.
   const bool ragged = (L % BN) != 0;
   f32x16_t s[NKB][QB];
   bf16x8_t pb[QB][NKB][2];
@@ -553,9 +554,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   // one iteration (two phases) for tile t; HK: K(t+1) exists
   auto iter = [&](int t, auto slot, auto do_pv, auto masked, auto hk) __attribute__((always_inline)) {
     constexpr int P = decltype(slot)::value;
-    if (lead) load_issue(t + 1, t, int_c<P ^ 1>{}, int_c<P>{}, hk, bool_c<true>{});
     m_phase(t, slot, bool_c<true>{}, do_pv, masked);
     barrier();
+    if (lead) load_issue(t + 1, t, int_c<P ^ 1>{}, int_c<P>{}, hk, bool_c<true>{});
     update_max(s, t == 0);
     softmax(s, pb);
     if (lead) load_finish(t + 1, t, int_c<P ^ 1>{}, int_c<P>{}, hk, bool_c<true>{});
