@@ -448,11 +448,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     }
   };
   // probabilities of a tile as bf16 B operands, row sums
+  // Row sums use plain fp32 adds of the probabilities, in four independent
+  // partial sums: dot-product instructions (v_dot2*) do not overlap with
+  // the other wave's MFMAs the way ordinary VALU instructions do.
   auto softmax = [&](f32x16_t (&s)[NKB][QB], bf16x8_t (&pb)[QB][NKB][2]) __attribute__((always_inline)) {
-    const bf16x2v_t one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float acc = 0.f;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -463,12 +465,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
             const float p0 = __builtin_amdgcn_exp2f(s[kb][qb][8 * hh + 2 * t]);
             const float p1 = __builtin_amdgcn_exp2f(s[kb][qb][8 * hh + 2 * t + 1]);
             w[t] = pack_bf16(p0, p1);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[t]), one, acc,
-                                                  false);
+            acc[t] += p0 + p1;
           }
           pb[qb][kb][hh] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
         }
-      lsum[qb] += acc;
+      lsum[qb] += (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
   };
   // O^T += V^T P^T for the V tile in slot SV.  Source lane (ta, te) of its
