@@ -77,12 +77,13 @@ struct AttnCfg {
   static constexpr int KCH = D / 8;               // 16-byte chunks per row
   static constexpr int CH = BN * KCH;             // chunks per tile
   static constexpr int TILE = BN * D;             // bf16 elements of one K or V tile
-  static constexpr int LW = NW / 2;               // loading waves (the leading half)
+  static constexpr int LW = NW / 2;               // waves per half
   static constexpr int LT = LW * 64;
   static constexpr int DPT = CH / 64;             // 64-lane DMA loads per tile
-  static constexpr int DPW = (2 * DPT + LW - 1) / LW;   // per loading wave, K and V together
-  static constexpr int SPT = (2 * CH + LT - 1) / LT;    // staged chunks per loading thread
+  static constexpr int DPW = DPT / LW;            // per wave of a half, one tensor
+  static constexpr int SPT = CH / LT;             // staged K chunks per leading thread
   static_assert(D % 32 == 0 && BN % 32 == 0 && CH % 64 == 0 && NW % 8 == 0, "tile shape");
+  static_assert(DPT % LW == 0 && CH % LT == 0, "every wave of a half loads the same amount");
 };
 
 // LDS for the RoPE rates and cos/sin table, only when a loader rotates.
@@ -151,17 +152,22 @@ template <int D, int QB, int BN, int NW, int OCC, bool ROPE_Q, bool ROPE_K, bool
 __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs a) {
   using C = AttnCfg<D, QB, BN, NW>;
   constexpr int NKB = BN / 32;        // 32-key blocks per tile
-  // K and V tiles, two slots each; separate arrays so that the compiler can
-  // see that an LDS DMA into one slot does not touch the slot being read
+  // K and V tiles, three slots each (tile x in slot x % 3); separate arrays
+  // so that the compiler can see that an LDS DMA into one slot does not
+  // touch the slot being read
   __shared__ __attribute__((aligned(1024))) uint16_t k_s0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t k_s1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_s2[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_s0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_s1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_s2[C::TILE];
   auto kslot = [&](auto sl) __attribute__((always_inline)) -> uint16_t* {
-    if constexpr (decltype(sl)::value == 0) return k_s0; else return k_s1;
+    constexpr int S = decltype(sl)::value;
+    if constexpr (S == 0) return k_s0; else if constexpr (S == 1) return k_s1; else return k_s2;
   };
   auto vslot = [&](auto sl) __attribute__((always_inline)) -> uint16_t* {
-    if constexpr (decltype(sl)::value == 0) return v_s0; else return v_s1;
+    constexpr int S = decltype(sl)::value;
+    if constexpr (S == 0) return v_s0; else if constexpr (S == 1) return v_s1; else return v_s2;
   };
   __shared__ __attribute__((aligned(16))) RopeSmem<ROPE_Q || ROPE_K> rsm;
   RopeLds* const rl = rsm.get();
@@ -248,15 +254,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
          : (r / uint32_t(kmul)) * uint32_t(kmul * kmul) + r % uint32_t(kmul);
   };
 
-  // DMA path: loading wave w issues loads t = 0..DPW-1 with index
-  // i = w + LW*t (K tile block i if i < DPT, else V tile block i - DPT).
+  // DMA path: wave w of a half (rank lw) loads the blocks i = lw + LW*t,
+  // t < DPW, of one tile (64 lanes x 16 bytes each).
   int32_t dm_off[C::DPW];
   int dm_row[C::DPW], dm_col[C::DPW];
 #pragma unroll
   for (int t = 0; t < C::DPW; ++t) {
-    const int i = lw + C::LW * t;
-    const int blk = (i < C::DPT) ? i : i - C::DPT;
-    const int p = 64 * blk + lane;
+    const int p = 64 * (lw + C::LW * t) + lane;
     dm_row[t] = p / C::KCH;
     dm_col[t] = (p % C::KCH) ^ chunk_swz<D>(dm_row[t]);    // logical chunk
     dm_off[t] = int32_t((int64_t(drow_of(dm_row[t])) * a_sn + 8 * dm_col[t]) * 2);
@@ -268,74 +272,52 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     if constexpr (FIXED_ROWS) return uint32_t(int64_t(kt) * BN * kmul + tile_c0);
     else return skiparse_token(mode, uint32_t(kt * BN), j, divk);
   };
-  auto dma_issue = [&](int kt_k, int kt_v, auto slot_k, auto slot_v, auto hk, auto hv)
-      __attribute__((always_inline)) {
-    constexpr bool HK = decltype(hk)::value, HV = decltype(hv)::value;
-    const uint32_t i0k = HK ? tile_first(kt_k) : 0u, i0v = HV ? tile_first(kt_v) : 0u;
-    const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(kg + int64_t(i0k) * a_sn), (short)0, kRecords, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(vg + int64_t(i0v) * a_sn), (short)0, kRecords, 0x00020000);
+  // tile kt of the tensor at src into LDS tile dst (rows past the end read
+  // as zeros: their offsets are out of the buffer's range)
+  auto dma_tile = [&](const uint16_t* src, int kt, uint16_t* dst) __attribute__((always_inline)) {
+    const uint32_t i0 = tile_first(kt);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(src + int64_t(i0) * a_sn), (short)0, kRecords, 0x00020000);
 #pragma unroll
     for (int t = 0; t < C::DPW; ++t) {
-      const int i = lw + C::LW * t;
-      if (i >= 2 * C::DPT) continue;
-      const bool is_k = i < C::DPT;
-      if (is_k ? !HK : !HV) continue;
-      const int kt = is_k ? kt_k : kt_v;
-      const int blk = is_k ? i : i - C::DPT;
       int32_t off = dm_off[t];
       if constexpr (!FIXED_ROWS) {
         const uint32_t r = uint32_t(min(kt * BN + dm_row[t], L - 1));
-        off = int32_t((int64_t(skiparse_token(mode, r, j, divk) - (is_k ? i0k : i0v)) * a_sn +
-                       8 * dm_col[t]) * 2);
+        off = int32_t((int64_t(skiparse_token(mode, r, j, divk) - i0) * a_sn + 8 * dm_col[t]) * 2);
       }
       off = (dm_row[t] < L - kt * BN) ? off : kRecords;
-      uint16_t* dst = (is_k ? kslot(slot_k) : vslot(slot_v)) + 512 * blk;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_k ? rsk : rsv, (lds_void_ptr)dst, 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(dst + 512 * (lw + C::LW * t)), 16,
+                                               off, 0, 0, 0);
     }
   };
 
-  // Staged path (K rotated in the loader): loading thread chunks
-  // idx = tid + LT*e, K chunk idx if idx < CH, else V chunk idx - CH.
+  // Staged K path (K rotated in the loader): leading thread chunks
+  // idx = lw*64 + lane + LT*e of the K tile.
   uint4 st_reg[ROPE_K ? C::SPT : 1];
-  auto staged_issue = [&](int kt_k, int kt_v, auto hk, auto hv) __attribute__((always_inline)) {
-    constexpr bool HK = decltype(hk)::value, HV = decltype(hv)::value;
+  auto staged_issue = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < C::SPT; ++e) {
       const int idx = lw * 64 + lane + C::LT * e;
-      const bool is_k = idx < C::CH;
-      const int ci = is_k ? idx : idx - C::CH;
-      const int row = ci / C::KCH, col = ci % C::KCH;
-      const int kt = is_k ? kt_k : kt_v;
-      const bool on = idx < 2 * C::CH && (is_k ? HK : HV) && kt * BN + row < L;
+      const int row = idx / C::KCH, col = idx % C::KCH;
+      const bool on = kt * BN + row < L;
       const uint32_t r = uint32_t(min(kt * BN + row, L - 1));
-      const uint32_t i = skiparse_token(mode, on ? r : 0u, j, divk);
-      st_reg[e] = on ? ld16((is_k ? kg : vg) + int64_t(i) * a_sn + 8 * col) : make_uint4(0, 0, 0, 0);
+      const uint32_t i = skiparse_token(mode, r, j, divk);
+      st_reg[e] = on ? ld16(kg + int64_t(i) * a_sn + 8 * col) : make_uint4(0, 0, 0, 0);
     }
   };
-  auto staged_store = [&](int kt_k, int kt_v, auto slot_k, auto slot_v, auto hk, auto hv)
-      __attribute__((always_inline)) {
-    constexpr bool HK = decltype(hk)::value, HV = decltype(hv)::value;
+  auto staged_store = [&](int kt, uint16_t* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < C::SPT; ++e) {
       const int idx = lw * 64 + lane + C::LT * e;
-      const bool is_k = idx < C::CH;
-      const int ci = is_k ? idx : idx - C::CH;
-      const int row = ci / C::KCH, col = ci % C::KCH;
-      if (idx >= 2 * C::CH || !(is_k ? HK : HV)) continue;
-      const int kt = is_k ? kt_k : kt_v;
+      const int row = idx / C::KCH, col = idx % C::KCH;
       uint4 val = st_reg[e];
-      if (is_k) {
-        const int r = kt * BN + row;
-        const uint32_t i = skiparse_token(mode, uint32_t(min(r, L - 1)), j, divk);
-        if (r < L && is_video(rg, i)) {
-          const Coord3 cc = video_coords(rg, i);
-          val = fast_rope ? rotate_chunk_col(rl, chunk_col(rg, 4 * col), cc, val)
-                          : rotate_chunk_tab(rg, rl, 4 * col, cc, val);
-        }
+      const int r = kt * BN + row;
+      const uint32_t i = skiparse_token(mode, uint32_t(min(r, L - 1)), j, divk);
+      if (r < L && is_video(rg, i)) {
+        const Coord3 cc = video_coords(rg, i);
+        val = fast_rope ? rotate_chunk_col(rl, chunk_col(rg, 4 * col), cc, val)
+                        : rotate_chunk_tab(rg, rl, 4 * col, cc, val);
       }
-      uint16_t* dst = is_k ? kslot(slot_k) : vslot(slot_v);
       *reinterpret_cast<uint4*>(dst + 8 * (row * C::KCH + (col ^ chunk_swz<D>(row)))) = val;
     }
   };
@@ -499,29 +481,44 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       }
   };
 
-  // issue / complete the loads of K tile kt_k into K slot SK and V tile kt_v
-  // into V slot SV (HK / HV: whether those tiles exist)
-  auto load_issue = [&](int kt_k, int kt_v, auto sk, auto sv, auto hk, auto hv) __attribute__((always_inline)) {
-    if constexpr (ROPE_K) staged_issue(kt_k, kt_v, hk, hv);
-    else dma_issue(kt_k, kt_v, sk, sv, hk, hv);
+  // Loads of one tile: the leading half loads K tiles, the trailing half V
+  // tiles.  issue_tile starts them; finish_tile completes the staged
+  // (rotating) K path.
+  auto issue_tile = [&](int kt, auto slot) __attribute__((always_inline)) {
+    if (lead) {
+      if constexpr (ROPE_K) staged_issue(kt);
+      else dma_tile(kg, kt, kslot(slot));
+    } else {
+      dma_tile(vg, kt, vslot(slot));
+    }
   };
-  auto load_finish = [&](int kt_k, int kt_v, auto sk, auto sv, auto hk, auto hv) __attribute__((always_inline)) {
-    if constexpr (ROPE_K) staged_store(kt_k, kt_v, sk, sv, hk, hv);
+  auto finish_tile = [&](int kt, auto slot) __attribute__((always_inline)) {
+    if constexpr (ROPE_K) {
+      if (lead) staged_store(kt, kslot(slot));
+    }
   };
 
   // ---- ping-pong schedule.  The waves form two halves, one wave of each
   // on every SIMD.  Per key tile t a wave runs a matrix phase M(t) (S(t) =
-  // K(t) Q^T from K slot t&1, then O += PV(t-1) from V slot (t-1)&1) and a
-  // softmax phase V(t) (max, rescale, exp2, row sums of S(t) into P), each
-  // ended by a workgroup barrier.  The trailing half passes one barrier
-  // first and so runs one phase behind: on each SIMD one wave's MFMAs
-  // overlap the other wave's softmax.  Only the leading half loads.  At the
-  // start of its softmax phase t it issues K(t+1) into K slot (t+1)&1 and
-  // V(t) into V slot t&1 (their previous tiles were last read by the
-  // trailing half in the phase before) and waits for them at the phase's
-  // end, one phase before their first reader; the loads stay out of its
-  // matrix phases.
+  // K(t) Q^T, then O += P(t-1) V(t-1)) and a softmax phase V(t) (max,
+  // rescale, exp2, row sums of S(t) into P), each ended by a workgroup
+  // barrier.  The trailing half passes one barrier first and so runs one
+  // phase behind: on each SIMD one wave's MFMAs overlap the other wave's
+  // softmax.
+  //
+  // Loads: tile x of K and V lives in slot x % 3.  In its softmax phase
+  // for tile t each wave of the leading half issues its share of K(t+2),
+  // each wave of the trailing half its share of V(t+2); the tiles they
+  // replace, K(t-1) and V(t-1), were last read in earlier phases.  At the
+  // end of that phase a wave waits for its loads of the previous iteration
+  // only (K(t+1) or V(t+1)), at least one phase before their first
+  // reader, so each load has two phases or more to arrive.  The tile count
+  // is padded to a multiple of 3 with tiles past the end of the
+  // subsequence (keys masked to -inf, loads out of range of the buffer,
+  // which read as zeros), so that every slot index is a compile-time
+  // constant.
   const bool ragged = (L % BN) != 0;
+  const int nkt3 = (nkt + 2) / 3 * 3;
   f32x16_t s[NKB][QB];
   bf16x8_t pb[QB][NKB][2];
 
@@ -530,21 +527,24 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // the compiler tracks this wait (vmcnt(0) lgkmcnt(0)), so it knows the
-  // loaded tiles are complete when they are read in later phases
+  // Wait for all but this iteration's DPW loads (vmcnt(DPW)); the leading
+  // half on the staged path has just stored its tile and waits for all
+  // (vmcnt(0) lgkmcnt(0)).  The compiler tracks these waits, so it knows
+  // which slots are complete.
   auto loads_done = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0070);
+    if (ROPE_K && lead) __builtin_amdgcn_s_waitcnt(0x0070);
+    else __builtin_amdgcn_s_waitcnt((C::DPW & 15) | ((C::DPW >> 4) << 14) | 0x0F70);
   };
-  // matrix phase of tile t: QK(t) (QK) and PV(t-1) (PV); slot P = t & 1
-  // Instruction order inside it: the LDS reads run OSP_M_LEAD MFMAs ahead
-  // of the MFMAs that use them.
+  // matrix phase of tile t: QK(t) from K slot P (QK) and PV(t-1) from V
+  // slot (P + 2) % 3 (PV).  Instruction order inside it: the LDS reads run
+  // OSP_M_LEAD MFMAs ahead of the MFMAs that use them.
   auto m_phase = [&](int t, auto slot, auto do_qk, auto do_pv, auto masked) __attribute__((always_inline)) {
     constexpr int P = decltype(slot)::value;
     constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
     __builtin_amdgcn_s_setprio(1);
     if constexpr (QK) qk(int_c<P>{}, s, t, masked);
-    if constexpr (PV) pv(int_c<P ^ 1>{}, pb);
+    if constexpr (PV) pv(int_c<(P + 2) % 3>{}, pb);
     if constexpr (QB == 1) {
       constexpr int NMV = PV ? NKB * 2 * (D / 32) : 0, NMK = QK ? NKB * (D / 16) : 0;
       __builtin_amdgcn_sched_group_barrier(0x100, m_first_reads<NMK, NMV, OSP_M_LEAD>(), 0);
@@ -552,56 +552,57 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     }
     __builtin_amdgcn_s_setprio(0);
   };
-  // one iteration (two phases) for tile t; HK: K(t+1) exists
-  auto iter = [&](int t, auto slot, auto do_pv, auto masked, auto hk) __attribute__((always_inline)) {
+  // tiles from tu on hold keys past the end (the last real tile when
+  // ragged, and the padding); whole groups before tu run unmasked
+  const int tu = nkt - (ragged ? 1 : 0);
+  // one iteration (two phases) for tile t in slot P = t % 3; MASKED: mask
+  // keys past the end (correct for any tile; used for the last groups)
+  auto iter = [&](int t, auto slot, auto masked) __attribute__((always_inline)) {
     constexpr int P = decltype(slot)::value;
-    m_phase(t, slot, bool_c<true>{}, do_pv, masked);
+    m_phase(t, slot, bool_c<true>{}, bool_c<true>{}, masked);
     barrier();
-    if (lead) load_issue(t + 1, t, int_c<P ^ 1>{}, int_c<P>{}, hk, bool_c<true>{});
+    issue_tile(t + 2, int_c<(P + 2) % 3>{});
     update_max(s, t == 0);
     softmax(s, pb);
-    if (lead) load_finish(t + 1, t, int_c<P ^ 1>{}, int_c<P>{}, hk, bool_c<true>{});
-    loads_done();   // a no-op for the trailing half, which loads nothing
+    finish_tile(t + 2, int_c<(P + 2) % 3>{});
+    loads_done();
     barrier();
   };
-  // the last tile t = nkt - 1 >= 1: masked when the subsequence is ragged
-  auto last = [&](int t, auto slot) __attribute__((always_inline)) {
-    if (ragged) iter(t, slot, bool_c<true>{}, bool_c<true>{}, bool_c<false>{});
-    else iter(t, slot, bool_c<true>{}, bool_c<false>{}, bool_c<false>{});
-  };
-  // the last matrix phase, PV of tile nkt - 1 (slot P = nkt & 1)
-  auto fin = [&](auto slot) __attribute__((always_inline)) {
-    m_phase(nkt, slot, bool_c<false>{}, bool_c<true>{}, bool_c<false>{});
-  };
 
-  // prologue: K(0) into K slot 0
-  if (lead) {
-    load_issue(0, 0, int_c<0>{}, int_c<0>{}, bool_c<true>{}, bool_c<false>{});
-    load_finish(0, 0, int_c<0>{}, int_c<0>{}, bool_c<true>{}, bool_c<false>{});
-  }
+  // prologue: K(0), K(1), V(0), V(1) into slots 0 and 1; V slot 2 (read
+  // as "V(-1)" by the first matrix phase, with P = 0) cleared
+  for (int e = tid; e < C::TILE / 8; e += C::NT)
+    reinterpret_cast<uint4*>(v_s2)[e] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      pb[qb][kb][0] = bf16x8_t{};
+      pb[qb][kb][1] = bf16x8_t{};
+    }
+  issue_tile(0, int_c<0>{});
+  finish_tile(0, int_c<0>{});
+  issue_tile(1, int_c<1>{});
+  finish_tile(1, int_c<1>{});
   __syncthreads();
   if (!lead) barrier();
-  if (nkt == 1) {
-    if (ragged) iter(0, int_c<0>{}, bool_c<false>{}, bool_c<true>{}, bool_c<false>{});
-    else iter(0, int_c<0>{}, bool_c<false>{}, bool_c<false>{}, bool_c<false>{});
-    fin(int_c<1>{});
-  } else {
-    iter(0, int_c<0>{}, bool_c<false>{}, bool_c<false>{}, bool_c<true>{});
-    int t = 1;
-    for (; t + 2 < nkt; t += 2) {
-      iter(t, int_c<1>{}, bool_c<true>{}, bool_c<false>{}, bool_c<true>{});
-      iter(t + 1, int_c<0>{}, bool_c<true>{}, bool_c<false>{}, bool_c<true>{});
-    }
-    if (t + 1 < nkt) {
-      iter(t, int_c<1>{}, bool_c<true>{}, bool_c<false>{}, bool_c<true>{});
-      last(t + 1, int_c<0>{});
-      fin(int_c<1>{});
-    } else {
-      last(t, int_c<1>{});
-      fin(int_c<0>{});
-    }
+  int t = 0;
+  for (; t + 3 <= tu; t += 3) {
+    iter(t, int_c<0>{}, bool_c<false>{});
+    iter(t + 1, int_c<1>{}, bool_c<false>{});
+    iter(t + 2, int_c<2>{}, bool_c<false>{});
   }
+  for (; t < nkt3; t += 3) {
+    iter(t, int_c<0>{}, bool_c<true>{});
+    iter(t + 1, int_c<1>{}, bool_c<true>{});
+    iter(t + 2, int_c<2>{}, bool_c<true>{});
+  }
+  // the last matrix phase: PV of tile nkt3 - 1 (V slot 2)
+  m_phase(nkt3, int_c<0>{}, bool_c<false>{}, bool_c<true>{}, bool_c<false>{});
   if (lead) barrier();   // the trailing half's last barrier
+  // loads of the padding tiles past nkt3 may still be writing LDS: finish
+  // them before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0070);
 
   // ---- epilogue: O = O^T / l, stored at the original token row ----
   uint16_t* og = a.o + int64_t(b) * a.osb + int64_t(h) * a.osh;
