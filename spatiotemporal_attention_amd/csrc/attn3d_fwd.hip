@@ -59,6 +59,7 @@ typedef i16x4_t __attribute__((address_space(3))) * lds_i16x4_ptr;
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 constexpr float kTau = 8.0f;
+constexpr float kSumTau = 256.0f;   // 2^kTau
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int32_t kRecords = 0x40000000;   // buffer range of one key tile (bytes)
 
@@ -391,28 +392,74 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       }
     }
   };
-  // Row max t of a tile's shifted scores; where t > kTau raise m by t and
-  // rescale (O, l, and this tile's scores).  first: the row's first tile,
-  // which sets m to its maximum whatever its sign.
-  auto update_max = [&](f32x16_t (&s)[NKB][QB], bool first) __attribute__((always_inline)) {
-    float tmax[QB];
-    bool need = first;
+  // Probabilities of a tile as bf16 B operands, and their row sums ts.
+  // The sums are plain fp32 adds in four independent partial sums:
+  // dot-product instructions (v_dot2*) do not overlap with the other
+  // wave's MFMAs the way ordinary VALU instructions do.
+  auto probs = [&](const f32x16_t (&s)[NKB][QB], bf16x8_t (&pb)[QB][NKB][2], float (&ts)[QB])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
+      float acc[4];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
-      tmax[qb] = max_pair32(mx);
-      need |= tmax[qb] > kTau;
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t w[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float p0 = __builtin_amdgcn_exp2f(s[kb][qb][8 * hh + 2 * t]);
+            const float p1 = __builtin_amdgcn_exp2f(s[kb][qb][8 * hh + 2 * t + 1]);
+            w[t] = pack_bf16(p0, p1);
+            acc[t] = (kb == 0 && hh == 0) ? p0 + p1 : acc[t] + (p0 + p1);
+          }
+          pb[qb][kb][hh] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+      ts[qb] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
+  };
+  // Softmax phase of a tile.  The probabilities are computed from the
+  // scores as shifted by the current m.  m must be raised (and O, l
+  // rescaled) only where a score exceeds kTau, and such a score alone
+  // makes the lane's tile sum exceed 2^kTau; so the row maximum t is
+  // reduced only in the branch taken when some lane's sum exceeds 2^kTau
+  // (or on the row's first tile, which sets m to its maximum whatever its
+  // sign).  There m is raised by t where t > kTau and the probabilities are
+  // computed again from the newly shifted scores; the branch is rare after
+  // the first tile, and any overflow of the first computation is discarded
+  // with it.
+  auto softmax_phase = [&](f32x16_t (&s)[NKB][QB], bf16x8_t (&pb)[QB][NKB][2], bool first)
+      __attribute__((always_inline)) {
+    float ts[QB];
+    probs(s, pb, ts);
+    // keep this computation ahead of the branch (the compiler would
+    // otherwise sink it into the path that uses it, behind the max chain)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      asm volatile("" : "+v"(ts[qb]));
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint4 u = __builtin_bit_cast(uint4, pb[qb][kb][hh]);
+          asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+          pb[qb][kb][hh] = __builtin_bit_cast(bf16x8_t, u);
+        }
+    }
+    bool need = first;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) need |= !(ts[qb] <= kSumTau);
     if (__builtin_expect(__ballot(need) != 0, 0)) {
-      // rare after the first tile; keep it a branch (no speculation)
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float dm = (first || tmax[qb] > kTau) ? tmax[qb] : 0.f;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
+        const float tmax = max_pair32(mx);
+        const float dm = (first || tmax > kTau) ? tmax : 0.f;
         mref[qb] += dm;
         const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-dm);
         lsum[qb] *= alpha;
@@ -427,32 +474,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
 #pragma unroll
         for (int e = 0; e < 16; ++e) negm[qb][e] = -mref[qb];
       }
+      probs(s, pb, ts);
     }
-  };
-  // probabilities of a tile as bf16 B operands, row sums
-  // Row sums use plain fp32 adds of the probabilities, in four independent
-  // partial sums: dot-product instructions (v_dot2*) do not overlap with
-  // the other wave's MFMAs the way ordinary VALU instructions do.
-  auto softmax = [&](f32x16_t (&s)[NKB][QB], bf16x8_t (&pb)[QB][NKB][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          uint32_t w[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float p0 = __builtin_amdgcn_exp2f(s[kb][qb][8 * hh + 2 * t]);
-            const float p1 = __builtin_amdgcn_exp2f(s[kb][qb][8 * hh + 2 * t + 1]);
-            w[t] = pack_bf16(p0, p1);
-            acc[t] += p0 + p1;
-          }
-          pb[qb][kb][hh] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-        }
-      lsum[qb] += (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    }
+    for (int qb = 0; qb < QB; ++qb) lsum[qb] += ts[qb];
   };
   // O^T += V^T P^T for the V tile in slot SV.  Source lane (ta, te) of its
   // 16-lane group G points at key 32kb + 16hh + 4(G/2) + te (+8), channels
@@ -562,8 +587,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     m_phase(t, slot, bool_c<true>{}, bool_c<true>{}, masked);
     barrier();
     issue_tile(t + 2, int_c<(P + 2) % 3>{});
-    update_max(s, t == 0);
-    softmax(s, pb);
+    softmax_phase(s, pb, t == 0);
     finish_tile(t + 2, int_c<(P + 2) % 3>{});
     loads_done();
     barrier();
