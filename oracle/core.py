@@ -34,7 +34,12 @@ design notes):
    (groups of k adjacent tokens);
 10. subsequences keep increasing token order and are listed by j;
 11. every token keeps its own (t, h, w) under Skiparse (RoPE acts per token
-    before the regrouping).
+    before the regrouping);
+12. block attention (the spatial half of separated spatial / temporal
+    attention, and window attention) attends within k runs of N/k adjacent
+    tokens; with the row-major unfold, k = T gives each frame's H*W tokens,
+    and the temporal half (same (h, w) across frames) is Single Skip with
+    k = H*W.
 
 Parity status: grid arithmetic, rotation and attention are pinned by closed
 forms, invariants, a library routine and brute force (tests/test_oracle_*.py).
@@ -48,7 +53,7 @@ import math
 
 import numpy as np
 
-MODES = ("full", "skiparse_single", "skiparse_group")
+MODES = ("full", "skiparse_single", "skiparse_group", "block")
 
 
 # --------------------------------------------------------------------------
@@ -136,6 +141,14 @@ def skiparse_groups(mode: str, k: int, n: int) -> list:
     every k-th token (reading 8); Group Skip gathers groups of adjacent
     tokens whose groups lie k-1 groups apart (reading 9, group size k).  The
     section assumes the length divides evenly; we require it.
+
+    "block": k runs of N/k adjacent tokens (reading 12).  This is the
+    spatial half of the separated spatial / temporal attention that
+    CogVideoX section 2.2 "3D Full Attention" and Table 8 compare with 3D
+    attention (k = frames: each frame's H*W tokens), and the window
+    attention that Open-Sora Plan section 2.2.2 contrasts with Group Skip
+    (k = N / window).  The temporal half (tokens with the same (h, w)) is
+    Single Skip with k = H*W.
     """
     idx = np.arange(n, dtype=np.int64)
     if mode == "full":
@@ -150,6 +163,10 @@ def skiparse_groups(mode: str, k: int, n: int) -> list:
         if n % (k * k):
             raise ValueError("group skip needs N divisible by k*k")
         key = (idx // k) % k
+    elif mode == "block":
+        if n % k:
+            raise ValueError("block attention needs N divisible by k")
+        key = idx // (n // k)
     else:
         raise ValueError(f"unknown mode {mode!r}")
     return [np.nonzero(key == j)[0] for j in range(k)]
@@ -200,8 +217,10 @@ def attn3d(q, k, v, *, grid, n_text: int = 0, mode: str = "full",
     ``rows``: optional sorted token indices; then only those query rows are
     computed and o has shape [B, len(rows), H, D], lse [B, H, len(rows)].
     ``rope=False`` takes q and k as already rotated.
-    Skiparse with text tokens is rejected (reading: Open-Sora Plan feeds text
-    through cross-attention, so its Skiparse self-attention has none).
+    Skiparse and block attention with text tokens are rejected (reading:
+    Open-Sora Plan feeds text through cross-attention, so its Skiparse
+    self-attention has none; the pages do not say how text joins separated
+    spatial or temporal attention).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -210,7 +229,7 @@ def attn3d(q, k, v, *, grid, n_text: int = 0, mode: str = "full",
     if n != n_text + int(np.prod(grid)):
         raise ValueError("sequence length does not match the grid")
     if mode != "full" and n_text:
-        raise ValueError("Skiparse takes no text tokens")
+        raise ValueError("Skiparse and block attention take no text tokens")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     if rope:

@@ -207,6 +207,37 @@ def pin_skiparse_structure(o):
             raise AssertionError("accepted a length that does not divide")
 
 
+def pin_spatial_temporal(o):
+    """Separated spatial / temporal attention (CogVideoX 2.2, Table 8) in
+    terms of the latent coordinates: block attention with k = T groups the
+    tokens of one frame, Single Skip with k = H*W the tokens of one (h, w)
+    position across frames; block attention is the reshape [k, N/k]; k = N
+    leaves every token alone."""
+    for grid in ((3, 4, 5), (5, 8, 8), (2, 3, 3)):
+        t, h, w = grid
+        n = t * h * w
+        c = o.video_coords(grid)
+        for j, g in enumerate(o.skiparse_groups("block", t, n)):
+            assert set(g.tolist()) == set(np.nonzero(c[:, 0] == j)[0].tolist())
+        seen = set()
+        for g in o.skiparse_groups("skiparse_single", h * w, n):
+            hw = {(int(c[i, 1]), int(c[i, 2])) for i in g}
+            assert len(hw) == 1 and len(g) == t
+            seen |= hw
+        assert len(seen) == h * w
+        perm, inv = o.skiparse_index("block", t, n)
+        assert np.array_equal(perm, np.arange(n)) and np.array_equal(inv, np.arange(n))
+    for n, k in ((48, 4), (48, 48), (48, 1), (320, 5)):
+        g = o.skiparse_groups("block", k, n)
+        assert np.array_equal(np.stack(g), np.arange(n).reshape(k, n // k))
+    try:
+        o.skiparse_groups("block", 5, 48)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("accepted a length that does not divide")
+
+
 # --------------------------------------------------------------------------
 # attention
 # --------------------------------------------------------------------------
@@ -230,10 +261,13 @@ def pin_attention_sdpa(o):
     qr = o.rope3d(q, grid, 0, split)
     kr = o.rope3d(k, grid, 0, split)
     for mode, kk in (("full", 1), ("skiparse_single", 4), ("skiparse_group", 4),
-                     ("skiparse_single", 2), ("skiparse_group", 2), ("skiparse_single", 8)):
+                     ("skiparse_single", 2), ("skiparse_group", 2), ("skiparse_single", 8),
+                     ("block", 4), ("block", 16), ("block", 1)):
         idx = np.arange(n)
         if mode == "full":
             lab = np.zeros(n, dtype=np.int64)
+        elif mode == "block":
+            lab = np.repeat(np.arange(kk), n // kk)
         elif mode == "skiparse_single":
             lab = np.empty(n, dtype=np.int64)
             lab[idx.reshape(n // kk, kk).T] = np.arange(kk)[:, None]
@@ -292,7 +326,7 @@ def pin_attention_special(o):
     const = np.full_like(v, 1.75)
     out, _ = o.attn3d(q, k, const, grid=grid, rope_split=split)
     assert np.allclose(out, 1.75, atol=1e-13)
-    for mode, kk in (("full", 1), ("skiparse_single", 4), ("skiparse_group", 2)):
+    for mode, kk in (("full", 1), ("skiparse_single", 4), ("skiparse_group", 2), ("block", 4)):
         out, lse = o.attn3d(np.zeros_like(q), k, v, grid=grid, mode=mode, sparse_k=kk,
                             rope_split=split)
         for g in o.skiparse_groups(mode, kk, n):
@@ -344,7 +378,7 @@ def pin_rows_subset(o):
     rng = _rng(25)
     q, k, v = (rng.standard_normal((1, 32, 2, 64)) for _ in range(3))
     rows = np.array([0, 3, 5, 17, 31])
-    for mode, kk in (("full", 1), ("skiparse_single", 4), ("skiparse_group", 2)):
+    for mode, kk in (("full", 1), ("skiparse_single", 4), ("skiparse_group", 2), ("block", 2)):
         a, la = o.attn3d(q, k, v, grid=grid, mode=mode, sparse_k=kk, rope_split=split)
         b, lb = o.attn3d(q, k, v, grid=grid, mode=mode, sparse_k=kk, rope_split=split, rows=rows)
         assert np.allclose(a[:, rows], b, rtol=0, atol=1e-14)
@@ -354,6 +388,6 @@ def pin_rows_subset(o):
 ALL_PINS = [
     pin_latent_grids, pin_video_coords, pin_rope_closed_form, pin_rope_complex,
     pin_rope_invariants, pin_rope_axis_chunks, pin_skiparse_reshape,
-    pin_skiparse_structure, pin_attention_sdpa, pin_attention_bruteforce,
+    pin_skiparse_structure, pin_spatial_temporal, pin_attention_sdpa, pin_attention_bruteforce,
     pin_attention_special, pin_attention_text, pin_rows_subset,
 ]

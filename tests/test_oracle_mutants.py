@@ -37,6 +37,8 @@ MUTANTS = {
     "lse_no_max": ("lse = (m + np.log(l))[:, 0]", "lse = (np.log(l))[:, 0]"),
     "default_scale_wrong": ("sm_scale = 1.0 / math.sqrt(d)", "sm_scale = 1.0 / d"),
     "k_not_rotated": ("k = rope3d(k, grid, n_text, rope_split, theta, pos_offset)", "pass"),
+    "block_strided": ("key = idx // (n // k)", "key = idx % k"),
+    "block_runs_of_k": ("key = idx // (n // k)", "key = idx // k % k"),
     "perm_inverse_wrong": ("inv[perm] = np.arange(n, dtype=np.int64)", "inv[:] = perm"),
 }
 
