@@ -56,9 +56,12 @@ typedef enum {
 typedef enum {
   OSP_MODE_FULL = 0,             /* every token attends to every token       */
   OSP_MODE_SKIPARSE_SINGLE = 1,  /* subsequence j = tokens i with i mod k = j */
-  OSP_MODE_SKIPARSE_GROUP = 2    /* subsequence j = tokens i with
+  OSP_MODE_SKIPARSE_GROUP = 2,   /* subsequence j = tokens i with
                                     floor(i/k) mod k = j (groups of k
                                     adjacent tokens, k-1 groups apart)       */
+  OSP_MODE_BLOCK = 3             /* subsequence j = tokens i with
+                                    floor(i/(N/k)) = j (k runs of N/k
+                                    adjacent tokens)                         */
 } osp_mode;
 
 /* flags of osp_attn3d_fwd */
@@ -117,11 +120,17 @@ osp_status osp_rope3d(const osp_attn3d_desc* desc, const void* x, void* y,
                       void* stream);
 
 /* Attention forward.
-   mode: osp_mode.  sparse_k: Skiparse ratio k >= 1 (ignored for FULL);
-   Skiparse (Open-Sora Plan section 2.2.2) needs N divisible by k (single)
-   or by k*k (group), and n_text == 0 (else OSP_ERR_UNSUPPORTED); k == 1
-   equals full attention.  The k subsequences are attended independently
-   and each output row is written back at its token's original position.
+   mode: osp_mode.  sparse_k: the number k >= 1 of subsequences (ignored
+   for FULL).  Skiparse (Open-Sora Plan section 2.2.2) needs N divisible by
+   k (single) or by k*k (group).  BLOCK needs N divisible by k: with k = T
+   it is the spatial half of separated spatial / temporal attention
+   (CogVideoX section 2.2 "3D Full Attention", Table 8), each frame's H*W
+   tokens attending among themselves, and with k = N / w it is window
+   attention over windows of w tokens; the temporal half is SKIPARSE_SINGLE
+   with k = H*W.  Modes other than FULL need n_text == 0 (else
+   OSP_ERR_UNSUPPORTED); k == 1 equals full attention.  The k
+   subsequences are attended independently and each output row is written
+   back at its token's original position.
    sm_scale: logit scale; <= 0 selects 1/sqrt(head_dim).
    flags: OSP_FUSE_ROPE_Q / OSP_FUSE_ROPE_K rotate Q / K in the loaders; a
    tensor whose flag is clear must already be rotated.  K is rotated
@@ -144,10 +153,11 @@ osp_status osp_attn3d_fwd(const osp_attn3d_desc* desc, int32_t mode,
                           const void* q, const void* k, const void* v, void* o,
                           float* lse, void* stream);
 
-/* Skiparse index maps of an N-token sequence (Open-Sora Plan section 2.2.2).
+/* Index maps of the subsequences of an N-token sequence (Skiparse,
+   Open-Sora Plan section 2.2.2; BLOCK as above).
    perm[j*L + r] = token at row r of subsequence j (L = N/k; rows in
-   increasing token order); inv[token] = its regrouped position.  FULL (or
-   k == 1) gives the identity.  Either of perm/inv may be NULL, not both.
+   increasing token order); inv[token] = its regrouped position.  FULL,
+   BLOCK and k == 1 give the identity.  Either of perm/inv may be NULL, not both.
    on_device == 0: perm/inv are host arrays, filled before returning
    (stream ignored).  on_device != 0: they are device arrays, filled by a
    kernel enqueued on stream.  OSP_ERR_SHAPE if N does not divide. */

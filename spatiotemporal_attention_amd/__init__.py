@@ -17,7 +17,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libosp.so")
 
-MODES = {"full": 0, "skiparse_single": 1, "skiparse_group": 2}
+MODES = {"full": 0, "skiparse_single": 1, "skiparse_group": 2, "block": 3}
 OSP_FUSE_ROPE_Q = 1
 OSP_FUSE_ROPE_K = 2
 OSP_FUSE_ROPE = 3

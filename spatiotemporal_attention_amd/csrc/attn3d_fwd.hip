@@ -1,17 +1,18 @@
 // attn3d_fwd.hip -- flash-style attention forward for gfx950 (MI355X):
-// 3D RoPE fused into the Q (and optionally K) loaders, Skiparse as a
-// row -> token remap in the loaders and the store, bf16 MFMA 32x32x16 with
-// fp32 accumulation, fp32 online softmax.
+// 3D RoPE fused into the Q (and optionally K) loaders, Skiparse and block
+// attention as a row -> token remap in the loaders and the store, bf16 MFMA
+// 32x32x16 with fp32 accumulation, fp32 online softmax.
 //
 // What it computes: softmax(scale * q k^T) v over every token of a
 // subsequence (CogVideoX section 2.2 "3D Full Attention"; Skiparse
-// subsequences from Open-Sora Plan section 2.2.2).  The blocked order with a
-// running maximum reaches the plain definition's result up to rounding (the
-// FlashAttention argument cited in CogVideoX section 2.2).
+// subsequences from Open-Sora Plan section 2.2.2; blocks of adjacent tokens
+// for separated spatial attention or window attention).  The blocked order
+// with a running maximum reaches the plain definition's result up to
+// rounding (the FlashAttention argument cited in CogVideoX section 2.2).
 //
-// Work split.  One workgroup = NW waves owns BM = NW*32*QB query rows of one
-// (batch, head, subsequence); each wave owns QB blocks of 32 rows.  Keys and
-// values stream through LDS in tiles of BN rows.
+// Work split.  One workgroup = NW = 8 waves owns BM = 8*32*QB query rows of
+// one (batch, head, subsequence); each wave owns QB blocks of 32 rows.  Keys
+// and values stream through LDS in tiles of BN rows.
 //
 // LDS tiles are unpadded rows of D bf16; the 16-byte chunks of row r are
 // XOR-swizzled (chunk_swz) so that the operand reads below hit distinct
@@ -19,32 +20,29 @@
 // few 64-lane loads that write 1 KiB of a tile directly, with no registers
 // and no LDS store instructions; rows past the end of a subsequence are
 // fetched out of the buffer range and land as zeros.  When K is rotated in
-// the loader, chunks go through registers instead.
+// the loader, K chunks go through registers instead.
 //
 // Per wave and key tile, S^T = K Q^T is formed with K as the A operand (LDS)
 // and Q^T as the B operand (registers), so a lane holds the scores of ONE
-// query (column = lane mod 32): row max and row sum are in-lane reductions
-// plus one exchange with lane +-32 (v_permlane32_swap).  O^T = V^T P^T takes
-// the probabilities straight from the score registers as the B operand; the
+// query (column = lane mod 32): row reductions are in-lane plus one
+// exchange with lane +-32 (v_permlane32_swap).  O^T = V^T P^T takes the
+// probabilities straight from the score registers as the B operand; the
 // V^T A operand is read from row-major V with ds_read_b64_tr_b16 (a
 // transposing LDS read), in the key order that matches the score layout.
 //
-// Pipeline: iteration j issues the S products of tile j+1 interleaved with
-// the exponentials of tile j, then the PV products of tile j interleaved
-// with the row max of tile j+1.  K runs one tile ahead of V in
-// double-buffered LDS; the loop is unrolled by two so buffer slots are
-// compile-time constants.
+// Schedule: the waves form two halves that alternate a matrix phase (MFMAs)
+// and a softmax phase (VALU) one phase apart, with a workgroup barrier
+// after every phase, so that each SIMD runs one wave's MFMAs beside the
+// other wave's softmax (see the schedule section below).
 //
 // Softmax: Q is multiplied by scale * log2(e) once (then bf16 again), so
 // scores come out in log2 units, and the first product of each score block
 // starts from -m instead of 0: the MFMA delivers z - m and v_exp_f32 takes
-// it as is (keys past the end of the last tile start from -inf).  A row's
-// reference maximum m is set by its first tile and afterwards only rises
-// when a tile's maximum exceeds it by more than kTau (= 8, a factor 256),
-// so the O rescale is skipped for most tiles; probabilities stay <= 2^8 and
-// O / l is unchanged in exact arithmetic.  Row sums add the bf16-rounded
-// probabilities (the same values the PV product uses) with
-// v_dot2c_f32_bf16.
+// it as is (keys past the end start from -inf).  A row's reference maximum
+// m is set by its first tile and afterwards only rises when a tile's scores
+// exceed it by more than kTau (= 8, a factor 256), so the O rescale is
+// skipped for most tiles; probabilities stay <= 2^8 and O / l is unchanged
+// in exact arithmetic.  Row sums add the fp32 probabilities.
 #include <type_traits>
 
 #include "osp_internal.hpp"
@@ -116,7 +114,8 @@ __device__ __forceinline__ float sum_pair32(float x) {
 
 // ROPE_Q / ROPE_K: rotate Q / K in the loaders (false = already rotated).
 // FIXED_ROWS: the row -> token offsets inside a key tile are the same for
-// every tile (full, single skip, or group skip with BN a multiple of k).
+// every tile (full, block, single skip, or group skip with BN a multiple of
+// k).
 // OCC: waves per SIMD the register budget is sized for.
 // Scheduling groups of a matrix phase: NMK QK MFMAs (one LDS read each)
 // then NMV PV MFMAs (two reads each), in the program order of their reads
@@ -222,7 +221,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   for (int qb = 0; qb < QB; ++qb) {
     const int r = int(qt) * C::BM + (wave * QB + qb) * 32 + l32;
     const bool valid = r < L;
-    const uint32_t i = skiparse_token(mode, uint32_t(valid ? r : 0), j, divk);
+    const uint32_t i = skiparse_token(mode, uint32_t(valid ? r : 0), j, divk, uint32_t(L));
     const uint16_t* p = qg + int64_t(i) * a_sn;
     const bool video = ROPE_Q && is_video(rg, i);
     const Coord3 cc = video_coords(rg, i);
@@ -247,10 +246,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   // remap is increasing in the row, and with FIXED_ROWS row r0 + row maps
   // to i0(kt) + drow(row), so per-lane byte offsets are fixed and only the
   // tile base moves.  K of tile kt goes to K slot kt&1, V to V slot kt&1.
-  const int kmul = (mode == MODE_FULL) ? 1 : int(divk.d);
+  const int kmul = (mode == MODE_SINGLE || mode == MODE_GROUP) ? int(divk.d) : 1;
   auto drow_of = [&](int rw) __attribute__((always_inline)) -> uint32_t {
     const uint32_t r = uint32_t(rw);
-    return (mode == MODE_FULL) ? r
+    return (mode == MODE_FULL || mode == MODE_BLOCK) ? r
          : (mode == MODE_SINGLE) ? r * uint32_t(kmul)
          : (r / uint32_t(kmul)) * uint32_t(kmul * kmul) + r % uint32_t(kmul);
   };
@@ -268,10 +267,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   }
   // first token of tile kt: with FIXED_ROWS, i0(kt) = kt*BN*kmul + c_j
   const int64_t tile_c0 = (mode == MODE_SINGLE) ? int64_t(j)
-                        : (mode == MODE_GROUP) ? int64_t(j) * kmul : 0;
+                        : (mode == MODE_GROUP) ? int64_t(j) * kmul
+                        : (mode == MODE_BLOCK) ? int64_t(j) * L : 0;
   auto tile_first = [&](int kt) __attribute__((always_inline)) -> uint32_t {
     if constexpr (FIXED_ROWS) return uint32_t(int64_t(kt) * BN * kmul + tile_c0);
-    else return skiparse_token(mode, uint32_t(kt * BN), j, divk);
+    else return skiparse_token(mode, uint32_t(kt * BN), j, divk, uint32_t(L));
   };
   // tile kt of the tensor at src into LDS tile dst (rows past the end read
   // as zeros: their offsets are out of the buffer's range)
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       int32_t off = dm_off[t];
       if constexpr (!FIXED_ROWS) {
         const uint32_t r = uint32_t(min(kt * BN + dm_row[t], L - 1));
-        off = int32_t((int64_t(skiparse_token(mode, r, j, divk) - i0) * a_sn + 8 * dm_col[t]) * 2);
+        off = int32_t((int64_t(skiparse_token(mode, r, j, divk, uint32_t(L)) - i0) * a_sn + 8 * dm_col[t]) * 2);
       }
       off = (dm_row[t] < L - kt * BN) ? off : kRecords;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(dst + 512 * (lw + C::LW * t)), 16,
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       const int row = idx / C::KCH, col = idx % C::KCH;
       const bool on = kt * BN + row < L;
       const uint32_t r = uint32_t(min(kt * BN + row, L - 1));
-      const uint32_t i = skiparse_token(mode, r, j, divk);
+      const uint32_t i = skiparse_token(mode, r, j, divk, uint32_t(L));
       st_reg[e] = on ? ld16(kg + int64_t(i) * a_sn + 8 * col) : make_uint4(0, 0, 0, 0);
     }
   };
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       const int row = idx / C::KCH, col = idx % C::KCH;
       uint4 val = st_reg[e];
       const int r = kt * BN + row;
-      const uint32_t i = skiparse_token(mode, uint32_t(min(r, L - 1)), j, divk);
+      const uint32_t i = skiparse_token(mode, uint32_t(min(r, L - 1)), j, divk, uint32_t(L));
       if (r < L && is_video(rg, i)) {
         const Coord3 cc = video_coords(rg, i);
         val = fast_rope ? rotate_chunk_col(rl, chunk_col(rg, 4 * col), cc, val)
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     const float inv = 1.0f / lt;
     const int r = int(qt) * C::BM + (wave * QB + qb) * 32 + l32;
     if (r < L) {
-      const uint32_t i = skiparse_token(mode, uint32_t(r), j, divk);
+      const uint32_t i = skiparse_token(mode, uint32_t(r), j, divk, uint32_t(L));
       uint16_t* p = og + int64_t(i) * a.osn;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)

@@ -117,17 +117,19 @@ void fill_rope(const osp_attn3d_desc* d, osp::RopeGeom* g) {
 }
 
 osp_status check_mode(const osp_attn3d_desc* d, int64_t n, int32_t mode, int32_t k) {
-  if (mode < OSP_MODE_FULL || mode > OSP_MODE_SKIPARSE_GROUP)
+  if (mode < OSP_MODE_FULL || mode > OSP_MODE_BLOCK)
     return fail(OSP_ERR_PARAM, "unknown mode %d", mode);
   if (mode == OSP_MODE_FULL) return OSP_OK;
   if (k < 1) return fail(OSP_ERR_PARAM, "sparse_k (%d) must be >= 1", k);
   if (d && d->n_text != 0)
-    return fail(OSP_ERR_UNSUPPORTED, "Skiparse takes no text tokens (n_text = %d)", d->n_text);
-  const int64_t div = (mode == OSP_MODE_SKIPARSE_SINGLE) ? int64_t(k) : int64_t(k) * k;
+    return fail(OSP_ERR_UNSUPPORTED, "Skiparse and block attention take no text tokens (n_text = %d)",
+                d->n_text);
+  const int64_t div = (mode == OSP_MODE_SKIPARSE_GROUP) ? int64_t(k) * k : int64_t(k);
   if (n % div)
-    return fail(OSP_ERR_SHAPE, "%s skip needs N (%lld) divisible by %lld",
-                mode == OSP_MODE_SKIPARSE_SINGLE ? "single" : "group", (long long)n,
-                (long long)div);
+    return fail(OSP_ERR_SHAPE, "%s needs N (%lld) divisible by %lld",
+                mode == OSP_MODE_SKIPARSE_SINGLE ? "single skip"
+                : mode == OSP_MODE_SKIPARSE_GROUP ? "group skip" : "block attention",
+                (long long)n, (long long)div);
   return OSP_OK;
 }
 
@@ -155,7 +157,11 @@ osp_status check_attn(const osp_attn3d_desc* d, int32_t mode, int32_t k, int32_t
   if (tiles > 0x7fffffffLL) return fail(OSP_ERR_SHAPE, "too many tiles (%lld)", (long long)tiles);
   // the loaders address one key tile through 32-bit byte offsets below 2^30
   const int64_t bn = osp::attn_keys_per_tile(d->head_dim);
-  const int64_t span = (bn + groups) * groups * s->sn * 2 + int64_t(d->head_dim) * 2;
+  // rows of one key tile span bn tokens (full, block), bn*k (single skip)
+  // or up to (bn + k)*k (group skip)
+  const int64_t rows = (mode == OSP_MODE_SKIPARSE_SINGLE) ? bn * groups
+                     : (mode == OSP_MODE_SKIPARSE_GROUP) ? (bn + groups) * groups : bn;
+  const int64_t span = rows * s->sn * 2 + int64_t(d->head_dim) * 2;
   if (span >= (int64_t(1) << 30))
     return fail(OSP_ERR_UNSUPPORTED, "token stride %lld with k=%lld spans more than 1 GiB per key tile",
                 (long long)s->sn, (long long)groups);
@@ -295,7 +301,7 @@ osp_status osp_skiparse_index(int32_t mode, int32_t sparse_k, int64_t n_tokens, 
   for (uint32_t j = 0; j < uint32_t(k); ++j)
     for (uint32_t r = 0; r < len; ++r) {
       const uint32_t pos = j * len + r;
-      const uint32_t i = osp::skiparse_token(mode, r, j, divk);
+      const uint32_t i = osp::skiparse_token(mode, r, j, divk, len);
       if (perm) perm[pos] = int32_t(i);
       if (inv) inv[i] = int32_t(pos);
     }

@@ -49,16 +49,21 @@ OSP_HD uint32_t fdiv(uint32_t n, const FastDiv& f) {
 //   single: row r of subsequence j holds token r*k + j        (i mod k = j)
 //   group:  row r of subsequence j holds token
 //           floor(r/k)*k*k + j*k + (r mod k)        (floor(i/k) mod k = j)
-enum : int32_t { MODE_FULL = 0, MODE_SINGLE = 1, MODE_GROUP = 2 };
+//   block:  row r of subsequence j holds token j*L + r   (floor(i/L) = j):
+//           the spatial half of separated spatial / temporal attention
+//           (CogVideoX section 2.2, Table 8) with k = frames, or window
+//           attention with k = N / window
+enum : int32_t { MODE_FULL = 0, MODE_SINGLE = 1, MODE_GROUP = 2, MODE_BLOCK = 3 };
 
 OSP_HD uint32_t skiparse_token(int32_t mode, uint32_t r, uint32_t j,
-                               const FastDiv& divk) {
+                               const FastDiv& divk, uint32_t len) {
   if (mode == MODE_SINGLE) return r * divk.d + j;
   if (mode == MODE_GROUP) {
     uint32_t a = fdiv(r, divk);
     uint32_t c = r - a * divk.d;
     return (a * divk.d + j) * divk.d + c;
   }
+  if (mode == MODE_BLOCK) return j * len + r;
   return r;
 }
 

@@ -1,6 +1,7 @@
-// skiparse_index.hip -- Skiparse index maps on the device (Open-Sora Plan
-// section 2.2.2): perm[j*L + r] = token of row r of subsequence j, and its
-// inverse.  Uses the same remap routine as the attention loaders.
+// skiparse_index.hip -- subsequence index maps on the device (Skiparse,
+// Open-Sora Plan section 2.2.2, and block attention): perm[j*L + r] = token
+// of row r of subsequence j, and its inverse.  Uses the same remap routine
+// as the attention loaders.
 #include "osp_internal.hpp"
 
 namespace osp {
@@ -11,7 +12,7 @@ __global__ __launch_bounds__(256) void skiparse_index_kernel(int32_t mode, uint3
   for (uint32_t pos = blockIdx.x * 256 + threadIdx.x; pos < n; pos += gridDim.x * 256) {
     const uint32_t j = fdiv(pos, div_len);
     const uint32_t r = pos - j * div_len.d;
-    const uint32_t i = skiparse_token(mode, r, j, divk);
+    const uint32_t i = skiparse_token(mode, r, j, divk, div_len.d);
     if (perm) perm[pos] = int32_t(i);
     if (inv) inv[i] = int32_t(pos);
   }

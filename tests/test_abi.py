@@ -105,6 +105,15 @@ def _code(desc, mode="full", k=1, flags=1):
     ({}, "full", 1, 0, OK),
     ({}, "full", 1, 2, OK),
     ({}, "full", 1, 8, PARAM),
+    ({}, "block", 5, 1, OK),                       # 320 = 5 * 64 (one frame each)
+    ({}, "block", 320, 1, OK),                     # every token alone
+    ({}, "block", 3, 1, SHAPE),                    # 320 % 3 != 0
+    ({}, "block", 0, 1, PARAM),
+    ({"n_text": 2, "grid": (2, 3, 53)}, "block", 2, 1, UNSUP),
+    # window attention over 28,800 tokens in windows of 64: 450 blocks
+    ({"grid": (24, 30, 40), "heads": 24, "head_dim": 96, "rope_split": (32, 32, 32)},
+     "block", 450, 1, OK),
+    ({}, 4, 1, 1, PARAM),
 ])
 def test_attn_check_codes(kw, mode, k, flags, want):
     assert _code(_desc(**kw), mode, k, flags) == want

@@ -59,3 +59,11 @@ def test_osp480_skiparse_k4(mode, variant):
 @pytest.mark.parametrize("mode,k", [("full", 1), ("skiparse_single", 4), ("skiparse_group", 4)])
 def test_osp720(mode, k):
     run_sampled("osp720", mode, k)
+
+
+@pytest.mark.parametrize("half", ["spatial", "temporal"])
+def test_osp480_separated_spatial_temporal(half):
+    # spatial: 24 frames of 1,200 tokens; temporal: 1,200 positions of 24
+    grid = grid_of(workloads.WORKLOADS["osp480"])
+    mode, k = ("block", grid[0]) if half == "spatial" else ("skiparse_single", grid[1] * grid[2])
+    run_sampled("osp480", mode, k, "unscaled")

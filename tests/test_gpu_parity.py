@@ -103,9 +103,26 @@ def test_tiny_skiparse(mode, k):
              mode=mode, sparse_k=k, tag=f"tiny-{mode}-{k}")
 
 
+@pytest.mark.parametrize("k", [1, 2, 5, 10, 64, 320])
+def test_tiny_block(k):
+    run_case(0, grid=(5, 8, 8), n_text=0, heads=2, head_dim=64, rope_split=(16, 24, 24),
+             mode="block", sparse_k=k, tag=f"tiny-block-{k}")
+
+
+@pytest.mark.parametrize("half", ["spatial", "temporal"])
+def test_separated_spatial_temporal(half):
+    # 2D+1D attention: spatial = block with k = frames (each frame's 150
+    # tokens: several key tiles, ragged); temporal = single skip with
+    # k = H*W (each (h, w) position's 6 tokens across frames)
+    grid = (6, 10, 15)
+    mode, k = ("block", grid[0]) if half == "spatial" else ("skiparse_single", grid[1] * grid[2])
+    run_case(11, grid=grid, n_text=0, heads=3, head_dim=96, rope_split=(32, 32, 32),
+             mode=mode, sparse_k=k, tag=f"2d1d-{half}")
+
+
 @pytest.mark.parametrize("variant", ["unscaled", "literal", "sharp"])
 @pytest.mark.parametrize("mode,k", [("full", 1), ("skiparse_single", 4), ("skiparse_group", 4),
-                                    ("skiparse_group", 2)])
+                                    ("skiparse_group", 2), ("block", 3)])
 def test_multitile_d96(variant, mode, k):
     # 720 tokens: several 256-row query tiles and 64-key tiles, ragged tails.
     # "sharp" multiplies Q by 4 (logit std ~4 instead of ~1).  The kernel
@@ -217,8 +234,8 @@ def test_output_strides():
 @pytest.mark.parametrize("n,k", [(320, 4), (28800, 4), (86400, 4), (720, 2), (4096, 8),
                                  (1 << 20, 16), (17550, 3), (1, 1)])
 def test_device_index_maps_bitexact(n, k):
-    for mode in ("full", "skiparse_single", "skiparse_group"):
-        div = {"full": 1, "skiparse_single": k, "skiparse_group": k * k}[mode]
+    for mode in ("full", "skiparse_single", "skiparse_group", "block"):
+        div = {"full": 1, "skiparse_single": k, "skiparse_group": k * k, "block": k}[mode]
         if n % div:
             continue
         note(f"device index map mode={mode} n={n} k={k}")

@@ -1,5 +1,5 @@
-"""Skiparse index maps from the library's host path equal the oracle's
-membership-predicate maps bit for bit.  CPU only."""
+"""Subsequence index maps (Skiparse, block) from the library's host path
+equal the oracle's membership-predicate maps bit for bit.  CPU only."""
 import numpy as np
 import pytest
 
@@ -13,8 +13,8 @@ CASES = [
 
 @pytest.mark.parametrize("n,k", CASES)
 def test_host_maps_bitexact(n, k):
-    for mode in ("full", "skiparse_single", "skiparse_group"):
-        div = k if mode == "skiparse_single" else (k * k if mode == "skiparse_group" else 1)
+    for mode in ("full", "skiparse_single", "skiparse_group", "block"):
+        div = k * k if mode == "skiparse_group" else (1 if mode == "full" else k)
         if n % div:
             with pytest.raises(osp.OspError):
                 osp.osp_skiparse_index(mode, k, n)
