@@ -165,6 +165,7 @@ def main():
     traffic = load_traffic()
 
     extra = {}
+    sep = None
     if not args.no_skiparse:
         for mode in ("skiparse_single", "skiparse_group"):
             s_step, s_launch, s_med, s_min, _ = timed(mode, 4, max(args.steps, 5), args.warmup)
@@ -172,6 +173,18 @@ def main():
             extra[mode] = {"k": 4, "ms_per_launch": round(s_launch, 4), "ms_min": round(s_min, 4),
                            "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                            "dense_equiv_tflops": round(f_full / (s_launch * 1e-3) / 1e12, 2)}
+        # separated spatial / temporal attention on the same tensors: block
+        # attention over each frame, then single skip over each (h, w) position
+        sep = {}
+        for name, mode, kk in (("spatial", "block", grid[0]),
+                               ("temporal", "skiparse_single", grid[1] * grid[2])):
+            _, s_launch, _, s_min, _ = timed(mode, kk, max(args.steps, 5), args.warmup)
+            tf = flops(kk) / (s_launch * 1e-3) / 1e12
+            sep[name] = {"mode": mode, "k": kk, "ms_per_launch": round(s_launch, 4),
+                         "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        sep["ms_spatial_plus_temporal"] = round(sep["spatial"]["ms_per_launch"] +
+                                                sep["temporal"]["ms_per_launch"], 4)
+        sep["vs_full_3d"] = round(sep["ms_spatial_plus_temporal"] / ms_launch, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -220,6 +233,7 @@ def main():
                      "flop_per_launch": f_full, "ms_per_launch": round(ms_launch, 4),
                      "ms_median": round(ms_med, 4), "ms_min": round(ms_min, 4)},
         "skiparse": extra,
+        "separated_2d1d": sep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
