@@ -67,3 +67,9 @@ def test_osp480_separated_spatial_temporal(half):
     grid = grid_of(workloads.WORKLOADS["osp480"])
     mode, k = ("block", grid[0]) if half == "spatial" else ("skiparse_single", grid[1] * grid[2])
     run_sampled("osp480", mode, k, "unscaled")
+
+
+@pytest.mark.parametrize("mode,k", [("full", 1), ("skiparse_single", 4), ("skiparse_group", 4)])
+def test_osp15_8x8x8_d128(mode, k):
+    # 121x576x1024 through the 8x8x8 VAE: 16x36x64 = 36,864 tokens, D=128
+    run_sampled("osp15", mode, k)

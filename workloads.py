@@ -18,6 +18,10 @@ Workloads (clip sizes from the pages; latent-grid arithmetic is done elsewhere):
   group).
 * ``osp720`` -- 93-frame 720x1280 clip, 24 heads, D=96, full and k=4; checked
   on 256 seeded query rows.
+* ``osp15`` -- Open-Sora Plan v1.5's 121-frame 576x1024 clip through its
+  8x8x8 VAE and 1x2x2 patchify, full and k=4; the pages give no head shape
+  for that model, so 24 heads of D=128 (split 32/48/48) are taken, which
+  also exercises the third head size.  Checked on 256 seeded query rows.
 """
 from __future__ import annotations
 
@@ -69,6 +73,10 @@ WORKLOADS = {
                        (32, 32, 32), 1e4, None, 4,
                        ("full", "skiparse_single", "skiparse_group"), 4,
                        sample_rows=256),
+    "osp15": Workload("osp15", (121, 576, 1024), 8, 8, 1, 2, None, 0, 1, 24, 128,
+                      (32, 48, 48), 1e4, None, 5,
+                      ("full", "skiparse_single", "skiparse_group"), 4,
+                      sample_rows=256),
 }
 
 
