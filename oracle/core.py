@@ -181,6 +181,40 @@ def skiparse_index(mode: str, k: int, n: int):
     return perm.astype(np.int32), inv.astype(np.int32)
 
 
+def rope3d_transpose(x: np.ndarray, grid, n_text: int, rope_split, theta: float = 1e4,
+                     pos_offset=(0, 0, 0)) -> np.ndarray:
+    """R^T x for the rotation R of ``rope3d``: every video pair turned by the
+    negative angle (x_a cos + x_b sin, -x_a sin + x_b cos).
+
+    The chain rule through y = R x gives dL/dx = R^T dL/dy, and R is a
+    product of plane rotations, so R^T turns each pair back.  Text rows are
+    unchanged, as in the forward rotation.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if sum(rope_split) != x.shape[-1] or any(s % 2 for s in rope_split):
+        raise ValueError("rope split must be even chunks summing to head_dim")
+    n_video = int(np.prod(grid))
+    if x.shape[1] != n_text + n_video:
+        raise ValueError("sequence length does not match the grid")
+    coords = video_coords(grid) + np.asarray(pos_offset, dtype=np.int64)[None, :]
+    out = x.copy()
+    c0 = 0
+    for axis, d_a in enumerate(rope_split):
+        if d_a == 0:
+            continue
+        r = np.arange(d_a // 2, dtype=np.float64)
+        omega = theta ** (-2.0 * r / d_a)
+        phi = coords[:, axis].astype(np.float64)[:, None] * omega[None, :]
+        cos = np.cos(phi)[None, :, None, :]
+        sin = np.sin(phi)[None, :, None, :]
+        xa = x[:, n_text:, :, c0 + 0:c0 + d_a:2]
+        xb = x[:, n_text:, :, c0 + 1:c0 + d_a:2]
+        out[:, n_text:, :, c0 + 0:c0 + d_a:2] = xa * cos + xb * sin
+        out[:, n_text:, :, c0 + 1:c0 + d_a:2] = -xa * sin + xb * cos
+        c0 += d_a
+    return out
+
+
 # --------------------------------------------------------------------------
 # Attention (rows a4-a7)
 # --------------------------------------------------------------------------
@@ -258,3 +292,71 @@ def attn3d(q, k, v, *, grid, n_text: int = 0, mode: str = "full",
                     o[b, dst[s0:s0 + block], h, :] = ob
                     lse[b, h, dst[s0:s0 + block]] = lb
     return o, lse
+
+
+# --------------------------------------------------------------------------
+# Backward (the training pass of the same layer)
+# --------------------------------------------------------------------------
+def softmax_attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                          sm_scale: float):
+    """Gradients of o = softmax(sm_scale * q k^T) v for one sequence.
+
+    With p the softmax rows and o = p v: dv = p^T do; dp = do v^T; the
+    softmax Jacobian gives ds = p * (dp - sum_j p_ij dp_ij) row by row;
+    s = sm_scale * q k^T then gives dq = sm_scale * ds k and
+    dk = sm_scale * ds^T q.  q: [M, D], k, v: [L, D], do: [M, D].
+    """
+    s = sm_scale * (q @ k.T)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    p /= p.sum(axis=1, keepdims=True)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq = sm_scale * (ds @ k)
+    dk = sm_scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attn3d_bwd(q, k, v, do, *, grid, n_text: int = 0, mode: str = "full",
+               sparse_k: int = 1, rope_split, theta: float = 1e4,
+               sm_scale: float | None = None, pos_offset=(0, 0, 0), rope: bool = True):
+    """Gradients of ``attn3d``'s output o with respect to q, k and v, given
+    the output gradient do ([B, N, H, D]).
+
+    The forward steps in reverse: each subsequence's attention is
+    differentiated on its own (``softmax_attention_bwd``), the gradients are
+    written back at the tokens' positions, and with ``rope`` the q and k
+    gradients pass back through the rotation (``rope3d_transpose``).  With
+    ``rope=False`` q and k are the rotated inputs and their gradients are
+    with respect to those.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    b_sz, n, h_sz, d = q.shape
+    if n != n_text + int(np.prod(grid)):
+        raise ValueError("sequence length does not match the grid")
+    if mode != "full" and n_text:
+        raise ValueError("Skiparse and block attention take no text tokens")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if rope:
+        q = rope3d(q, grid, n_text, rope_split, theta, pos_offset)
+        k = rope3d(k, grid, n_text, rope_split, theta, pos_offset)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for g in skiparse_groups(mode, sparse_k, n):
+        for b in range(b_sz):
+            for h in range(h_sz):
+                gq, gk, gv = softmax_attention_bwd(q[b, g, h, :], k[b, g, h, :], v[b, g, h, :],
+                                                   do[b, g, h, :], sm_scale)
+                dq[b, g, h, :] = gq
+                dk[b, g, h, :] = gk
+                dv[b, g, h, :] = gv
+    if rope:
+        dq = rope3d_transpose(dq, grid, n_text, rope_split, theta, pos_offset)
+        dk = rope3d_transpose(dk, grid, n_text, rope_split, theta, pos_offset)
+    return dq, dk, dv

@@ -385,9 +385,81 @@ def pin_rows_subset(o):
         assert np.allclose(la[:, :, rows], lb, rtol=0, atol=1e-14)
 
 
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+def pin_rope_transpose(o):
+    """rope3d_transpose is the adjoint of rope3d: <R x, y> = <x, R^T y>, and
+    R^T R = I (text rows, offsets and an uneven split included)."""
+    rng = _rng(31)
+    for grid, n_text, split, off in (((2, 3, 4), 0, (16, 24, 24), (0, 0, 0)),
+                                     ((3, 2, 5), 4, (4, 6, 54), (2, -1, 7))):
+        n = n_text + int(np.prod(grid))
+        x, y = (rng.standard_normal((2, n, 3, 64)) for _ in range(2))
+        lhs = (o.rope3d(x, grid, n_text, split, 1e4, off) * y).sum()
+        rhs = (x * o.rope3d_transpose(y, grid, n_text, split, 1e4, off)).sum()
+        assert abs(lhs - rhs) <= 1e-10 * abs(lhs)
+        back = o.rope3d_transpose(o.rope3d(x, grid, n_text, split, 1e4, off), grid, n_text, split,
+                                  1e4, off)
+        assert np.allclose(back, x, rtol=0, atol=1e-13)
+
+
+def pin_bwd_autograd(o):
+    """Gradients equal torch float64 autograd through scaled_dot_product_attention
+    on the rotated inputs, with the subsequences as a boolean mask."""
+    grid, split = (4, 4, 4), (16, 24, 24)
+    n = 64
+    rng = _rng(32)
+    q, k, v, do = (rng.standard_normal((2, n, 3, 64)) for _ in range(4))
+    qr = o.rope3d(q, grid, 0, split)
+    kr = o.rope3d(k, grid, 0, split)
+    for mode, kk in (("full", 1), ("skiparse_single", 4), ("skiparse_group", 2), ("block", 4)):
+        lab = np.zeros(n, dtype=np.int64)
+        for j, g in enumerate(o.skiparse_groups(mode, kk, n)):
+            lab[g] = j
+        mask = torch.from_numpy(lab[:, None] == lab[None, :])
+        tq, tk, tv = (torch.from_numpy(a).permute(0, 2, 1, 3).clone().requires_grad_(True)
+                      for a in (qr, kr, v))
+        out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask,
+                                                               scale=0.125)
+        out.backward(torch.from_numpy(do).permute(0, 2, 1, 3))
+        want = [t.grad.permute(0, 2, 1, 3).numpy() for t in (tq, tk, tv)]
+        got = o.attn3d_bwd(qr, kr, v, do, grid=grid, mode=mode, sparse_k=kk, rope_split=split,
+                           rope=False)
+        for g_, w_, name in zip(got, want, "qkv"):
+            assert np.allclose(g_, w_, rtol=0, atol=1e-12), (mode, name)
+
+
+def pin_bwd_finite_differences(o):
+    """Central differences of the forward oracle, through 3D RoPE, text tokens
+    and the subsequence modes, match the backward oracle."""
+    rng = _rng(33)
+    cases = (((2, 2, 3), 0, "full", 1), ((1, 2, 3), 2, "full", 1),
+             ((2, 2, 3), 0, "skiparse_single", 2), ((2, 2, 3), 0, "block", 3),
+             ((2, 2, 4), 0, "skiparse_group", 2))
+    split, eps = (2, 2, 4), 1e-6
+    for grid, n_text, mode, kk in cases:
+        n = n_text + int(np.prod(grid))
+        q, k, v, w = (rng.standard_normal((1, n, 1, 8)) for _ in range(4))
+        kw = dict(grid=grid, n_text=n_text, mode=mode, sparse_k=kk, rope_split=split,
+                  pos_offset=(1, 2, 3))
+        loss = lambda a, b, c: float((o.attn3d(a, b, c, **kw)[0] * w).sum())
+        grads = o.attn3d_bwd(q, k, v, w, **kw)
+        for which, g in enumerate(grads):
+            num = np.zeros_like(g)
+            for idx in np.ndindex(*g.shape):
+                args = [q.copy(), k.copy(), v.copy()]
+                args[which][idx] += eps
+                up = loss(*args)
+                args[which][idx] -= 2 * eps
+                num[idx] = (up - loss(*args)) / (2 * eps)
+            assert np.allclose(g, num, rtol=0, atol=1e-7), (mode, "qkv"[which])
+
+
 ALL_PINS = [
     pin_latent_grids, pin_video_coords, pin_rope_closed_form, pin_rope_complex,
     pin_rope_invariants, pin_rope_axis_chunks, pin_skiparse_reshape,
     pin_skiparse_structure, pin_spatial_temporal, pin_attention_sdpa, pin_attention_bruteforce,
     pin_attention_special, pin_attention_text, pin_rows_subset,
+    pin_rope_transpose, pin_bwd_autograd, pin_bwd_finite_differences,
 ]

@@ -39,6 +39,14 @@ MUTANTS = {
     "k_not_rotated": ("k = rope3d(k, grid, n_text, rope_split, theta, pos_offset)", "pass"),
     "block_strided": ("key = idx // (n // k)", "key = idx % k"),
     "block_runs_of_k": ("key = idx // (n // k)", "key = idx // k % k"),
+    "bwd_no_row_term": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp"),
+    "bwd_dk_from_ds_not_transposed": ("dk = sm_scale * (ds.T @ q)", "dk = sm_scale * (ds @ q)"),
+    "bwd_dv_from_p_not_transposed": ("dv = p.T @ do", "dv = p @ do"),
+    "bwd_dq_unscaled": ("dq = sm_scale * (ds @ k)", "dq = ds @ k"),
+    "bwd_rope_forward_not_transpose": ("dq = rope3d_transpose(dq, grid, n_text, rope_split, theta, pos_offset)",
+                                       "dq = rope3d(dq, grid, n_text, rope_split, theta, pos_offset)"),
+    "rope_transpose_sign": ("out[:, n_text:, :, c0 + 0:c0 + d_a:2] = xa * cos + xb * sin",
+                            "out[:, n_text:, :, c0 + 0:c0 + d_a:2] = xa * cos - xb * sin"),
     "perm_inverse_wrong": ("inv[perm] = np.arange(n, dtype=np.int64)", "inv[:] = perm"),
 }
 
