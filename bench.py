@@ -67,9 +67,11 @@ def parse():
                    help="heads of the workload the oracle times (all query rows each)")
     p.add_argument("--profile", action="store_true",
                    help="few steps of one attention mode only (for rocprofv3)")
+    p.add_argument("--no-backward", action="store_true", help="skip the backward line")
     p.add_argument("--profile-mode", default="full",
-                   choices=("full", "skiparse_single", "skiparse_group"),
-                   help="attention mode of --profile (Skiparse with k=4)")
+                   choices=("full", "skiparse_single", "skiparse_group", "bwd"),
+                   help="attention mode of --profile (Skiparse with k=4; bwd: the full-attention "
+                        "backward)")
     p.add_argument("--copy", type=int, default=0,
                    help="instead: time a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -125,16 +127,56 @@ def main():
     def flops(sk=1):
         return 4.0 * B * H * float(n_tok) ** 2 * D / sk
 
+    # backward: gradients with respect to the rotated q and k (then through
+    # the RoPE transpose), from the forward's o and lse
+    bwd_state = {}
+
+    def bwd_setup():
+        if bwd_state:
+            return bwd_state
+        q_rot = osp.osp_rope3d(q, grid=grid, n_text=wl.n_text, rope_split=wl.rope_split,
+                               theta=wl.theta)
+        osp.osp_rope3d(k, grid=grid, n_text=wl.n_text, rope_split=wl.rope_split,
+                       theta=wl.theta, out=k_rot)
+        o_b, lse_b = osp.osp_attn3d_fwd(q_rot, k_rot, v, grid=grid, n_text=wl.n_text,
+                                        rope_split=wl.rope_split, theta=wl.theta,
+                                        fuse_rope=False, return_lse=True)
+        dout = workloads.make_dout(wl.seed, shape, wl.input_scale).to(dev)
+        desc = osp.make_desc(batch=B, n_text=wl.n_text, grid=grid, heads=H, head_dim=D,
+                             rope_split=wl.rope_split)
+        ws = torch.empty(osp.osp_attn3d_bwd_workspace(desc), dtype=torch.uint8, device=dev)
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+        bwd_state.update(q_rot=q_rot, o=o_b, lse=lse_b, dout=dout, ws=ws, grads=grads)
+        return bwd_state
+
+    def bwd_step(marks=None):
+        st = bwd_state
+        dq, dk, dv = st["grads"]
+        if marks:
+            marks[0].record(stream)
+        osp.osp_attn3d_bwd(st["q_rot"], k_rot, v, st["o"], st["lse"], st["dout"], grid=grid,
+                           n_text=wl.n_text, dq=dq, dk=dk, dv=dv, workspace=st["ws"])
+        if marks:
+            marks[1].record(stream)
+        for t in (dq, dk):
+            osp.osp_rope3d_inv(t, grid=grid, n_text=wl.n_text, rope_split=wl.rope_split,
+                               theta=wl.theta, out=t)
+
     if args.profile:
         pm = args.profile_mode
-        pk = 1 if pm == "full" else 4
+        if pm == "bwd":
+            bwd_setup()
+            run = bwd_step
+        else:
+            pk = 1 if pm == "full" else 4
+            run = lambda: step(pm, pk)   # noqa: E731
         for _ in range(max(args.warmup, 1)):
-            step(pm, pk)
+            run()
         torch.cuda.synchronize()
         for _ in range(max(args.steps, 1)):
-            step(pm, pk)
+            run()
         torch.cuda.synchronize()
-        print(json.dumps({"profile_launches": args.steps, "workload": f"osp480 {pm} k={pk}"}))
+        print(json.dumps({"profile_launches": args.steps, "workload": f"osp480 {pm}"}))
         return
 
     def timed(mode, sk, steps, warmup):
@@ -186,6 +228,36 @@ def main():
                                                 sep["temporal"]["ms_per_launch"], 4)
         sep["vs_full_3d"] = round(sep["ms_spatial_plus_temporal"] / ms_launch, 4)
 
+    bwd = None
+    if not args.no_backward:
+        bwd_setup()
+        nb = max(args.steps // 2, 5)
+        for _ in range(args.warmup):
+            bwd_step()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(nb)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for marks in evs:
+            bwd_step(marks)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        per = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+        b_launch = sum(per) / len(per)
+        b_step = t0.elapsed_time(t1) / nb
+        # FlashAttention convention: the backward counts 2.5x the forward's
+        # flops (5 matrix products against 2); the kernels execute 7
+        f_bwd = 2.5 * f_full
+        tf = f_bwd / (b_launch * 1e-3) / 1e12
+        bwd = {"ms_per_call": round(b_launch, 4), "ms_min": round(per[0], 4),
+               "ms_per_step_with_rope_transpose": round(b_step, 4),
+               "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+               "flop_per_call": f_bwd, "executed_mfma_tflops": round(tf * 7 / 5, 2),
+               "kernels": "bwd_prep + bwd_dkdv_kernel + bwd_dq_kernel (D=96, NW=4)",
+               "fwd_plus_bwd_ms": round(ms_launch + b_launch, 4)}
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -234,6 +306,7 @@ def main():
                      "ms_median": round(ms_med, 4), "ms_min": round(ms_min, 4)},
         "skiparse": extra,
         "separated_2d1d": sep,
+        "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -1,6 +1,7 @@
 /*
- * osp.h -- C ABI of libosp: 3D-RoPE full and Skiparse attention (forward)
- * for video diffusion transformers, on AMD Instinct MI355X (gfx950).
+ * osp.h -- C ABI of libosp: 3D-RoPE full and Skiparse attention (forward
+ * and backward) for video diffusion transformers, on AMD Instinct MI355X
+ * (gfx950).
  *
  * What is computed (sources are web pages; sections named per function):
  *   - A video clip's latent grid after a causal VAE and patchify
@@ -119,6 +120,16 @@ osp_status osp_attn3d_check(const osp_attn3d_desc* desc, int32_t mode,
 osp_status osp_rope3d(const osp_attn3d_desc* desc, const void* x, void* y,
                       void* stream);
 
+/* Transpose (= inverse) of osp_rope3d: y = rotate(x) by the negative
+   angle for every video [b, n, h] row, text rows copied, same strides,
+   layout and rounding as osp_rope3d.  It maps the gradient with respect to
+   a rotated tensor to the gradient with respect to the tensor before the
+   rotation (the rotation is orthogonal, so its Jacobian's transpose is the
+   rotation by the negative angle; CogVideoX section 2.2 "3D-RoPE",
+   RoFormer).  y == x works in place. */
+osp_status osp_rope3d_inv(const osp_attn3d_desc* desc, const void* x, void* y,
+                          void* stream);
+
 /* Attention forward.
    mode: osp_mode.  sparse_k: the number k >= 1 of subsequences (ignored
    for FULL).  Skiparse (Open-Sora Plan section 2.2.2) needs N divisible by
@@ -152,6 +163,44 @@ osp_status osp_attn3d_fwd(const osp_attn3d_desc* desc, int32_t mode,
                           int32_t sparse_k, float sm_scale, int32_t flags,
                           const void* q, const void* k, const void* v, void* o,
                           float* lse, void* stream);
+
+/* Bytes of device workspace osp_attn3d_bwd needs for these settings:
+   two fp32 [B, H, N] arrays, each rounded up to 256 bytes.  Host only. */
+osp_status osp_attn3d_bwd_workspace(const osp_attn3d_desc* desc, int32_t mode,
+                                    int32_t sparse_k, int64_t* bytes);
+
+/* Attention backward: the gradients of the loss with respect to the
+   (rotated) q and k and to v, given dout = dLoss/do of the forward
+   o = softmax(sm_scale * q k^T) v, attended over the same subsequences
+   (mode, sparse_k as in osp_attn3d_fwd; CogVideoX section 2.2 "3D Full
+   Attention", Open-Sora Plan section 2.2.2).  With P = softmax rows:
+   dv = P^T dout, dP = dout v^T, dS = P o (dP - rowsum(o o dout)),
+   dq = sm_scale dS k, dk = sm_scale dS^T q.
+   q and k must be the ROTATED tensors (osp_rope3d output, or what the
+   forward rotated in its loaders); dq and dk are the gradients with
+   respect to them: apply osp_rope3d_inv to get the gradients with respect
+   to q and k before the rotation.  Text tokens (FULL only) work as in the
+   forward.
+   q, k, v, o, dout: [B, N, H, D] bf16 read with stride_*; o is the
+   forward's output.  lse: [B, H, N] fp32 contiguous, the forward's row
+   log-sum-exp (natural log).  dq, dk, dv: [B, N, H, D] bf16 written with
+   ostride_*; they must not overlap any input or each other.
+   workspace: device memory of at least osp_attn3d_bwd_workspace() bytes,
+   256-byte aligned, owned by the caller, contents on entry ignored; it is
+   in use until the enqueued work has finished.
+   sm_scale: as in osp_attn3d_fwd (<= 0 selects 1/sqrt(head_dim)); it
+   must be the forward's.
+   Arithmetic: bf16 MFMA products with fp32 accumulation; probabilities
+   exp2(sm_scale log2(e) s - lse log2(e)) in fp32, rounded to bf16 (as
+   dS) for the products that take them; outputs rounded to bf16.
+   Pointers 16-byte aligned, strides multiples of 8.  OSP_ERR_PARAM if
+   workspace_bytes is too small. */
+osp_status osp_attn3d_bwd(const osp_attn3d_desc* desc, int32_t mode,
+                          int32_t sparse_k, float sm_scale, const void* q,
+                          const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq,
+                          void* dk, void* dv, void* workspace,
+                          int64_t workspace_bytes, void* stream);
 
 /* Index maps of the subsequences of an N-token sequence (Skiparse,
    Open-Sora Plan section 2.2.2; BLOCK as above).

@@ -67,7 +67,10 @@ def lib() -> ctypes.CDLL:
             "osp_latent_grid": (I32, [I32, I32, I32, I32, I32, I32, I32, ctypes.POINTER(I32)]),
             "osp_attn3d_check": (I32, [D, I32, I32, I32]),
             "osp_rope3d": (I32, [D, P, P, P]),
+            "osp_rope3d_inv": (I32, [D, P, P, P]),
             "osp_attn3d_fwd": (I32, [D, I32, I32, F32, I32, P, P, P, P, P, P]),
+            "osp_attn3d_bwd_workspace": (I32, [D, I32, I32, ctypes.POINTER(I64)]),
+            "osp_attn3d_bwd": (I32, [D, I32, I32, F32, P, P, P, P, P, P, P, P, P, P, I64, P]),
             "osp_skiparse_index": (I32, [I32, I32, I64, P, P, I32, P]),
         }
         for name, (res, args) in sig.items():
@@ -81,7 +84,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("osp_abi_version", "osp_status_string", "osp_last_error", "osp_latent_grid",
-            "osp_attn3d_check", "osp_rope3d", "osp_attn3d_fwd", "osp_skiparse_index")
+            "osp_attn3d_check", "osp_rope3d", "osp_rope3d_inv", "osp_attn3d_fwd",
+            "osp_attn3d_bwd_workspace", "osp_attn3d_bwd", "osp_skiparse_index")
 
 
 def _check(status: int):
@@ -143,6 +147,19 @@ def osp_attn3d_check(desc: OspAttn3dDesc, mode="full", sparse_k: int = 1,
 def osp_rope3d(x: torch.Tensor, *, grid, n_text: int = 0, rope_split, theta: float = 1e4,
                pos_offset=(0, 0, 0), out: torch.Tensor | None = None) -> torch.Tensor:
     """3D RoPE of x ([B, N, H, D] bf16 on the GPU); out may be x (in place)."""
+    return _rope_call("osp_rope3d", x, grid=grid, n_text=n_text, rope_split=rope_split,
+                      theta=theta, pos_offset=pos_offset, out=out)
+
+
+def osp_rope3d_inv(x: torch.Tensor, *, grid, n_text: int = 0, rope_split, theta: float = 1e4,
+                   pos_offset=(0, 0, 0), out: torch.Tensor | None = None) -> torch.Tensor:
+    """Transpose of osp_rope3d (rotation by the negative angle): maps a
+    gradient with respect to the rotated tensor back through the rotation."""
+    return _rope_call("osp_rope3d_inv", x, grid=grid, n_text=n_text, rope_split=rope_split,
+                      theta=theta, pos_offset=pos_offset, out=out)
+
+
+def _rope_call(name, x, *, grid, n_text, rope_split, theta, pos_offset, out):
     if out is None:
         out = torch.empty_like(x)
     b, n, h, d = x.shape
@@ -151,8 +168,8 @@ def osp_rope3d(x: torch.Tensor, *, grid, n_text: int = 0, rope_split, theta: flo
                      strides=_bnhd(x, "x"), ostrides=_bnhd(out, "out"))
     if tuple(out.shape) != tuple(x.shape):
         raise ValueError("out must have the shape of x")
-    _check(lib().osp_rope3d(ctypes.byref(desc), ctypes.c_void_p(x.data_ptr()),
-                            ctypes.c_void_p(out.data_ptr()), _stream(x)))
+    _check(getattr(lib(), name)(ctypes.byref(desc), ctypes.c_void_p(x.data_ptr()),
+                                ctypes.c_void_p(out.data_ptr()), _stream(x)))
     return out
 
 
@@ -196,6 +213,53 @@ def osp_attn3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid,
         ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
         ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), _stream(q)))
     return (out, lse) if lse is not None else out
+
+
+def osp_attn3d_bwd_workspace(desc: OspAttn3dDesc, mode="full", sparse_k: int = 1) -> int:
+    """Bytes of workspace osp_attn3d_bwd needs (host-only query)."""
+    out = ctypes.c_int64(0)
+    _check(lib().osp_attn3d_bwd_workspace(ctypes.byref(desc), _mode(mode), int(sparse_k),
+                                          ctypes.byref(out)))
+    return int(out.value)
+
+
+def osp_attn3d_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                   lse: torch.Tensor, dout: torch.Tensor, *, grid, n_text: int = 0,
+                   mode="full", sparse_k: int = 1, sm_scale: float | None = None,
+                   dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                   dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Attention backward over [B, N, H, D] bf16 tensors on the GPU.
+
+    q and k are the rotated tensors; dq and dk are gradients with respect to
+    them (osp_rope3d_inv maps them back through the rotation).  lse is the
+    forward's [B, H, N] fp32 log-sum-exp.  Returns (dq, dk, dv)."""
+    b, n, h, d = q.shape
+    st = _bnhd(q, "q")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if _bnhd(t, name) != st or t.shape != q.shape:
+            raise ValueError("q, k, v, o and dout must share shape and strides")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (b, h, n) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    outs = []
+    for t in (dq, dk, dv):
+        outs.append(torch.empty((b, n, h, d), dtype=torch.bfloat16, device=q.device)
+                    if t is None else t)
+    ost = _bnhd(outs[0], "dq")
+    if any(_bnhd(t, "dk/dv") != ost or tuple(t.shape) != (b, n, h, d) for t in outs):
+        raise ValueError("dq, dk and dv must share the shape of q and one set of strides")
+    desc = make_desc(batch=b, n_text=n_text, grid=grid, heads=h, head_dim=d,
+                     rope_split=(d, 0, 0), strides=st, ostrides=ost)
+    need = osp_attn3d_bwd_workspace(desc, mode, sparse_k)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace of {need} bytes needed")
+    _check(lib().osp_attn3d_bwd(
+        ctypes.byref(desc), _mode(mode), int(sparse_k),
+        float(sm_scale) if sm_scale is not None else 0.0,
+        *(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o, lse, dout, *outs, workspace)),
+        int(workspace.numel() * workspace.element_size()), _stream(q)))
+    return tuple(outs)
 
 
 def osp_skiparse_index(mode, sparse_k: int, n_tokens: int, device=None):

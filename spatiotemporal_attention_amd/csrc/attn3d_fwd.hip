@@ -46,28 +46,13 @@
 #include <type_traits>
 
 #include "osp_internal.hpp"
+#include "osp_mfma.hpp"
 
 namespace osp {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef i16x4_t __attribute__((address_space(3))) * lds_i16x4_ptr;
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 constexpr float kTau = 8.0f;
 constexpr float kSumTau = 256.0f;   // 2^kTau
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int32_t kRecords = 0x40000000;   // buffer range of one key tile (bytes)
-
-// XOR swizzle of the 16-byte chunks of LDS row r: a permutation of the
-// row's chunks.  It is the same for rows r, r + 16 and r + 32, which keeps
-// the operand addresses of different 16/32-key blocks a constant apart.
-template <int D> __device__ __forceinline__ int chunk_swz(int r);
-template <> __device__ __forceinline__ int chunk_swz<64>(int r) { return (5 * (r >> 1)) & 7; }
-template <> __device__ __forceinline__ int chunk_swz<96>(int r) { return (r >> 2) & 3; }
-template <> __device__ __forceinline__ int chunk_swz<128>(int r) { return (5 * r) & 15; }
 
 template <int D, int QB, int BN, int NW>
 struct AttnCfg {
@@ -95,22 +80,6 @@ template <> struct RopeSmem<false> {
   __device__ RopeLds* get() { return nullptr; }
 };
 
-template <bool B> using bool_c = std::integral_constant<bool, B>;
-template <int I> using int_c = std::integral_constant<int, I>;
-
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
-
-// max / sum over lanes l and l^32
-__device__ __forceinline__ float max_pair32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_pair32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // ROPE_Q / ROPE_K: rotate Q / K in the loaders (false = already rotated).
 // FIXED_ROWS: the row -> token offsets inside a key tile are the same for
@@ -479,10 +448,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lsum[qb] += ts[qb];
   };
-  // O^T += V^T P^T for the V tile in slot SV.  Source lane (ta, te) of its
-  // 16-lane group G points at key 32kb + 16hh + 4(G/2) + te (+8), channels
-  // 32db + 16(G%2) + 4ta .. +3; the transposing read hands each lane 4 keys
-  // of one channel.
+  // O^T += V^T P^T for the V tile in slot SV; the V^T operand of keys
+  // 32kb + 16hh .. +15 comes in the key order of the score rows.
   auto pv = [&](auto slot, bf16x8_t (&pb)[QB][NKB][2]) __attribute__((always_inline)) {
     const char* vs = reinterpret_cast<const char*>(vslot(slot));
 #pragma unroll
@@ -492,12 +459,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
         bf16x8_t va[D / 32];
         const char* blk = vs + (32 * kb + 16 * hh) * C::KCH * 16;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(blk + v_off[0][db]));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(blk + v_off[1][db]));
-          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-          va[db] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
-        }
+        for (int db = 0; db < D / 32; ++db) va[db] = tr_read<D>(blk, v_off, db);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
 
 #include "../../include/osp.h"
@@ -168,6 +169,40 @@ osp_status check_attn(const osp_attn3d_desc* d, int32_t mode, int32_t k, int32_t
   return OSP_OK;
 }
 
+// Checks of an attention backward call (q and k taken as already rotated).
+osp_status check_bwd(const osp_attn3d_desc* d, int32_t mode, int32_t k, Shape* s) {
+  osp_status st = check_desc(d, true, s);
+  if (st) return st;
+  st = check_mode(d, s->n_tokens, mode, k);
+  if (st) return st;
+  const int64_t groups = (mode == OSP_MODE_FULL) ? 1 : k;
+  const int64_t len = s->n_tokens / groups;
+  const int64_t rows_total = int64_t(d->batch) * d->heads * s->n_tokens;
+  if (rows_total > 0x7fffffffLL)
+    return fail(OSP_ERR_SHAPE, "batch*heads*N = %lld exceeds 2^31-1", (long long)rows_total);
+  const int64_t rb = std::min(osp::bwd_kv_rows_per_block(d->head_dim),
+                              osp::bwd_q_rows_per_block(d->head_dim));
+  const int64_t blocks = int64_t(d->batch) * d->heads * groups * ((len + rb - 1) / rb);
+  if (blocks > 0x7fffffffLL)
+    return fail(OSP_ERR_SHAPE, "too many workgroups (%lld)", (long long)blocks);
+  // streamed tiles are addressed through 32-bit byte offsets below 2^30
+  // from their first token
+  const int64_t bn = osp::bwd_tile_rows(d->head_dim);
+  const int64_t rows = (mode == OSP_MODE_SKIPARSE_SINGLE) ? bn * groups
+                     : (mode == OSP_MODE_SKIPARSE_GROUP) ? (bn + groups) * groups : bn;
+  const int64_t span = rows * s->sn * 2 + int64_t(d->head_dim) * 2;
+  if (span >= (int64_t(1) << 30))
+    return fail(OSP_ERR_UNSUPPORTED, "token stride %lld with k=%lld spans more than 1 GiB per tile",
+                (long long)s->sn, (long long)groups);
+  return OSP_OK;
+}
+
+// bytes of one of the two fp32 [B, H, N] workspace arrays, rounded up to 256
+int64_t bwd_ws_half(const osp_attn3d_desc* d, const Shape& s) {
+  const int64_t b = int64_t(d->batch) * d->heads * s.n_tokens * 4;
+  return (b + 255) / 256 * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -213,7 +248,8 @@ osp_status osp_attn3d_check(const osp_attn3d_desc* desc, int32_t mode, int32_t s
   return st ? st : ok();
 }
 
-osp_status osp_rope3d(const osp_attn3d_desc* desc, const void* x, void* y, void* stream) {
+static osp_status rope3d_call(const osp_attn3d_desc* desc, const void* x, void* y, void* stream,
+                              int inverse) {
   Shape s;
   osp_status st = check_desc(desc, false, &s);
   if (st) return st;
@@ -228,6 +264,7 @@ osp_status osp_rope3d(const osp_attn3d_desc* desc, const void* x, void* y, void*
   a.n_tokens = int32_t(s.n_tokens);
   a.heads = desc->heads;
   a.head_dim = desc->head_dim;
+  a.inverse = inverse;
   fill_rope(desc, &a.rope);
   const uint64_t total = uint64_t(a.batch) * uint64_t(a.n_tokens) * uint64_t(a.heads) *
                          uint64_t(a.head_dim / 8);
@@ -236,6 +273,14 @@ osp_status osp_rope3d(const osp_attn3d_desc* desc, const void* x, void* y, void*
   hipError_t e = osp::launch_rope3d(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(e, "rope3d launch");
   return ok();
+}
+
+osp_status osp_rope3d(const osp_attn3d_desc* desc, const void* x, void* y, void* stream) {
+  return rope3d_call(desc, x, y, stream, 0);
+}
+
+osp_status osp_rope3d_inv(const osp_attn3d_desc* desc, const void* x, void* y, void* stream) {
+  return rope3d_call(desc, x, y, stream, 1);
 }
 
 osp_status osp_attn3d_fwd(const osp_attn3d_desc* desc, int32_t mode, int32_t sparse_k,
@@ -278,6 +323,71 @@ osp_status osp_attn3d_fwd(const osp_attn3d_desc* desc, int32_t mode, int32_t spa
                                     (flags & OSP_FUSE_ROPE_K) ? 1 : 0,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(e, "attn3d_fwd launch");
+  return ok();
+}
+
+osp_status osp_attn3d_bwd_workspace(const osp_attn3d_desc* desc, int32_t mode, int32_t sparse_k,
+                                    int64_t* bytes) {
+  if (!bytes) return fail(OSP_ERR_NULL, "bytes is NULL");
+  Shape s;
+  osp_status st = check_bwd(desc, mode, sparse_k, &s);
+  if (st) return st;
+  *bytes = 2 * bwd_ws_half(desc, s);
+  return ok();
+}
+
+osp_status osp_attn3d_bwd(const osp_attn3d_desc* desc, int32_t mode, int32_t sparse_k,
+                          float sm_scale, const void* q, const void* k, const void* v,
+                          const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                          void* dv, void* workspace, int64_t workspace_bytes, void* stream) {
+  Shape s;
+  osp_status st = check_bwd(desc, mode, sparse_k, &s);
+  if (st) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+    return fail(OSP_ERR_NULL, "q, k, v, o, lse, dout, dq, dk, dv and workspace must be non-NULL");
+  const void* bf[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : bf)
+    if (!aligned16(p)) return fail(OSP_ERR_PARAM, "bf16 tensors must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(OSP_ERR_PARAM, "lse must be 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(OSP_ERR_PARAM, "workspace must be 256-byte aligned");
+  const int64_t half = bwd_ws_half(desc, s);
+  if (workspace_bytes < 2 * half)
+    return fail(OSP_ERR_PARAM, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                (long long)(2 * half));
+  if (isnan(sm_scale) || isinf(sm_scale)) return fail(OSP_ERR_PARAM, "sm_scale must be finite");
+  const int D = desc->head_dim;
+  const double scale = sm_scale > 0.f ? double(sm_scale) : 1.0 / sqrt(double(D));
+  const int32_t groups = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
+  osp::BwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.neg_delta = static_cast<float*>(workspace);
+  a.neg_lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + half);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.sb = s.sb; a.sn = s.sn; a.sh = s.sh;
+  a.osb = s.osb; a.osn = s.osn; a.osh = s.osh;
+  a.batch = desc->batch;
+  a.heads = desc->heads;
+  a.n_tokens = int32_t(s.n_tokens);
+  a.groups = groups;
+  a.seq_len = int32_t(s.n_tokens / groups);
+  a.mode = mode;
+  a.divk = osp::make_fastdiv(uint32_t(groups));
+  a.scale = float(scale);
+  a.scale_log2 = float(scale * 1.4426950408889634);
+  const int kvr = osp::bwd_kv_rows_per_block(D), qr = osp::bwd_q_rows_per_block(D);
+  a.kv_blocks = (a.seq_len + kvr - 1) / kvr;
+  a.q_blocks = (a.seq_len + qr - 1) / qr;
+  if (a.seq_len == 0) return ok();
+  hipError_t e = osp::launch_attn3d_bwd(a, D, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "attn3d_bwd launch");
   return ok();
 }
 

@@ -40,10 +40,43 @@ struct RopeArgs {
   uint16_t* y;
   int64_t sb, sn, sh, osb, osn, osh;
   int32_t batch, n_tokens, heads, head_dim;
+  int32_t inverse;              // rotate by the negative angle (the transpose)
   RopeGeom rope;
 };
 
 hipError_t launch_rope3d(const RopeArgs& a, hipStream_t s);
+
+// One attention backward call, after validation.  q, k, v, o, dout are
+// read with the input strides, dq, dk, dv written with the output strides.
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;             // [B, H, N] natural-log units
+  float* neg_delta;             // workspace [B, H, N]: -sum_d o * dout
+  float* neg_lse2;              // workspace [B, H, N]: -lse * log2(e)
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int64_t sb, sn, sh;
+  int64_t osb, osn, osh;
+  int32_t batch, heads, n_tokens, seq_len, groups, mode;
+  int32_t kv_blocks;            // per (b, h, subsequence): key rows / rows per dK-dV workgroup
+  int32_t q_blocks;             // per (b, h, subsequence): query rows / rows per dQ workgroup
+  FastDiv divk;
+  float scale;                  // sm_scale
+  float scale_log2;             // sm_scale * log2(e)
+};
+
+// Rows handled by one workgroup of the dK/dV and of the dQ kernel, and the
+// rows of one streamed LDS tile.
+int bwd_kv_rows_per_block(int head_dim);
+int bwd_q_rows_per_block(int head_dim);
+int bwd_tile_rows(int head_dim);
+
+hipError_t launch_attn3d_bwd(const BwdArgs& a, int head_dim, hipStream_t s);
 
 hipError_t launch_skiparse_index(int32_t mode, int32_t k, int32_t n, int32_t* perm,
                                  int32_t* inv, hipStream_t s);

@@ -12,6 +12,12 @@ namespace osp {
 
 constexpr int kRopeThreads = 256;
 
+// (x0, x1) -> (x0, -x1) for the 4 bf16 pairs of a chunk (sign bit only, exact)
+__device__ __forceinline__ uint4 flip_pairs(uint4 v) {
+  v.x ^= 0x80000000u; v.y ^= 0x80000000u; v.z ^= 0x80000000u; v.w ^= 0x80000000u;
+  return v;
+}
+
 __global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(const RopeArgs a,
                                                                uint32_t total,
                                                                FastDiv div_row_chunks,
@@ -35,7 +41,13 @@ __global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(const RopeArgs a,
     const uint16_t* src = a.x + int64_t(b) * a.sb + int64_t(n) * a.sn + int64_t(h) * a.sh + 8 * ch;
     uint16_t* dst = a.y + int64_t(b) * a.osb + int64_t(n) * a.osn + int64_t(h) * a.osh + 8 * ch;
     uint4 v = *reinterpret_cast<const uint4*>(src);
-    if (is_video(a.rope, n)) v = rotate_chunk(a.rope, &rl, 4 * int(ch), video_coords(a.rope, n), v);
+    if (is_video(a.rope, n)) {
+      // the transpose of a rotation is the rotation by the negative angle:
+      // negate the second channel of every pair before and after rotating
+      if (a.inverse) v = flip_pairs(v);
+      v = rotate_chunk(a.rope, &rl, 4 * int(ch), video_coords(a.rope, n), v);
+      if (a.inverse) v = flip_pairs(v);
+    }
     *reinterpret_cast<uint4*>(dst) = v;
   }
 }

@@ -145,6 +145,47 @@ def test_null_and_alignment_errors_before_launch():
     assert lib.osp_skiparse_index(1, 2, -1, buf.ctypes.data_as(ctypes.c_void_p), None, 0, None) == SHAPE
 
 
+def test_bwd_workspace_size_and_checks():
+    d = _desc(batch=2, heads=3, grid=(5, 7, 9))          # N = 315
+    half = (2 * 3 * 315 * 4 + 255) // 256 * 256
+    assert osp.osp_attn3d_bwd_workspace(d) == 2 * half
+    assert osp.osp_attn3d_bwd_workspace(_desc(), "skiparse_group", 4) == 2 * (2 * 320 * 4)
+    for kw, mode, k, want in [({}, "skiparse_single", 3, SHAPE), ({}, "block", 0, PARAM),
+                              ({"head_dim": 80, "rope_split": (16, 32, 32)}, "full", 1, UNSUP),
+                              ({"n_text": 2, "grid": (2, 3, 53)}, "skiparse_group", 2, UNSUP),
+                              ({"grid": (2000, 2000, 1000)}, "full", 1, SHAPE),
+                              ({"grid": (200, 100, 100), "heads": 1100}, "full", 1, SHAPE)]:
+        with pytest.raises(osp.OspError) as e:
+            osp.osp_attn3d_bwd_workspace(_desc(**kw), mode, k)
+        assert e.value.code == want and e.value.message
+    # text tokens are fine for full attention (the backward does not rotate)
+    assert osp.osp_attn3d_bwd_workspace(_desc(n_text=37)) > 0
+
+
+def test_bwd_null_alignment_and_workspace_errors_before_launch():
+    lib = osp.lib()
+    d = _desc()
+    f = ctypes.c_void_p(4096)
+    ws = osp.osp_attn3d_bwd_workspace(d)
+
+    def call(desc=ctypes.byref(d), q=f, lse=f, dq=f, ws_ptr=f, ws_bytes=ws, scale=0.0):
+        return lib.osp_attn3d_bwd(desc, 0, 1, scale, q, f, f, f, lse, f, dq, f, f, ws_ptr,
+                                  ws_bytes, None)
+    assert call(desc=None) == NULL
+    assert call(q=None) == NULL
+    assert call(lse=None) == NULL
+    assert call(ws_ptr=None) == NULL
+    assert call(q=ctypes.c_void_p(4098)) == PARAM
+    assert call(dq=ctypes.c_void_p(4104)) == PARAM
+    assert call(lse=ctypes.c_void_p(4098)) == PARAM
+    assert call(ws_ptr=ctypes.c_void_p(4096 + 64)) == PARAM    # 256-byte alignment
+    assert call(ws_bytes=ws - 4) == PARAM
+    assert b"workspace" in lib.osp_last_error()
+    assert call(scale=float("inf")) == PARAM
+    assert lib.osp_rope3d_inv(ctypes.byref(d), None, f, None) == NULL
+    assert lib.osp_rope3d_inv(ctypes.byref(d), f, ctypes.c_void_p(4100), None) == PARAM
+
+
 def test_success_clears_last_error():
     lib = osp.lib()
     osp.osp_attn3d_check(_desc())

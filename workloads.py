@@ -106,6 +106,11 @@ def make_qkv(seed, shape, scale: float | None = None, q_mult: float | None = Non
     return q, k, v
 
 
+def make_dout(seed, shape, scale: float | None = None):
+    """Output gradient dO for the backward, bf16 CPU tensor (tensor id 3)."""
+    return gaussian_bf16(seed, 3, shape, scale)
+
+
 def sample_rows(seed: int, n_tokens: int, count: int) -> np.ndarray:
     """Sorted, distinct query rows drawn with ``default_rng([seed, 99])``."""
     rng = np.random.default_rng([int(seed), 99])
