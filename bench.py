@@ -37,7 +37,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn3d_fwd_osp480_traffic.json")
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("attn3d_fwd.hip", "osp_rope.hpp", "osp_common.hpp", "osp_internal.hpp"):
+    for name in ("attn3d_fwd.hip", "osp_mfma.hpp", "osp_rope.hpp", "osp_common.hpp",
+                 "osp_internal.hpp"):
         with open(os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -255,7 +256,7 @@ def main():
                "ms_per_step_with_rope_transpose": round(b_step, 4),
                "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                "flop_per_call": f_bwd, "executed_mfma_tflops": round(tf * 7 / 5, 2),
-               "kernels": "bwd_prep + bwd_dkdv_kernel + bwd_dq_kernel (D=96, NW=4)",
+               "kernels": "bwd_prep + bwd_dkdv_kernel (8 waves, pairs, KB=1) + bwd_dq_kernel (4 waves), D=96",
                "fwd_plus_bwd_ms": round(ms_launch + b_launch, 4)}
 
     cpu = None

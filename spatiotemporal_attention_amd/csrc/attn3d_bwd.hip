@@ -12,21 +12,24 @@
 // from O and dO, before the blocked passes (the FlashAttention-2 backward).
 //
 // Three kernels:
-//  1. bwd_prep: per row, -delta and -lse * log2(e) into the workspace.
-//  2. bwd_dkdv: a workgroup owns NW*32 keys of one (batch, head,
-//     subsequence), 32 per wave, K and V in registers, and streams the
-//     subsequence's queries through LDS in tiles of 64 rows (Q, dO and the
-//     two workspace rows).  Per 32-query block:
-//       S = Q K^T and dP - delta = dO V^T - delta, with the rows of the Q /
-//       dO tile as A operand and K / V as B (the C init of the second
-//       carries -delta): a lane holds ONE key (column l%32) and 16 queries;
-//       P = exp2(scale log2(e) S - lse log2(e)), dS = P o (dP - delta), each
-//       packed to bf16 as a B operand in the C row order;
-//       dV^T += dO^T P and dK^T += Q^T dS, their A operands read transposed
-//       from the same LDS tiles (ds_read_b64_tr_b16) in that row order.
+//  1. bwd_prep: per row, -delta and -lse / scale into the workspace.
+//  2. bwd_dkdv: a workgroup of 8 waves owns 4*KB*32 keys of one (batch,
+//     head, subsequence) and streams the subsequence's queries through LDS
+//     in tiles of 64 rows (Q, dO and the two workspace rows).  The waves
+//     work in pairs on the same keys: the P wave (K rows in registers)
+//     forms S - lse/scale = Q K^T - lse/scale, the dS wave (V rows) forms
+//     dP - delta = dO V^T - delta, with the rows of the Q / dO tile as A
+//     operand and K / V as B and the row terms as the C init, so a lane
+//     holds ONE key (column l%32) and 16 queries; P = exp2(scale log2(e)
+//     (S - lse/scale)) goes from the P wave to the dS wave through LDS,
+//     dS = P o (dP - delta); both are packed to bf16 as B operands in the C
+//     row order, and dV^T += dO^T P (P wave), dK^T += Q^T dS (dS wave)
+//     take their A operands transposed from the same LDS tiles
+//     (ds_read_b64_tr_b16) in that row order.
 //  3. bwd_dq: a workgroup owns NW*32 queries, 32 per wave, Q and dO in
-//     registers, and streams the keys (K and V tiles): S^T = K Q^T,
-//     dP^T - delta = V dO^T - delta (a lane holds ONE query), P^T and dS^T
+//     registers, and streams the keys (K and V tiles): S^T - lse/scale =
+//     K Q^T - lse/scale, dP^T - delta = V dO^T - delta (a lane holds ONE
+//     query, so both row terms are one value per lane), P^T and dS^T
 //     as above, dQ^T += K^T dS^T with K^T read transposed.
 // dQ gets a pass of its own instead of atomic fp32 adds from the dK/dV
 // pass: the score products are formed twice (7 MFMA products per 32x32
@@ -41,35 +44,45 @@
 
 namespace osp {
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBwdRows = 64;         // rows of one streamed LDS tile
 constexpr int kPrepThreads = 256;
 
-// waves per workgroup of the two blocked kernels, and the waves per SIMD
-// their register budget is sized for
+// Geometry of the blocked kernels.  Both stream 64-row tiles through LDS,
+// each loaded by 4 waves (the dQ kernel's 4 waves load K and V; in the
+// dK/dV kernel the 4 waves of each role load their tensor).
 template <int D> struct BwdCfg {
-  static constexpr int NW = 4;
-  static constexpr int OCC_KV = (D == 64) ? 2 : 1;
-  static constexpr int OCC_Q = (D == 128) ? 1 : 2;
   static constexpr int KCH = D / 8;                       // 16-byte chunks per row
   static constexpr int TILE = kBwdRows * D;               // bf16 elements of a tile
-  static constexpr int DPW = kBwdRows * KCH / 64 / NW;    // DMA loads per wave and tensor
-  static_assert((kBwdRows * KCH / 64) % NW == 0, "every wave loads the same share");
+  static constexpr int LW = 4;                            // waves loading one tensor
+  static constexpr int DPW = kBwdRows * KCH / 64 / LW;    // DMA loads per wave and tensor
+  static_assert((kBwdRows * KCH / 64) % LW == 0, "every loading wave has the same share");
+  // dK/dV: 4 pairs of waves, each pair owning KB blocks of 32 keys
+  static constexpr int KB = (D == 64) ? 2 : 1;
+  static constexpr int KV_ROWS = 4 * KB * 32;
+  // dQ: 4 waves of 32 queries each
+  static constexpr int NW_Q = 4;
+  static constexpr int OCC_Q = (D == 128) ? 1 : 2;
+  static constexpr int Q_ROWS = NW_Q * 32;
 };
 
-static int bwd_waves(int head_dim) {
+int bwd_kv_rows_per_block(int head_dim) {
   switch (head_dim) {
-    case 64: return BwdCfg<64>::NW;
-    case 96: return BwdCfg<96>::NW;
-    default: return BwdCfg<128>::NW;
+    case 64: return BwdCfg<64>::KV_ROWS;
+    case 96: return BwdCfg<96>::KV_ROWS;
+    default: return BwdCfg<128>::KV_ROWS;
   }
 }
-int bwd_kv_rows_per_block(int head_dim) { return bwd_waves(head_dim) * 32; }
-int bwd_q_rows_per_block(int head_dim) { return bwd_waves(head_dim) * 32; }
+int bwd_q_rows_per_block(int head_dim) {
+  switch (head_dim) {
+    case 64: return BwdCfg<64>::Q_ROWS;
+    case 96: return BwdCfg<96>::Q_ROWS;
+    default: return BwdCfg<128>::Q_ROWS;
+  }
+}
 int bwd_tile_rows(int) { return kBwdRows; }
 
 // ---------------------------------------------------------------------------
-// 1. -delta_i = -sum_d O_id dO_id and -lse_i log2(e), per (b, h, token);
+// 1. -delta_i = -sum_d O_id dO_id and -lse_i / scale, per (b, h, token);
 //    thread idx = (b*H + h)*N + n, the workspace layout.
 template <int D>
 __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdArgs a, uint32_t total,
@@ -95,7 +108,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdArgs a,
     }
   }
   a.neg_delta[idx] = -((acc[0] + acc[1]) + (acc[2] + acc[3]));
-  a.neg_lse2[idx] = -a.lse[idx] * kLog2e;
+  a.neg_lse_s[idx] = -a.lse[idx] / a.scale;
 }
 
 // ---------------------------------------------------------------------------
@@ -122,9 +135,9 @@ __device__ __forceinline__ BwdBlock bwd_block(const BwdArgs& a, uint32_t blocks_
   return r;
 }
 
-// LDS DMA of row tiles: wave w issues the 64-lane loads w + NW*u, u < DPW,
-// of each tile; position p = 64*(w + NW*u) + lane of the tile is row
-// p / KCH, stored chunk p % KCH, which holds logical chunk
+// LDS DMA of row tiles: loading wave w (of LW) issues the 64-lane loads
+// w + LW*u, u < DPW, of each tile; position p = 64*(w + LW*u) + lane of the
+// tile is row p / KCH, stored chunk p % KCH, which holds logical chunk
 // (p % KCH) ^ chunk_swz(row).
 template <int D>
 struct TileDma {
@@ -132,10 +145,10 @@ struct TileDma {
   int row[C::DPW], col[C::DPW];
   int32_t off[C::DPW];   // byte offsets of the current tile, relative to its first token
 
-  __device__ __forceinline__ void init(int wave, int lane) {
+  __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
     for (int u = 0; u < C::DPW; ++u) {
-      const int p = 64 * (wave + C::NW * u) + lane;
+      const int p = 64 * (w + C::LW * u) + lane;
       row[u] = p / C::KCH;
       col[u] = (p % C::KCH) ^ chunk_swz<D>(row[u]);
     }
@@ -184,11 +197,31 @@ __device__ __forceinline__ void load_row_operand(const uint16_t* row, bool valid
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK, dV.
-template <int D, int NW, int OCC>
-__global__ __launch_bounds__(NW * 64, OCC) void bwd_dkdv_kernel(const BwdArgs a) {
+// 2. dK, dV.  8 waves in 4 pairs; pair p owns KB blocks of 32 keys.  In a
+// pair, wave p (the P wave, K rows in registers) forms S - lse/scale and
+// P, and accumulates dV^T; wave p + 4 (the dS wave, V rows in registers)
+// forms dP - delta, takes P from the P wave through LDS, and accumulates
+// dK^T.  Both waves of a pair sit on one SIMD, so each one's exp or
+// multiply work overlaps the other's MFMAs, and each wave holds one K-or-V
+// operand and one accumulator set instead of two.
+//
+// Per 32-query block qb of a tile, two phases split by a workgroup barrier:
+//   1. both: X = A_rows . R + C0 (MFMA; A_rows = Q rows, R = K, C0 =
+//      -lse/scale for the P wave; dO rows, V, -delta for the dS wave);
+//      P wave: P = exp2(scale log2(e) X), written to the exchange buffer
+//      (fp32) and packed to bf16;
+//   2. dS wave: dS = P o X, packed; both: acc += T^T B (T = dO for the P
+//      wave with B = P, Q for the dS wave with B = dS; T^T read transposed).
+// The exchange buffer alternates between two halves from block to block:
+// a half is rewritten two blocks later, after the barrier that the reading
+// wave reaches only once it has used it.  KB = 2 (64 keys per pair) halves
+// the LDS reads per product but needs more than the 256 registers a wave
+// gets at two waves per SIMD for head_dim 96 and 128, so those take KB = 1.
+template <int D>
+__global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
-  constexpr int KCH = C::KCH;
+  constexpr int KCH = C::KCH, KB = C::KB;
+  constexpr int XB = 4 * KB * 4 * 64;          // float4 per exchange half
   // two slots per streamed tensor, separate arrays so that the compiler
   // sees that a DMA into one slot does not touch the other
   __shared__ __attribute__((aligned(1024))) uint16_t q_s0[C::TILE];
@@ -199,6 +232,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void bwd_dkdv_kernel(const BwdArgs a)
   __shared__ __attribute__((aligned(256))) float l_s1[kBwdRows];
   __shared__ __attribute__((aligned(256))) float e_s0[kBwdRows];
   __shared__ __attribute__((aligned(256))) float e_s1[kBwdRows];
+  __shared__ __attribute__((aligned(1024))) float4 x_s0[XB];
+  __shared__ __attribute__((aligned(1024))) float4 x_s1[XB];
   auto qslot = [&](auto sl) __attribute__((always_inline)) -> uint16_t* {
     if constexpr (decltype(sl)::value == 0) return q_s0; else return q_s1;
   };
@@ -211,10 +246,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void bwd_dkdv_kernel(const BwdArgs a)
   auto eslot = [&](auto sl) __attribute__((always_inline)) -> float* {
     if constexpr (decltype(sl)::value == 0) return e_s0; else return e_s1;
   };
+  auto xslot = [&](auto h) __attribute__((always_inline)) -> float4* {
+    if constexpr (decltype(h)::value == 0) return x_s0; else return x_s1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool pw = wave < 4;          // P wave (else dS wave)
+  const int pr = wave & 3;           // pair, and rank among the loading waves of a role
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
@@ -227,143 +267,210 @@ __global__ __launch_bounds__(NW * 64, OCC) void bwd_dkdv_kernel(const BwdArgs a)
   const int64_t bhn = (int64_t(wb.b) * a.heads + wb.h) * a.n_tokens;
   const float c2 = a.scale_log2;
 
-  // ---- this lane's key: K and V rows as B operands
-  const int kr = int(wb.blk) * NW * 32 + wave * 32 + l32;
-  const bool kvalid = kr < L;
-  const uint32_t ki = skiparse_token(mode, uint32_t(kvalid ? kr : 0), wb.j, divk, uint32_t(L));
-  bf16x8_t kreg[D / 16], vreg[D / 16];
-  load_row_operand<D>(a.k + in_off + int64_t(ki) * sn, kvalid, g, kreg);
-  load_row_operand<D>(a.v + in_off + int64_t(ki) * sn, kvalid, g, vreg);
-
-  f32x16_t dk[D / 32], dv[D / 32];
+  // ---- this lane's keys (one per key block): K rows (P wave) or V rows
+  // (dS wave) as B operands
+  bf16x8_t xreg[KB][D / 16];
+  uint32_t ktok[KB];
+  bool kval[KB];
+  {
+    const uint16_t* src = (pw ? a.k : a.v) + in_off;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      dk[db][e] = 0.f;
-      dv[db][e] = 0.f;
+    for (int kb = 0; kb < KB; ++kb) {
+      const int r = int(wb.blk) * C::KV_ROWS + (pr * KB + kb) * 32 + l32;
+      kval[kb] = r < L;
+      ktok[kb] = skiparse_token(mode, uint32_t(kval[kb] ? r : 0), wb.j, divk, uint32_t(L));
+      load_row_operand<D>(src + int64_t(ktok[kb]) * sn, kval[kb], g, xreg[kb]);
     }
+  }
+
+  f32x16_t acc[KB][D / 32];          // dV^T (P wave) or dK^T (dS wave)
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[kb][db][e] = 0.f;
   int r_off[D / 16];
   row_read_offsets<D>(lane, r_off);
   int t_off[2][D / 32];
   tr_read_offsets<D>(lane, t_off);
 
+  // ---- loads: the P waves load the Q tile and the -lse/scale row, the dS
+  // waves the dO tile and the -delta row
   TileDma<D> dma;
-  dma.init(wave, lane);
-  const uint16_t* qg = a.q + in_off;
-  const uint16_t* dg = a.dout + in_off;
-  // the tile of src (this (b, h)'s base) whose first token is i0 into dst
-  auto load = [&](const uint16_t* src, uint32_t i0, uint16_t* dst) __attribute__((always_inline)) {
+  dma.init(pr, lane);
+  const uint16_t* tsrc = (pw ? a.q : a.dout) + in_off;
+  const float* fsrc = (pw ? a.neg_lse_s : a.neg_delta) + bhn;
+  auto load = [&](uint32_t i0, uint16_t* dst) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(src + int64_t(i0) * sn), (short)0, kRecords, 0x00020000);
+        const_cast<uint16_t*>(tsrc + int64_t(i0) * sn), (short)0, kRecords, 0x00020000);
 #pragma unroll
     for (int u = 0; u < C::DPW; ++u) {
       const int32_t off = dma.off[u];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(dst + 512 * (wave + NW * u)),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(dst + 512 * (pr + C::LW * u)),
                                                16, off, 0, 0, 0);
     }
   };
-  // one fp32 per row of the tile (a workspace row), by one wave
-  auto load_floats = [&](const float* src, uint32_t i0, int t, float* dst) __attribute__((always_inline)) {
+  auto load_floats = [&](uint32_t i0, int t, float* dst) __attribute__((always_inline)) {
     const int r = t * kBwdRows + lane;
     const uint32_t i = skiparse_token(mode, uint32_t(min(r, L - 1)), wb.j, divk, uint32_t(L));
     const int32_t off = (r < L) ? int32_t((i - i0) * 4) : kRecords;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(src + i0), (short)0, kRecords, 0x00020000);
+        const_cast<float*>(fsrc + i0), (short)0, kRecords, 0x00020000);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 4, off, 0, 0, 0);
   };
   auto issue = [&](int t, auto sl) __attribute__((always_inline)) {
     const uint32_t i0 = dma.at(t, mode, wb.j, divk, L, sn);
-    load(qg, i0, qslot(sl));
-    load(dg, i0, dslot(sl));
-    if (wave == 0) load_floats(a.neg_lse2 + bhn, i0, t, lslot(sl));
-    if (wave == 1) load_floats(a.neg_delta + bhn, i0, t, eslot(sl));
-  };
-
-  auto compute = [&](auto sl) __attribute__((always_inline)) {
-    const char* qs = reinterpret_cast<const char*>(qslot(sl));
-    const char* ds = reinterpret_cast<const char*>(dslot(sl));
-    const float* ls = lslot(sl);
-    const float* es = eslot(sl);
-#pragma unroll
-    for (int qb = 0; qb < kBwdRows / 32; ++qb) {
-      const char* qblk = qs + 32 * qb * KCH * 16;
-      const char* dblk = ds + 32 * qb * KCH * 16;
-      // C rows of this lane: queries 32qb + 8i + 4g + 0..3, i = 0..3
-      f32x16_t s, dp;
-      float nl[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 e4 = *reinterpret_cast<const float4*>(es + 32 * qb + 8 * i + 4 * g);
-        const float4 l4 = *reinterpret_cast<const float4*>(ls + 32 * qb + 8 * i + 4 * g);
-        dp[4 * i + 0] = e4.x; dp[4 * i + 1] = e4.y; dp[4 * i + 2] = e4.z; dp[4 * i + 3] = e4.w;
-        nl[4 * i + 0] = l4.x; nl[4 * i + 1] = l4.y; nl[4 * i + 2] = l4.z; nl[4 * i + 3] = l4.w;
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = 0.f;
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qblk + r_off[c]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[c], s, 0, 0, 0);
-        const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(dblk + r_off[c]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[c], dp, 0, 0, 0);
-      }
-      bf16x8_t pb[2], sb[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        uint32_t pw[4], sw[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int e0 = 8 * hh + 2 * t, e1 = e0 + 1;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[e0], c2, nl[e0]));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[e1], c2, nl[e1]));
-          pw[t] = pack_bf16(p0, p1);
-          sw[t] = pack_bf16(p0 * dp[e0], p1 * dp[e1]);
-        }
-        pb[hh] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-        sb[hh] = __builtin_bit_cast(bf16x8_t, make_uint4(sw[0], sw[1], sw[2], sw[3]));
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const char* qh = qblk + 16 * hh * KCH * 16;
-        const char* dh = dblk + 16 * hh * KCH * 16;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(dh, t_off, db), pb[hh], dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(qh, t_off, db), sb[hh], dk[db], 0, 0, 0);
-        }
-      }
+    if (pw) {
+      load(i0, qslot(sl));
+      if (pr == 0) load_floats(i0, t, lslot(sl));
+    } else {
+      load(i0, dslot(sl));
+      if (pr == 0) load_floats(i0, t, eslot(sl));
     }
   };
 
-  const int nqt = (L + kBwdRows - 1) / kBwdRows;
-  issue(0, int_c<0>{});
-  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-  __syncthreads();
-  for (int t = 0; t < nqt; t += 2) {
-    if (t + 1 < nqt) issue(t + 1, int_c<1>{});
-    compute(int_c<0>{});
-    __builtin_amdgcn_s_waitcnt(0x0070);
-    __syncthreads();
-    if (t + 1 >= nqt) break;
-    if (t + 2 < nqt) issue(t + 2, int_c<0>{});
-    compute(int_c<1>{});
-    __builtin_amdgcn_s_waitcnt(0x0070);
-    __syncthreads();
-  }
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  if (kvalid) {
-    const int64_t out = int64_t(wb.b) * a.osb + int64_t(wb.h) * a.osh + int64_t(ki) * a.osn;
-    store_rows_t<D>(a.dk + out, dk, a.scale, g);
-    store_rows_t<D>(a.dv + out, dv, 1.0f, g);
-  }
+  // phase 1 of block qb for role R (true: P wave) from tile slot SL into
+  // exchange half XH; x: the phase-1 products, bop: the phase-2 B operands
+  // (P or dS)
+  auto phase1 = [&](auto role, auto sl, auto xh, int qb, f32x16_t (&x)[KB], bf16x8_t (&bop)[KB][2])
+      __attribute__((always_inline)) {
+    constexpr bool R = decltype(role)::value;
+    const char* rows = reinterpret_cast<const char*>(R ? qslot(sl) : dslot(sl)) + 32 * qb * KCH * 16;
+    const float* c0 = (R ? lslot(sl) : eslot(sl)) + 32 * qb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(c0 + 8 * i + 4 * g);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        x[kb][4 * i + 0] = v.x; x[kb][4 * i + 1] = v.y; x[kb][4 * i + 2] = v.z; x[kb][4 * i + 3] = v.w;
+      }
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const bf16x8_t ra = *reinterpret_cast<const bf16x8_t*>(rows + r_off[c]);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        x[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra, xreg[kb][c], x[kb], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if constexpr (R) {
+      float4* xo = xslot(xh) + pr * KB * 4 * 64 + lane;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[kb][e] = __builtin_amdgcn_exp2f(x[kb][e] * c2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          xo[(kb * 4 + i) * 64] = make_float4(x[kb][4 * i], x[kb][4 * i + 1], x[kb][4 * i + 2],
+                                              x[kb][4 * i + 3]);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t w[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) w[t] = pack_bf16(x[kb][8 * hh + 2 * t], x[kb][8 * hh + 2 * t + 1]);
+          bop[kb][hh] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+      }
+      // the stores must have landed before the barrier that publishes them
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    }
+  };
+  auto phase2 = [&](auto role, auto sl, auto xh, int qb, f32x16_t (&x)[KB], bf16x8_t (&bop)[KB][2])
+      __attribute__((always_inline)) {
+    constexpr bool R = decltype(role)::value;
+    if constexpr (!R) {
+      const float4* xi = xslot(xh) + pr * KB * 4 * 64 + lane;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 p = xi[(kb * 4 + i) * 64];
+          x[kb][4 * i + 0] *= p.x; x[kb][4 * i + 1] *= p.y;
+          x[kb][4 * i + 2] *= p.z; x[kb][4 * i + 3] *= p.w;
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t w[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) w[t] = pack_bf16(x[kb][8 * hh + 2 * t], x[kb][8 * hh + 2 * t + 1]);
+          bop[kb][hh] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+      }
+    }
+    const char* tsl = reinterpret_cast<const char*>(R ? dslot(sl) : qslot(sl)) + 32 * qb * KCH * 16;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const char* blk = tsl + 16 * hh * KCH * 16;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8_t ta = tr_read<D>(blk, t_off, db);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          acc[kb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, bop[kb][hh], acc[kb][db], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // end of a tile: this wave's DMA has landed, then every wave's has (and
+  // every wave is done reading the tile slot that the next DMA refills)
+  auto tile_end = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    barrier();
+  };
+  // the whole query loop of one role (the two roles run the same sequence
+  // of barriers)
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    f32x16_t x[KB];
+    bf16x8_t bop[KB][2];
+    // the two blocks of the tile in slot SL
+    auto tile = [&](auto sl) __attribute__((always_inline)) {
+      phase1(role, sl, int_c<0>{}, 0, x, bop);
+      barrier();
+      phase2(role, sl, int_c<0>{}, 0, x, bop);
+      phase1(role, sl, int_c<1>{}, 1, x, bop);
+      barrier();
+      phase2(role, sl, int_c<1>{}, 1, x, bop);
+    };
+    const int nqt = (L + kBwdRows - 1) / kBwdRows;
+    issue(0, int_c<0>{});
+    tile_end();
+    for (int t = 0; t < nqt; t += 2) {
+      if (t + 1 < nqt) issue(t + 1, int_c<1>{});
+      tile(int_c<0>{});
+      tile_end();
+      if (t + 1 >= nqt) break;
+      if (t + 2 < nqt) issue(t + 2, int_c<0>{});
+      tile(int_c<1>{});
+      tile_end();
+    }
+  };
+  if (pw) run(bool_c<true>{});
+  else run(bool_c<false>{});
+
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    if (kval[kb]) {
+      const int64_t out = int64_t(wb.b) * a.osb + int64_t(wb.h) * a.osh + int64_t(ktok[kb]) * a.osn;
+      if (pw) store_rows_t<D>(a.dv + out, acc[kb], 1.0f, g);
+      else store_rows_t<D>(a.dk + out, acc[kb], a.scale, g);
+    }
 }
 
 // ---------------------------------------------------------------------------
 // 3. dQ.
-template <int D, int NW, int OCC>
-__global__ __launch_bounds__(NW * 64, OCC) void bwd_dq_kernel(const BwdArgs a) {
+template <int D>
+__global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
+  constexpr int NW = C::NW_Q;
   constexpr int KCH = C::KCH;
   __shared__ __attribute__((aligned(1024))) uint16_t k_s0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t k_s1[C::TILE];
@@ -398,7 +505,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void bwd_dq_kernel(const BwdArgs a) {
   bf16x8_t qreg[D / 16], oreg[D / 16];
   load_row_operand<D>(a.q + in_off + int64_t(qi) * sn, qvalid, g, qreg);
   load_row_operand<D>(a.dout + in_off + int64_t(qi) * sn, qvalid, g, oreg);
-  const float nl = qvalid ? a.neg_lse2[bhn + qi] : 0.f;
+  const float nl = qvalid ? a.neg_lse_s[bhn + qi] : 0.f;
   const float ne = qvalid ? a.neg_delta[bhn + qi] : 0.f;
 
   f32x16_t dq[D / 32];
@@ -421,7 +528,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < C::DPW; ++u) {
       const int32_t off = dma.off[u];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(dst + 512 * (wave + NW * u)),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(dst + 512 * (wave + C::LW * u)),
                                                16, off, 0, 0, 0);
     }
   };
@@ -444,7 +551,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void bwd_dq_kernel(const BwdArgs a) {
       f32x16_t s, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        s[e] = 0.f;
+        s[e] = nl;
         dp[e] = ne;
       }
 #pragma unroll
@@ -461,8 +568,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const int e0 = 8 * hh + 2 * tt, e1 = e0 + 1;
-          float p0 = __builtin_amdgcn_exp2f(fmaf(s[e0], c2, nl));
-          float p1 = __builtin_amdgcn_exp2f(fmaf(s[e1], c2, nl));
+          float p0 = __builtin_amdgcn_exp2f(s[e0] * c2);
+          float p1 = __builtin_amdgcn_exp2f(s[e1] * c2);
           if (tail) {
             const int key0 = t * kBwdRows + 32 * kb + 8 * (e0 >> 2) + 4 * g + (e0 & 3);
             p0 = (key0 < L) ? p0 : 0.f;
@@ -516,12 +623,11 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t seqs = uint32_t(a.batch) * uint32_t(a.heads) * uint32_t(a.groups);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, C::NW, C::OCC_KV>), dim3(seqs * uint32_t(a.kv_blocks)),
-                     dim3(C::NW * 64), 0, s, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(seqs * uint32_t(a.kv_blocks)), dim3(512), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, C::NW, C::OCC_Q>), dim3(seqs * uint32_t(a.q_blocks)),
-                     dim3(C::NW * 64), 0, s, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(seqs * uint32_t(a.q_blocks)), dim3(C::NW_Q * 64),
+                     0, s, a);
   return hipGetLastError();
 }
 

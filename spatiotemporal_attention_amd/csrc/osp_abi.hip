@@ -367,7 +367,7 @@ osp_status osp_attn3d_bwd(const osp_attn3d_desc* desc, int32_t mode, int32_t spa
   a.dout = static_cast<const uint16_t*>(dout);
   a.lse = lse;
   a.neg_delta = static_cast<float*>(workspace);
-  a.neg_lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + half);
+  a.neg_lse_s = reinterpret_cast<float*>(static_cast<char*>(workspace) + half);
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);

@@ -56,7 +56,7 @@ struct BwdArgs {
   const uint16_t* dout;
   const float* lse;             // [B, H, N] natural-log units
   float* neg_delta;             // workspace [B, H, N]: -sum_d o * dout
-  float* neg_lse2;              // workspace [B, H, N]: -lse * log2(e)
+  float* neg_lse_s;             // workspace [B, H, N]: -lse / sm_scale
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
