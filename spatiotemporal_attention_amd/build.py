@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libosp.so")
 
-SOURCES = ["osp_abi.hip", "attn3d_fwd.hip", "attn3d_bwd.hip", "rope3d.hip", "skiparse_index.hip"]
+SOURCES = ["osp_abi.hip", "attn3d_fwd.hip", "attn3d_short.hip", "attn3d_bwd.hip", "rope3d.hip",
+           "skiparse_index.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

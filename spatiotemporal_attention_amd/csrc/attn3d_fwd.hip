@@ -673,6 +673,7 @@ static hipError_t launch_d(const AttnArgs& a, int rope_q, int rope_k, hipStream_
 }
 
 hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_q, int rope_k, hipStream_t s) {
+  if (a.seq_len <= kShortRows) return launch_attn3d_short(a, head_dim, rope_q, rope_k, s);
   switch (head_dim) {
     case 64: return launch_d<64>(a, rope_q, rope_k, s);
     case 96: return launch_d<96>(a, rope_q, rope_k, s);

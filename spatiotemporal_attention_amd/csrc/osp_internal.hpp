@@ -33,7 +33,12 @@ int attn_rows_per_block(int head_dim);
 int attn_keys_per_tile(int head_dim);
 
 // rope_q / rope_k: rotate Q / K in the loaders (0 = already rotated).
+// Subsequences of at most kShortRows rows go to the one-wave-per-unit
+// kernel (launch_attn3d_short), longer ones to the flash kernel.
+constexpr int kShortRows = 64;
 hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_q, int rope_k, hipStream_t s);
+hipError_t launch_attn3d_short(const AttnArgs& a, int head_dim, int rope_q, int rope_k,
+                               hipStream_t s);
 
 struct RopeArgs {
   const uint16_t* x;

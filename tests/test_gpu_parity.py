@@ -230,6 +230,43 @@ def test_output_strides():
     assert not big[:, :, 0].any() and not big[:, :, 3].any()
 
 
+# --------------------------------------- short subsequences (L <= 64 rows)
+# One wave per (batch, head, subsequence): temporal attention, small windows,
+# Skiparse at large k, and whole sequences of at most 64 tokens.
+@pytest.mark.parametrize("grid,n_text,d,split,mode,k,batch", [
+    ((24, 6, 5), 0, 96, (32, 32, 32), "skiparse_single", 30, 1),     # temporal, L = 24
+    ((33, 2, 3), 0, 64, (16, 24, 24), "skiparse_single", 6, 2),      # L = 33: two blocks
+    ((8, 4, 4), 0, 128, (32, 48, 48), "skiparse_single", 2, 1),      # L = 64
+    ((8, 4, 4), 0, 128, (32, 48, 48), "skiparse_group", 4, 1),       # L = 32
+    ((5, 4, 8), 0, 96, (36, 36, 24), "block", 5, 2),                 # windows of 32
+    ((5, 4, 8), 0, 64, (16, 24, 24), "skiparse_group", 4, 1),        # L = 40
+    ((2, 3, 4), 7, 64, (16, 24, 24), "full", 1, 2),                  # text + video, N = 31
+    ((3, 4, 5), 2, 96, (32, 32, 32), "full", 1, 1),                  # N = 62
+])
+def test_short_subsequences(grid, n_text, d, split, mode, k, batch):
+    run_case(21, grid=grid, n_text=n_text, heads=3, head_dim=d, rope_split=split, mode=mode,
+             sparse_k=k, batch=batch, tag=f"short-{mode}-{k}")
+    run_case(22, grid=grid, n_text=n_text, heads=3, head_dim=d, rope_split=split, mode=mode,
+             sparse_k=k, batch=batch, q_mult=4.0, tag=f"short-sharp-{mode}-{k}", tol=4.0)
+
+
+def test_short_fused_equals_unfused_and_fully_written():
+    args = dict(grid=(24, 6, 5), n_text=0, heads=5, head_dim=96, rope_split=(32, 32, 32),
+                mode="skiparse_single", sparse_k=30)
+    a, la = run_case(23, **args, tag="short-fused")
+    b, lb = run_case(23, **args, fuse_rope="q", tag="short-fuse=q")
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    # 5 heads x 30 subsequences = 150 units: a partly filled last workgroup
+    _, (q, k, v) = qkv_for(23, (1, 720, 5, 96))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((1, 5, 720), float("nan"), device=q.device)
+    osp.osp_attn3d_fwd(q, k, v, grid=(24, 6, 5), rope_split=(32, 32, 32),
+                       mode="skiparse_single", sparse_k=30, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    assert torch.equal(o, a)
+
+
 # ------------------------------------------------------------ index maps
 @pytest.mark.parametrize("n,k", [(320, 4), (28800, 4), (86400, 4), (720, 2), (4096, 8),
                                  (1 << 20, 16), (17550, 3), (1, 1)])
