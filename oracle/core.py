@@ -39,7 +39,10 @@ design notes):
     attention, and window attention) attends within k runs of N/k adjacent
     tokens; with the row-major unfold, k = T gives each frame's H*W tokens,
     and the temporal half (same (h, w) across frames) is Single Skip with
-    k = H*W.
+    k = H*W;
+13. a packed sequence (several videos in one sequence) attends block
+    diagonally, each video within itself, with RoPE positions from 0 on its
+    own grid.
 
 Parity status: grid arithmetic, rotation and attention are pinned by closed
 forms, invariants, a library routine and brute force (tests/test_oracle_*.py).
@@ -291,6 +294,54 @@ def attn3d(q, k, v, *, grid, n_text: int = 0, mode: str = "full",
                     ob, lb = softmax_attention(q[b, sel, h, :], kk, vv, sm_scale)
                     o[b, dst[s0:s0 + block], h, :] = ob
                     lse[b, h, dst[s0:s0 + block]] = lb
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# Packed sequences (several videos in one sequence)
+# --------------------------------------------------------------------------
+def packed_segments(segments):
+    """(start, end, n_text, grid) of each segment of a packed sequence, in
+    order; ``segments`` is a list of (n_text, (T, H, W))."""
+    out, start = [], 0
+    for n_text, grid in segments:
+        end = start + int(n_text) + int(np.prod(grid))
+        out.append((start, end, int(n_text), tuple(int(x) for x in grid)))
+        start = end
+    return out
+
+
+def attn3d_packed(q, k, v, *, segments, mode: str = "full", sparse_k: int = 1,
+                  rope_split, theta: float = 1e4, sm_scale: float | None = None,
+                  pos_offset=(0, 0, 0), rope: bool = True):
+    """Attention over a packed sequence: several videos of different
+    durations and resolutions, each with its own text tokens in front, one
+    after the other in one sequence (CogVideoX section 3.1 "Multi-Resolution
+    Frame Pack", after Patch'n Pack, its reference [21]).
+
+    Reading: every video attends only to its own tokens (the packed
+    sequence's attention is block diagonal: packing exists to batch unequal
+    shapes, not to let videos see each other), and its 3D RoPE positions
+    start from 0 on its own grid (section 3.1 keeps RoPE by extrapolation,
+    each video taking the front of the position table).  Each segment is
+    then exactly ``attn3d`` on its slice.  Returns o [B, N, H, D] and lse
+    [B, H, N] over the packed N.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b_sz, n, h_sz, d = q.shape
+    segs = packed_segments(segments)
+    if not segs or segs[-1][1] != n:
+        raise ValueError("segments do not cover the sequence")
+    o = np.full(q.shape, np.nan)
+    lse = np.full((b_sz, h_sz, n), np.nan)
+    for start, end, n_text, grid in segs:
+        os_, ls_ = attn3d(q[:, start:end], k[:, start:end], v[:, start:end], grid=grid,
+                          n_text=n_text, mode=mode, sparse_k=sparse_k, rope_split=rope_split,
+                          theta=theta, sm_scale=sm_scale, pos_offset=pos_offset, rope=rope)
+        o[:, start:end] = os_
+        lse[:, :, start:end] = ls_
     return o, lse
 
 

@@ -456,10 +456,46 @@ def pin_bwd_finite_differences(o):
             assert np.allclose(g, num, rtol=0, atol=1e-7), (mode, "qkv"[which])
 
 
+def pin_packed_block_diagonal(o):
+    """A packed sequence equals torch float64 SDPA over the whole sequence
+    with a block-diagonal mask, each segment rotated on its own grid from
+    position 0; a single segment equals attn3d; reversing the segments
+    reverses the output blocks."""
+    split = (16, 24, 24)
+    segs = [(3, (2, 3, 4)), (0, (1, 4, 5)), (5, (3, 2, 2)), (0, (2, 2, 2))]
+    lay = o.packed_segments(segs)
+    n = lay[-1][1]
+    rng = _rng(34)
+    q, k, v = (rng.standard_normal((2, n, 2, 64)) for _ in range(3))
+    qr, kr = np.empty_like(q), np.empty_like(k)
+    lab = np.zeros(n, dtype=np.int64)
+    for idx, (s0, s1, nt, grid) in enumerate(lay):
+        qr[:, s0:s1] = o.rope3d(q[:, s0:s1], grid, nt, split)
+        kr[:, s0:s1] = o.rope3d(k[:, s0:s1], grid, nt, split)
+        lab[s0:s1] = idx
+    mask = lab[:, None] == lab[None, :]
+    want = _sdpa64(qr, kr, v, 0.125, mask)
+    got, lse = o.attn3d_packed(q, k, v, segments=segs, rope_split=split)
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+    assert np.isfinite(lse).all()
+    one, lone = o.attn3d(q[:, :lay[0][1]], k[:, :lay[0][1]], v[:, :lay[0][1]], grid=(2, 3, 4),
+                         n_text=3, rope_split=split)
+    g1, l1 = o.attn3d_packed(q[:, :lay[0][1]], k[:, :lay[0][1]], v[:, :lay[0][1]],
+                             segments=segs[:1], rope_split=split)
+    assert np.array_equal(one, g1) and np.array_equal(lone, l1)
+    rev = segs[::-1]
+    rlay = o.packed_segments(rev)
+    perm = np.concatenate([np.arange(s0, s1) for s0, s1, _, _ in lay[::-1]])
+    gr, _ = o.attn3d_packed(q[:, perm], k[:, perm], v[:, perm], segments=rev, rope_split=split)
+    assert np.allclose(gr, got[:, perm], rtol=0, atol=1e-12)
+    assert rlay[0][1] == lay[-1][1] - lay[-1][0]
+
+
 ALL_PINS = [
     pin_latent_grids, pin_video_coords, pin_rope_closed_form, pin_rope_complex,
     pin_rope_invariants, pin_rope_axis_chunks, pin_skiparse_reshape,
     pin_skiparse_structure, pin_spatial_temporal, pin_attention_sdpa, pin_attention_bruteforce,
     pin_attention_special, pin_attention_text, pin_rows_subset,
     pin_rope_transpose, pin_bwd_autograd, pin_bwd_finite_differences,
+    pin_packed_block_diagonal,
 ]
