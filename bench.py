@@ -69,6 +69,7 @@ def parse():
     p.add_argument("--profile", action="store_true",
                    help="few steps of one attention mode only (for rocprofv3)")
     p.add_argument("--no-backward", action="store_true", help="skip the backward line")
+    p.add_argument("--no-packed", action="store_true", help="skip the frame-pack line")
     p.add_argument("--profile-mode", default="full",
                    choices=("full", "skiparse_single", "skiparse_group", "bwd"),
                    help="attention mode of --profile (Skiparse with k=4; bwd: the full-attention "
@@ -229,6 +230,40 @@ def main():
                                                 sep["temporal"]["ms_per_launch"], 4)
         sep["vs_full_3d"] = round(sep["ms_spatial_plus_temporal"] / ms_launch, 4)
 
+    packed = None
+    if not args.no_packed:
+        # CogVideoX Multi-Resolution Frame Pack: four clips with their text
+        # in one sequence, block-diagonal attention
+        pk = workloads.COGVIDEOX_PACK
+        wlc = workloads.WORKLOADS[pk["base"]]
+        segs = [(pk["n_text"], osp.osp_latent_grid(*c, wlc.c_t, wlc.c_s, wlc.p_t, wlc.p_s))
+                for c in pk["clips"]]
+        lens = [nt + g[0] * g[1] * g[2] for nt, g in segs]
+        pshape = (1, sum(lens), wlc.heads, wlc.head_dim)
+        qp, kp, vp = (t.to(dev) for t in workloads.make_qkv(pk["seed"], pshape))
+        op = torch.empty_like(qp)
+        runp = lambda: osp.osp_attn3d_packed_fwd(qp, kp, vp, segments=segs,   # noqa: E731
+                                                 rope_split=wlc.rope_split, out=op)
+        for _ in range(args.warmup):
+            runp()
+        torch.cuda.synchronize()
+        npk = max(args.steps // 2, 5)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(npk):
+            runp()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        p_ms = t0.elapsed_time(t1) / npk
+        f_pack = sum(4.0 * wlc.heads * float(L) ** 2 * wlc.head_dim for L in lens)
+        tf = f_pack / (p_ms * 1e-3) / 1e12
+        packed = {"segments": [[nt, list(g)] for nt, g in segs], "tokens": sum(lens),
+                  "heads": wlc.heads, "head_dim": wlc.head_dim, "ms_per_call": round(p_ms, 4),
+                  "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                  "flop_per_call": f_pack,
+                  "launches": f"one per segment ({len(segs)}), fused 3D RoPE on Q and K"}
+
     bwd = None
     if not args.no_backward:
         bwd_setup()
@@ -308,6 +343,7 @@ def main():
         "skiparse": extra,
         "separated_2d1d": sep,
         "backward": bwd,
+        "packed": packed,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -87,6 +87,13 @@ typedef struct {
   int64_t ostride_b, ostride_n, ostride_h; /* O (and rope3d output)            */
 } osp_attn3d_desc;
 
+/* One video of a packed sequence: n_text text tokens, then the
+   grid_t x grid_h x grid_w video tokens. */
+typedef struct {
+  int32_t n_text;
+  int32_t grid_t, grid_h, grid_w;
+} osp_segment;
+
 /* ABI version compiled into the library (OSP_ABI_VERSION). */
 int32_t osp_abi_version(void);
 
@@ -119,6 +126,30 @@ osp_status osp_attn3d_check(const osp_attn3d_desc* desc, int32_t mode,
    Pointers 16-byte aligned, strides multiples of 8. */
 osp_status osp_rope3d(const osp_attn3d_desc* desc, const void* x, void* y,
                       void* stream);
+
+/* Attention forward over a packed sequence: n_segments videos of different
+   durations and resolutions, each [n_text text | grid video tokens], one
+   after the other along N (CogVideoX section 3.1 "Multi-Resolution Frame
+   Pack").  Each video attends only to its own tokens (block-diagonal
+   attention) and its RoPE positions start from 0 on its own grid, so
+   segment s gives exactly what osp_attn3d_fwd gives on its slice of the
+   tensors with desc's grid and n_text set to the segment's.  mode,
+   sparse_k, sm_scale and flags apply to every segment and are checked per
+   segment (Skiparse and block need n_text == 0 and N_s divisible as in
+   osp_attn3d_fwd).  desc supplies batch, heads, head_dim, the RoPE
+   settings and the strides; its n_text and grid_* are ignored, and the
+   contiguous default strides use the packed length N = sum of the
+   segment lengths.  q, k, v, o: [B, N, H, D]; lse: NULL or [B, H, N] fp32
+   contiguous over the packed N.  segments: host array, read during the
+   call only.  Every segment is checked before anything is enqueued; the
+   segments then run one launch each, in order, on the stream. */
+osp_status osp_attn3d_packed_fwd(const osp_attn3d_desc* desc,
+                                 const osp_segment* segments,
+                                 int32_t n_segments, int32_t mode,
+                                 int32_t sparse_k, float sm_scale,
+                                 int32_t flags, const void* q, const void* k,
+                                 const void* v, void* o, float* lse,
+                                 void* stream);
 
 /* Transpose (= inverse) of osp_rope3d: y = rotate(x) by the negative
    angle for every video [b, n, h] row, text rows copied, same strides,

@@ -313,7 +313,7 @@ def packed_segments(segments):
 
 def attn3d_packed(q, k, v, *, segments, mode: str = "full", sparse_k: int = 1,
                   rope_split, theta: float = 1e4, sm_scale: float | None = None,
-                  pos_offset=(0, 0, 0), rope: bool = True):
+                  pos_offset=(0, 0, 0), rope: bool = True, rows=None):
     """Attention over a packed sequence: several videos of different
     durations and resolutions, each with its own text tokens in front, one
     after the other in one sequence (CogVideoX section 3.1 "Multi-Resolution
@@ -325,7 +325,9 @@ def attn3d_packed(q, k, v, *, segments, mode: str = "full", sparse_k: int = 1,
     start from 0 on its own grid (section 3.1 keeps RoPE by extrapolation,
     each video taking the front of the position table).  Each segment is
     then exactly ``attn3d`` on its slice.  Returns o [B, N, H, D] and lse
-    [B, H, N] over the packed N.
+    [B, H, N] over the packed N; with ``rows`` (sorted packed token
+    indices) only those query rows, as o [B, len(rows), H, D] and lse
+    [B, H, len(rows)].
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -334,14 +336,19 @@ def attn3d_packed(q, k, v, *, segments, mode: str = "full", sparse_k: int = 1,
     segs = packed_segments(segments)
     if not segs or segs[-1][1] != n:
         raise ValueError("segments do not cover the sequence")
-    o = np.full(q.shape, np.nan)
-    lse = np.full((b_sz, h_sz, n), np.nan)
+    out_rows = np.arange(n, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.full((b_sz, len(out_rows), h_sz, d), np.nan)
+    lse = np.full((b_sz, h_sz, len(out_rows)), np.nan)
     for start, end, n_text, grid in segs:
+        sel = np.nonzero((out_rows >= start) & (out_rows < end))[0]
+        if sel.size == 0:
+            continue
         os_, ls_ = attn3d(q[:, start:end], k[:, start:end], v[:, start:end], grid=grid,
                           n_text=n_text, mode=mode, sparse_k=sparse_k, rope_split=rope_split,
-                          theta=theta, sm_scale=sm_scale, pos_offset=pos_offset, rope=rope)
-        o[:, start:end] = os_
-        lse[:, :, start:end] = ls_
+                          theta=theta, sm_scale=sm_scale, pos_offset=pos_offset, rope=rope,
+                          rows=out_rows[sel] - start)
+        o[:, sel] = os_
+        lse[:, :, sel] = ls_
     return o, lse
 
 

@@ -46,6 +46,11 @@ class OspAttn3dDesc(ctypes.Structure):
     ]
 
 
+class OspSegment(ctypes.Structure):
+    _fields_ = [("n_text", ctypes.c_int32), ("grid_t", ctypes.c_int32),
+                ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -69,6 +74,8 @@ def lib() -> ctypes.CDLL:
             "osp_rope3d": (I32, [D, P, P, P]),
             "osp_rope3d_inv": (I32, [D, P, P, P]),
             "osp_attn3d_fwd": (I32, [D, I32, I32, F32, I32, P, P, P, P, P, P]),
+            "osp_attn3d_packed_fwd": (I32, [D, ctypes.POINTER(OspSegment), I32, I32, I32, F32,
+                                            I32, P, P, P, P, P, P]),
             "osp_attn3d_bwd_workspace": (I32, [D, I32, I32, ctypes.POINTER(I64)]),
             "osp_attn3d_bwd": (I32, [D, I32, I32, F32, P, P, P, P, P, P, P, P, P, P, I64, P]),
             "osp_skiparse_index": (I32, [I32, I32, I64, P, P, I32, P]),
@@ -85,6 +92,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("osp_abi_version", "osp_status_string", "osp_last_error", "osp_latent_grid",
             "osp_attn3d_check", "osp_rope3d", "osp_rope3d_inv", "osp_attn3d_fwd",
+            "osp_attn3d_packed_fwd",
             "osp_attn3d_bwd_workspace", "osp_attn3d_bwd", "osp_skiparse_index")
 
 
@@ -209,6 +217,52 @@ def osp_attn3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid,
     _check(lib().osp_attn3d_fwd(
         ctypes.byref(desc), _mode(mode), int(sparse_k),
         float(sm_scale) if sm_scale is not None else 0.0, flags,
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+        ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), _stream(q)))
+    return (out, lse) if lse is not None else out
+
+
+def _flags(fuse_rope) -> int:
+    if fuse_rope is True:
+        return OSP_FUSE_ROPE
+    if fuse_rope is False or fuse_rope is None:
+        return 0
+    return {"q": OSP_FUSE_ROPE_Q, "k": OSP_FUSE_ROPE_K, "qk": OSP_FUSE_ROPE}[fuse_rope]
+
+
+def osp_attn3d_packed_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, segments,
+                          mode="full", sparse_k: int = 1, rope_split, theta: float = 1e4,
+                          sm_scale: float | None = None, fuse_rope=True, pos_offset=(0, 0, 0),
+                          out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                          return_lse: bool = False):
+    """Attention forward over a packed [B, N, H, D] sequence of several
+    videos; ``segments`` lists (n_text, (T, H, W)) in order along N."""
+    b, n, h, d = q.shape
+    st = _bnhd(q, "q")
+    if _bnhd(k, "k") != st or _bnhd(v, "v") != st or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must share shape and strides")
+    if out is None:
+        out = torch.empty((b, n, h, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (b, h, n)
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    segs = (OspSegment * len(segments))()
+    total = 0
+    for i, (n_text, grid) in enumerate(segments):
+        segs[i].n_text = int(n_text)
+        segs[i].grid_t, segs[i].grid_h, segs[i].grid_w = (int(x) for x in grid)
+        total += int(n_text) + int(grid[0]) * int(grid[1]) * int(grid[2])
+    if total != n:
+        raise ValueError(f"segments cover {total} tokens, the tensors hold {n}")
+    desc = make_desc(batch=b, n_text=0, grid=(1, 1, n), heads=h, head_dim=d,
+                     rope_split=rope_split, theta=theta, pos_offset=pos_offset, strides=st,
+                     ostrides=_bnhd(out, "out"))
+    _check(lib().osp_attn3d_packed_fwd(
+        ctypes.byref(desc), segs, len(segments), _mode(mode), int(sparse_k),
+        float(sm_scale) if sm_scale is not None else 0.0, _flags(fuse_rope),
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
         ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
         ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), _stream(q)))

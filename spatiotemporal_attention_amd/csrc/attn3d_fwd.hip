@@ -609,7 +609,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
           *reinterpret_cast<uint2*>(p + 32 * db + 8 * r4 + 4 * g) = make_uint2(w0, w1);
         }
       if (a.lse && g == 0)
-        a.lse[(int64_t(b) * a.heads + h) * a.n_tokens + i] = (mref[qb] + __log2f(lt)) * kLn2;
+        a.lse[(int64_t(b) * a.heads + h) * a.lse_ld + i] = (mref[qb] + __log2f(lt)) * kLn2;
     }
   }
 }

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
           *reinterpret_cast<uint2*>(p + 32 * db + 8 * r4 + 4 * g) = make_uint2(w0, w1);
         }
       if (a.lse && g == 0)
-        a.lse[(int64_t(b) * a.heads + h) * a.n_tokens + i] = (m + __log2f(lt)) * 0.69314718055994530942f;
+        a.lse[(int64_t(b) * a.heads + h) * a.lse_ld + i] = (m + __log2f(lt)) * 0.69314718055994530942f;
     }
   }
 }

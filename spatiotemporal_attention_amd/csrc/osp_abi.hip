@@ -197,6 +197,47 @@ osp_status check_bwd(const osp_attn3d_desc* d, int32_t mode, int32_t k, Shape* s
   return OSP_OK;
 }
 
+osp_status check_fwd_pointers(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, float sm_scale) {
+  if (!q || !k || !v || !o) return fail(OSP_ERR_NULL, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(OSP_ERR_PARAM, "q, k, v and o must be 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(OSP_ERR_PARAM, "lse must be 4-byte aligned");
+  if (isnan(sm_scale) || isinf(sm_scale)) return fail(OSP_ERR_PARAM, "sm_scale must be finite");
+  return OSP_OK;
+}
+
+// Kernel arguments of one checked forward call; lse_ld: the lse row length.
+void fill_fwd_args(const osp_attn3d_desc* desc, const Shape& s, int32_t mode, int32_t sparse_k,
+                   float sm_scale, const void* q, const void* k, const void* v, void* o,
+                   float* lse, int64_t lse_ld, osp::AttnArgs* out) {
+  const int D = desc->head_dim;
+  const double scale = sm_scale > 0.f ? double(sm_scale) : 1.0 / sqrt(double(D));
+  const int32_t groups = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
+  osp::AttnArgs& a = *out;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.lse_ld = lse_ld;
+  a.sb = s.sb; a.sn = s.sn; a.sh = s.sh;
+  a.osb = s.osb; a.osn = s.osn; a.osh = s.osh;
+  a.batch = desc->batch;
+  a.heads = desc->heads;
+  a.n_tokens = int32_t(s.n_tokens);
+  a.groups = groups;
+  a.seq_len = int32_t(s.n_tokens / groups);
+  a.mode = mode;
+  a.divk = osp::make_fastdiv(uint32_t(groups));
+  a.scale_log2 = float(scale * 1.4426950408889634);
+  const int bm = osp::attn_rows_per_block(D);
+  a.q_tiles = (a.seq_len + bm - 1) / bm;
+  a.total_tiles = a.batch * a.heads * groups * a.q_tiles;
+  fill_rope(desc, &a.rope);
+}
+
 // bytes of one of the two fp32 [B, H, N] workspace arrays, rounded up to 256
 int64_t bwd_ws_half(const osp_attn3d_desc* d, const Shape& s) {
   const int64_t b = int64_t(d->batch) * d->heads * s.n_tokens * 4;
@@ -289,40 +330,78 @@ osp_status osp_attn3d_fwd(const osp_attn3d_desc* desc, int32_t mode, int32_t spa
   Shape s;
   osp_status st = check_attn(desc, mode, sparse_k, flags, &s);
   if (st) return st;
-  if (!q || !k || !v || !o) return fail(OSP_ERR_NULL, "q, k, v and o must be non-NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(OSP_ERR_PARAM, "q, k, v and o must be 16-byte aligned");
-  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
-    return fail(OSP_ERR_PARAM, "lse must be 4-byte aligned");
-  if (isnan(sm_scale) || isinf(sm_scale)) return fail(OSP_ERR_PARAM, "sm_scale must be finite");
-  const int D = desc->head_dim;
-  const double scale = sm_scale > 0.f ? double(sm_scale) : 1.0 / sqrt(double(D));
-  const int32_t groups = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
+  st = check_fwd_pointers(q, k, v, o, lse, sm_scale);
+  if (st) return st;
   osp::AttnArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.o = static_cast<uint16_t*>(o);
-  a.lse = lse;
-  a.sb = s.sb; a.sn = s.sn; a.sh = s.sh;
-  a.osb = s.osb; a.osn = s.osn; a.osh = s.osh;
-  a.batch = desc->batch;
-  a.heads = desc->heads;
-  a.n_tokens = int32_t(s.n_tokens);
-  a.groups = groups;
-  a.seq_len = int32_t(s.n_tokens / groups);
-  a.mode = mode;
-  a.divk = osp::make_fastdiv(uint32_t(groups));
-  a.scale_log2 = float(scale * 1.4426950408889634);
-  const int bm = osp::attn_rows_per_block(D);
-  a.q_tiles = (a.seq_len + bm - 1) / bm;
-  a.total_tiles = a.batch * a.heads * groups * a.q_tiles;
-  fill_rope(desc, &a.rope);
+  fill_fwd_args(desc, s, mode, sparse_k, sm_scale, q, k, v, o, lse, s.n_tokens, &a);
   if (a.total_tiles == 0) return ok();
-  hipError_t e = osp::launch_attn3d(a, D, (flags & OSP_FUSE_ROPE_Q) ? 1 : 0,
+  hipError_t e = osp::launch_attn3d(a, desc->head_dim, (flags & OSP_FUSE_ROPE_Q) ? 1 : 0,
                                     (flags & OSP_FUSE_ROPE_K) ? 1 : 0,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(e, "attn3d_fwd launch");
+  return ok();
+}
+
+osp_status osp_attn3d_packed_fwd(const osp_attn3d_desc* desc, const osp_segment* segments,
+                                 int32_t n_segments, int32_t mode, int32_t sparse_k,
+                                 float sm_scale, int32_t flags, const void* q, const void* k,
+                                 const void* v, void* o, float* lse, void* stream) {
+  if (!desc) return fail(OSP_ERR_NULL, "desc is NULL");
+  if (!segments) return fail(OSP_ERR_NULL, "segments is NULL");
+  if (n_segments < 1) return fail(OSP_ERR_PARAM, "n_segments (%d) must be >= 1", n_segments);
+  // every segment is checked before anything is enqueued
+  int64_t total = 0;
+  for (int32_t i = 0; i < n_segments; ++i) {
+    osp_attn3d_desc d = *desc;
+    d.n_text = segments[i].n_text;
+    d.grid_t = segments[i].grid_t;
+    d.grid_h = segments[i].grid_h;
+    d.grid_w = segments[i].grid_w;
+    Shape s;
+    osp_status st = check_attn(&d, mode, sparse_k, flags, &s);
+    if (st) {
+      const std::string why = g_last_error;
+      return fail(st, "segment %d: %s", i, why.c_str());
+    }
+    total += s.n_tokens;
+    if (total > 0x7fffffffLL)
+      return fail(OSP_ERR_SHAPE, "packed sequence of more than 2^31-1 tokens");
+  }
+  osp_status st = check_fwd_pointers(q, k, v, o, lse, sm_scale);
+  if (st) return st;
+  // the strides of the packed tensors: contiguous defaults use the total length
+  osp_attn3d_desc pd = *desc;
+  pd.n_text = 0;
+  pd.grid_t = 1;
+  pd.grid_h = 1;
+  pd.grid_w = int32_t(total);
+  Shape ps;
+  st = check_desc(&pd, true, &ps);
+  if (st) return st;
+  int64_t start = 0;
+  for (int32_t i = 0; i < n_segments; ++i) {
+    osp_attn3d_desc d = *desc;
+    d.n_text = segments[i].n_text;
+    d.grid_t = segments[i].grid_t;
+    d.grid_h = segments[i].grid_h;
+    d.grid_w = segments[i].grid_w;
+    Shape s;
+    check_desc(&d, true, &s);
+    s.sb = ps.sb; s.sn = ps.sn; s.sh = ps.sh;
+    s.osb = ps.osb; s.osn = ps.osn; s.osh = ps.osh;
+    osp::AttnArgs a;
+    fill_fwd_args(&d, s, mode, sparse_k, sm_scale,
+                  static_cast<const uint16_t*>(q) + start * s.sn,
+                  static_cast<const uint16_t*>(k) + start * s.sn,
+                  static_cast<const uint16_t*>(v) + start * s.sn,
+                  static_cast<uint16_t*>(o) + start * s.osn, lse ? lse + start : nullptr, total,
+                  &a);
+    hipError_t e = osp::launch_attn3d(a, desc->head_dim, (flags & OSP_FUSE_ROPE_Q) ? 1 : 0,
+                                      (flags & OSP_FUSE_ROPE_K) ? 1 : 0,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_error(e, "attn3d_packed_fwd launch");
+    start += s.n_tokens;
+  }
   return ok();
 }
 

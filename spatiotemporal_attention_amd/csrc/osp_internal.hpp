@@ -16,7 +16,8 @@ struct AttnArgs {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
-  float* lse;                   // nullable, [B, H, N]
+  float* lse;                   // nullable, [B, H, lse_ld] (token i of (b, h) at (b*H + h)*lse_ld + i)
+  int64_t lse_ld;               // n_tokens, or the packed sequence's length
   int64_t sb, sn, sh;           // q/k/v strides (elements)
   int64_t osb, osn, osh;        // o strides (elements)
   int32_t batch, heads, n_tokens, seq_len, groups, mode;

@@ -489,6 +489,10 @@ def pin_packed_block_diagonal(o):
     gr, _ = o.attn3d_packed(q[:, perm], k[:, perm], v[:, perm], segments=rev, rope_split=split)
     assert np.allclose(gr, got[:, perm], rtol=0, atol=1e-12)
     assert rlay[0][1] == lay[-1][1] - lay[-1][0]
+    rows = np.array([0, 2, 10, 23, 24, 40, n - 1])
+    gs, ls = o.attn3d_packed(q, k, v, segments=segs, rope_split=split, rows=rows)
+    assert np.allclose(gs, got[:, rows], rtol=0, atol=1e-12)
+    assert np.allclose(ls, lse[:, :, rows], rtol=0, atol=1e-12)
 
 
 ALL_PINS = [

@@ -186,6 +186,36 @@ def test_bwd_null_alignment_and_workspace_errors_before_launch():
     assert lib.osp_rope3d_inv(ctypes.byref(d), f, ctypes.c_void_p(4100), None) == PARAM
 
 
+def test_packed_checks_every_segment_before_launch():
+    lib = osp.lib()
+    d = _desc()
+    f = ctypes.c_void_p(4096)
+
+    def call(segs, mode=0, k=1, flags=1, q=f, desc=ctypes.byref(d)):
+        arr = (osp.OspSegment * max(len(segs), 1))()
+        for i, (nt, g) in enumerate(segs):
+            arr[i].n_text = nt
+            arr[i].grid_t, arr[i].grid_h, arr[i].grid_w = g
+        return lib.osp_attn3d_packed_fwd(desc, arr, len(segs), mode, k, 0.0, flags, q, f, f, f,
+                                         None, None)
+    good = [(3, (2, 3, 4)), (0, (1, 4, 5))]
+    assert call(good, desc=None) == NULL
+    assert lib.osp_attn3d_packed_fwd(ctypes.byref(d), None, 1, 0, 1, 0.0, 1, f, f, f, f, None,
+                                     None) == NULL
+    assert call([]) == PARAM
+    assert call(good + [(0, (0, 4, 4))]) == PARAM
+    assert b"segment 2" in lib.osp_last_error()
+    assert call(good, mode=1, k=2) == UNSUP                  # Skiparse with text tokens
+    assert call([(0, (2, 4, 4)), (0, (1, 3, 5))], mode=1, k=2) == SHAPE   # 15 % 2
+    assert b"segment 1" in lib.osp_last_error()
+    assert call([(0, (2, 4, 4)), (0, (1, 3, 5))], mode=3, k=3) == SHAPE   # 32 % 3
+    assert call(good, q=None) == NULL
+    assert call(good, q=ctypes.c_void_p(4098)) == PARAM
+    assert call([(0, (2000, 2000, 300)), (0, (2000, 2000, 300))]) == SHAPE  # N > 2^31 - 1
+    d80 = _desc(head_dim=80, rope_split=(16, 32, 32))
+    assert call(good, desc=ctypes.byref(d80)) == UNSUP
+
+
 def test_success_clears_last_error():
     lib = osp.lib()
     osp.osp_attn3d_check(_desc())

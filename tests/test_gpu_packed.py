@@ -1,0 +1,106 @@
+"""GPU parity of packed sequences (several videos in one sequence,
+block-diagonal attention, RoPE from 0 on each video's own grid) against
+the fp64 oracle, through the C ABI: small packs element by element (both
+the short-subsequence and the flash kernel, Skiparse inside the segments,
+fused and unfused K rotation), each segment against a plain forward call on
+its slice, and the CogVideoX frame pack on sampled rows.  Needs an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import spatiotemporal_attention_amd as osp
+import workloads
+from parity_util import LSE_ABS, MAX_ABS, REL_L2, assert_parity, note, qkv_for, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    osp.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _packed_case(seed, segments, *, heads, head_dim, split, mode="full", sparse_k=1, batch=1,
+                 fuse_rope=True, tag=""):
+    n = sum(nt + int(np.prod(g)) for nt, g in segments)
+    shape = (batch, n, heads, head_dim)
+    note(f"packed {tag} seed={seed} shape={shape} segments={segments} mode={mode} k={sparse_k}")
+    cpu, (q, k, v) = qkv_for(seed, shape)
+    o, lse = osp.osp_attn3d_packed_fwd(q, k, v, segments=segments, mode=mode, sparse_k=sparse_k,
+                                       rope_split=split, fuse_rope=fuse_rope, return_lse=True)
+    torch.cuda.synchronize()
+    want_o, want_l = oracle.attn3d_packed(*(workloads.to_f64(t) for t in cpu), segments=segments,
+                                          mode=mode, sparse_k=sparse_k, rope_split=split)
+    assert_parity(to_np(o), want_o, f"O packed {tag}", MAX_ABS, REL_L2)
+    got_l = to_np(lse)
+    assert np.abs(got_l - want_l).max() <= LSE_ABS, np.abs(got_l - want_l).max()
+    return (q, k, v), o, lse
+
+
+SMALL = [(3, (2, 3, 4)), (0, (1, 4, 5)), (5, (3, 2, 2)), (0, (2, 8, 10))]
+
+
+@pytest.mark.parametrize("d,split", [(64, (16, 24, 24)), (96, (32, 32, 32)),
+                                     (128, (32, 48, 48))])
+def test_packed_small(d, split):
+    # three segments of <= 64 tokens (short kernel) and one of 160 (flash kernel)
+    _packed_case(30, SMALL, heads=2, head_dim=d, split=split, batch=2, tag=f"d{d}")
+
+
+@pytest.mark.parametrize("mode,k", [("skiparse_single", 4), ("skiparse_group", 2), ("block", 2)])
+def test_packed_skiparse_per_segment(mode, k):
+    segs = [(0, (4, 4, 4)), (0, (2, 8, 8)), (0, (1, 6, 8)), (0, (2, 10, 12))]
+    _packed_case(31, segs, heads=3, head_dim=64, split=(16, 24, 24), mode=mode, sparse_k=k,
+                 tag=f"{mode}-{k}")
+
+
+def test_packed_segments_equal_plain_calls_and_fused_k():
+    segs = [(7, (3, 6, 8)), (0, (1, 5, 5)), (11, (5, 4, 6))]
+    split = (32, 32, 32)
+    (q, k, v), o, lse = _packed_case(32, segs, heads=3, head_dim=96, split=split, tag="vs-plain")
+    start = 0
+    for nt, g in segs:
+        end = start + nt + int(np.prod(g))
+        os_, ls_ = osp.osp_attn3d_fwd(q[:, start:end], k[:, start:end], v[:, start:end], grid=g,
+                                      n_text=nt, rope_split=split, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(os_, o[:, start:end]) and torch.equal(ls_, lse[:, :, start:end])
+        start = end
+    # K rotated per segment by osp_rope3d, Q in the loader: same bits
+    k_rot = torch.empty_like(k)
+    start = 0
+    for nt, g in segs:
+        end = start + nt + int(np.prod(g))
+        osp.osp_rope3d(k[:, start:end], grid=g, n_text=nt, rope_split=split,
+                       out=k_rot[:, start:end])
+        start = end
+    o2, l2 = osp.osp_attn3d_packed_fwd(q, k_rot, v, segments=segs, rope_split=split,
+                                       fuse_rope="q", return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(l2, lse)
+
+
+def test_cogvideox_frame_pack_sampled_rows():
+    pk = workloads.COGVIDEOX_PACK
+    wl = workloads.WORKLOADS[pk["base"]]
+    segs = [(pk["n_text"], osp.osp_latent_grid(*clip, wl.c_t, wl.c_s, wl.p_t, wl.p_s))
+            for clip in pk["clips"]]
+    n = sum(nt + int(np.prod(g)) for nt, g in segs)
+    shape = (1, n, wl.heads, wl.head_dim)
+    note(f"cogvideox frame pack segments={segs} n={n}")
+    cpu, (q, k, v) = qkv_for(pk["seed"], shape)
+    o, lse = osp.osp_attn3d_packed_fwd(q, k, v, segments=segs, rope_split=wl.rope_split,
+                                       return_lse=True)
+    torch.cuda.synchronize()
+    rows = workloads.sample_rows(pk["seed"], n, pk["sample_rows"])
+    hs = slice(0, 8)
+    want_o, want_l = oracle.attn3d_packed(*(workloads.to_f64(t[:, :, hs]) for t in cpu),
+                                          segments=segs, rope_split=wl.rope_split, rows=rows)
+    assert_parity(to_np(o[:, rows][:, :, hs]), want_o, "O frame pack rows")
+    got_l = to_np(lse[:, hs][:, :, rows])
+    assert np.abs(got_l - want_l).max() <= LSE_ABS
+    assert not torch.isnan(o).any()

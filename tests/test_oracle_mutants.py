@@ -48,8 +48,8 @@ MUTANTS = {
     "rope_transpose_sign": ("out[:, n_text:, :, c0 + 0:c0 + d_a:2] = xa * cos + xb * sin",
                             "out[:, n_text:, :, c0 + 0:c0 + d_a:2] = xa * cos - xb * sin"),
     "perm_inverse_wrong": ("inv[perm] = np.arange(n, dtype=np.int64)", "inv[:] = perm"),
-    "packed_global_positions": ("pos_offset=pos_offset, rope=rope)\n        o[:, start:end] = os_",
-                                "pos_offset=(pos_offset[0] + start, pos_offset[1], pos_offset[2]), rope=rope)\n        o[:, start:end] = os_"),
+    "packed_global_positions": ("pos_offset=pos_offset, rope=rope,\n                          rows=out_rows[sel] - start)",
+                                "pos_offset=(pos_offset[0] + start, pos_offset[1], pos_offset[2]), rope=rope,\n                          rows=out_rows[sel] - start)"),
     "packed_attends_across": ("        os_, ls_ = attn3d(q[:, start:end], k[:, start:end], v[:, start:end], grid=grid,",
                               "        os_, ls_ = attn3d(q[:, start:end], k[:, start:end], v[:, start:end] + v[:, :1].mean(), grid=grid,"),
     "packed_segment_off_by_one": ("        end = start + int(n_text) + int(np.prod(grid))",

@@ -22,6 +22,10 @@ Workloads (clip sizes from the pages; latent-grid arithmetic is done elsewhere):
   8x8x8 VAE and 1x2x2 patchify, full and k=4; the pages give no head shape
   for that model, so 24 heads of D=128 (split 32/48/48) are taken, which
   also exercises the third head size.  Checked on 256 seeded query rows.
+* ``COGVIDEOX_PACK`` -- a Multi-Resolution Frame Pack (CogVideoX section 3.1):
+  clips of 49, 25 and 1 frames at 480x720 and one of 33 frames at 256x384
+  (Table 8's smallest resolution), each with its 226 text tokens, in one
+  sequence at CogVideoX's 48 heads of D=64.
 """
 from __future__ import annotations
 
@@ -120,3 +124,8 @@ def sample_rows(seed: int, n_tokens: int, count: int) -> np.ndarray:
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of a bf16 tensor to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+# Frame pack: raw clips (frames, height, width) with 226 text tokens each,
+# through the cogvideox workload's VAE and patchify factors
+COGVIDEOX_PACK = {"clips": ((49, 480, 720), (25, 480, 720), (1, 480, 720), (33, 256, 384)),
+                  "n_text": 226, "base": "cogvideox", "seed": 6, "sample_rows": 192}
