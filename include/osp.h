@@ -151,6 +151,15 @@ osp_status osp_attn3d_packed_fwd(const osp_attn3d_desc* desc,
                                  const void* v, void* o, float* lse,
                                  void* stream);
 
+/* osp_rope3d over a packed sequence (segments as in osp_attn3d_packed_fwd):
+   each segment's rows rotated on its own grid, from position 0.  One launch
+   per segment; y == x works in place.  Rotating K this way and passing
+   OSP_FUSE_ROPE_Q alone to osp_attn3d_packed_fwd gives the same result as
+   OSP_FUSE_ROPE, usually faster. */
+osp_status osp_rope3d_packed(const osp_attn3d_desc* desc,
+                             const osp_segment* segments, int32_t n_segments,
+                             const void* x, void* y, void* stream);
+
 /* Transpose (= inverse) of osp_rope3d: y = rotate(x) by the negative
    angle for every video [b, n, h] row, text rows copied, same strides,
    layout and rounding as osp_rope3d.  It maps the gradient with respect to

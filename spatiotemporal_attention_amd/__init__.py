@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
             "osp_attn3d_fwd": (I32, [D, I32, I32, F32, I32, P, P, P, P, P, P]),
             "osp_attn3d_packed_fwd": (I32, [D, ctypes.POINTER(OspSegment), I32, I32, I32, F32,
                                             I32, P, P, P, P, P, P]),
+            "osp_rope3d_packed": (I32, [D, ctypes.POINTER(OspSegment), I32, P, P, P]),
             "osp_attn3d_bwd_workspace": (I32, [D, I32, I32, ctypes.POINTER(I64)]),
             "osp_attn3d_bwd": (I32, [D, I32, I32, F32, P, P, P, P, P, P, P, P, P, P, I64, P]),
             "osp_skiparse_index": (I32, [I32, I32, I64, P, P, I32, P]),
@@ -92,7 +93,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("osp_abi_version", "osp_status_string", "osp_last_error", "osp_latent_grid",
             "osp_attn3d_check", "osp_rope3d", "osp_rope3d_inv", "osp_attn3d_fwd",
-            "osp_attn3d_packed_fwd",
+            "osp_attn3d_packed_fwd", "osp_rope3d_packed",
             "osp_attn3d_bwd_workspace", "osp_attn3d_bwd", "osp_skiparse_index")
 
 
@@ -231,6 +232,36 @@ def _flags(fuse_rope) -> int:
     return {"q": OSP_FUSE_ROPE_Q, "k": OSP_FUSE_ROPE_K, "qk": OSP_FUSE_ROPE}[fuse_rope]
 
 
+def _segments(segments, n):
+    segs = (OspSegment * len(segments))()
+    total = 0
+    for i, (n_text, grid) in enumerate(segments):
+        segs[i].n_text = int(n_text)
+        segs[i].grid_t, segs[i].grid_h, segs[i].grid_w = (int(x) for x in grid)
+        total += int(n_text) + int(grid[0]) * int(grid[1]) * int(grid[2])
+    if total != n:
+        raise ValueError(f"segments cover {total} tokens, the tensors hold {n}")
+    return segs
+
+
+def osp_rope3d_packed(x: torch.Tensor, *, segments, rope_split, theta: float = 1e4,
+                      pos_offset=(0, 0, 0), out: torch.Tensor | None = None) -> torch.Tensor:
+    """3D RoPE of a packed [B, N, H, D] sequence, each segment on its own grid."""
+    if out is None:
+        out = torch.empty_like(x)
+    b, n, h, d = x.shape
+    if tuple(out.shape) != tuple(x.shape):
+        raise ValueError("out must have the shape of x")
+    segs = _segments(segments, n)
+    desc = make_desc(batch=b, n_text=0, grid=(1, 1, n), heads=h, head_dim=d,
+                     rope_split=rope_split, theta=theta, pos_offset=pos_offset,
+                     strides=_bnhd(x, "x"), ostrides=_bnhd(out, "out"))
+    _check(lib().osp_rope3d_packed(ctypes.byref(desc), segs, len(segments),
+                                   ctypes.c_void_p(x.data_ptr()),
+                                   ctypes.c_void_p(out.data_ptr()), _stream(x)))
+    return out
+
+
 def osp_attn3d_packed_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, segments,
                           mode="full", sparse_k: int = 1, rope_split, theta: float = 1e4,
                           sm_scale: float | None = None, fuse_rope=True, pos_offset=(0, 0, 0),
@@ -249,14 +280,7 @@ def osp_attn3d_packed_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, 
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (b, h, n)
                             or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
-    segs = (OspSegment * len(segments))()
-    total = 0
-    for i, (n_text, grid) in enumerate(segments):
-        segs[i].n_text = int(n_text)
-        segs[i].grid_t, segs[i].grid_h, segs[i].grid_w = (int(x) for x in grid)
-        total += int(n_text) + int(grid[0]) * int(grid[1]) * int(grid[2])
-    if total != n:
-        raise ValueError(f"segments cover {total} tokens, the tensors hold {n}")
+    segs = _segments(segments, n)
     desc = make_desc(batch=b, n_text=0, grid=(1, 1, n), heads=h, head_dim=d,
                      rope_split=rope_split, theta=theta, pos_offset=pos_offset, strides=st,
                      ostrides=_bnhd(out, "out"))

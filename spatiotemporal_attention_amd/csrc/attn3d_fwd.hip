@@ -117,7 +117,8 @@ __device__ __forceinline__ void m_phase_order() {
 #define OSP_LEAD_RANK (wave % (NW / 2))
 #endif
 
-template <int D, int QB, int BN, int NW, int OCC, bool ROPE_Q, bool ROPE_K, bool FIXED_ROWS>
+template <int D, int QB, int BN, int NW, int OCC, bool ROPE_Q, bool ROPE_K, bool FIXED_ROWS,
+          bool PACKED>
 __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs a) {
   using C = AttnCfg<D, QB, BN, NW>;
   constexpr int NKB = BN / 32;        // 32-key blocks per tile
@@ -150,27 +151,55 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   const int l32 = lane & 31;
 
   // ---- which tile: consecutive tiles of one (b, h, j) stay on one XCD ----
+  // (workgroup x runs on XCD x mod 8; XCD c takes the c-th eighth of the tiles)
   const uint32_t total = uint32_t(a.total_tiles);
   const uint32_t t8 = total & ~7u;
   const uint32_t x = blockIdx.x;
   uint32_t u = (x < t8) ? (x & 7u) * (t8 >> 3) + (x >> 3) : x;
-  const uint32_t qt = u % uint32_t(a.q_tiles);
-  u /= uint32_t(a.q_tiles);
+
+  // kernel arguments used below, as locals (keeps the argument block out of
+  // private memory)
+  RopeGeom rg = rope_scalars(a.rope);
+  int32_t seq_len = a.seq_len, q_tiles = a.q_tiles;
+  int64_t tok0 = 0;   // first token of the tile's sequence (packed launches)
+  if constexpr (PACKED) {
+    // the segment of workgroup x; every index is a constant (no dynamic
+    // indexing into the argument block).  Each segment starts at a multiple
+    // of 8 workgroups and is spread over the 8 XCDs on its own, as a whole
+    // launch is above, so that segments of different cost do not load the
+    // XCDs unevenly; its padding workgroups exit at once.
+    PackSeg ps = a.pack[0];
+#pragma unroll
+    for (int sg = 1; sg < kMaxPackSegs; ++sg)
+      if (sg < a.n_pack && x >= uint32_t(a.pack[sg].tile0)) ps = a.pack[sg];
+    const uint32_t xs = x - uint32_t(ps.tile0);
+    const uint32_t n8 = (uint32_t(ps.tiles) + 7u) >> 3;
+    u = (xs & 7u) * n8 + (xs >> 3);
+    if (u >= uint32_t(ps.tiles)) return;   // before any barrier
+    seq_len = ps.seq_len;
+    q_tiles = ps.q_tiles;
+    tok0 = ps.start;
+    rg.n_text = ps.n_text;
+    rg.off1 = ps.off1;
+    rg.off2 = ps.off2;
+    rg.tab_entries = ps.tab_entries;
+    rg.div_hw = ps.div_hw;
+    rg.div_w = ps.div_w;
+  }
+  const uint32_t qt = u % uint32_t(q_tiles);
+  u /= uint32_t(q_tiles);
   const uint32_t j = u % uint32_t(a.groups);
   u /= uint32_t(a.groups);
   const uint32_t h = u % uint32_t(a.heads);
   const uint32_t b = u / uint32_t(a.heads);
 
-  // kernel arguments used below, as locals (keeps the argument block out of
-  // private memory)
   const int mode = a.mode;
   const FastDiv divk = a.divk;
-  const RopeGeom rg = rope_scalars(a.rope);
   const int64_t a_sn = a.sn;
 
-  const int L = a.seq_len;
+  const int L = seq_len;
   const int nkt = (L + BN - 1) / BN;
-  const int64_t in_off = int64_t(b) * a.sb + int64_t(h) * a.sh;
+  const int64_t in_off = int64_t(b) * a.sb + int64_t(h) * a.sh + tok0 * a_sn;
   const uint16_t* __restrict__ qg = a.q + in_off;
   const uint16_t* __restrict__ kg = a.k + in_off;
   const uint16_t* __restrict__ vg = a.v + in_off;
@@ -591,7 +620,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   __builtin_amdgcn_s_waitcnt(0x0070);
 
   // ---- epilogue: O = O^T / l, stored at the original token row ----
-  uint16_t* og = a.o + int64_t(b) * a.osb + int64_t(h) * a.osh;
+  uint16_t* og = a.o + int64_t(b) * a.osb + int64_t(h) * a.osh + tok0 * a.osn;
+  float* const lse_out = a.lse ? a.lse + tok0 : nullptr;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = sum_pair32(lsum[qb]);
@@ -608,8 +638,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
           const uint32_t w1 = pack_bf16(o[qb][db][4 * r4 + 2] * inv, o[qb][db][4 * r4 + 3] * inv);
           *reinterpret_cast<uint2*>(p + 32 * db + 8 * r4 + 4 * g) = make_uint2(w0, w1);
         }
-      if (a.lse && g == 0)
-        a.lse[(int64_t(b) * a.heads + h) * a.lse_ld + i] = (mref[qb] + __log2f(lt)) * kLn2;
+      if (lse_out && g == 0)
+        lse_out[(int64_t(b) * a.heads + h) * a.lse_ld + i] = (mref[qb] + __log2f(lt)) * kLn2;
     }
   }
 }
@@ -624,60 +654,83 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
 #define OSP_D96_TILE 1, 64, 8, 2
 #endif
 #ifndef OSP_D128_TILE
-#define OSP_D128_TILE 1, 32, 8, 2
+#define OSP_D128_TILE 1, 64, 8, 2
+#endif
+// D=128 with K rotated in the loader: 64-key tiles spill, 32 do not
+#ifndef OSP_D128_ROPE_K_TILE
+#define OSP_D128_ROPE_K_TILE 1, 32, 8, 2
 #endif
 template <int QB_, int BN_, int NW_, int OCC_> struct TileShape {
   static constexpr int QB = QB_, BN = BN_, NW = NW_, OCC = OCC_;
 };
-template <int D> struct TileCfg;
-template <> struct TileCfg<64> : TileShape<OSP_D64_TILE> {};
-template <> struct TileCfg<96> : TileShape<OSP_D96_TILE> {};
-template <> struct TileCfg<128> : TileShape<OSP_D128_TILE> {};
+template <int D, bool RK> struct TileCfg;
+template <bool RK> struct TileCfg<64, RK> : TileShape<OSP_D64_TILE> {};
+template <bool RK> struct TileCfg<96, RK> : TileShape<OSP_D96_TILE> {};
+template <> struct TileCfg<128, false> : TileShape<OSP_D128_TILE> {};
+template <> struct TileCfg<128, true> : TileShape<OSP_D128_ROPE_K_TILE> {};
 
+template <int D> constexpr int max_keys_per_tile() {
+  return TileCfg<D, false>::BN > TileCfg<D, true>::BN ? TileCfg<D, false>::BN : TileCfg<D, true>::BN;
+}
 int attn_keys_per_tile(int head_dim) {
   switch (head_dim) {
-    case 64: return TileCfg<64>::BN;
-    case 96: return TileCfg<96>::BN;
-    case 128: return TileCfg<128>::BN;
+    case 64: return max_keys_per_tile<64>();
+    case 96: return max_keys_per_tile<96>();
+    case 128: return max_keys_per_tile<128>();
     default: return 0;
   }
 }
 
+// (rows per workgroup are the same with and without K rotation)
 int attn_rows_per_block(int head_dim) {
   switch (head_dim) {
-    case 64: return TileCfg<64>::NW * 32 * TileCfg<64>::QB;
-    case 96: return TileCfg<96>::NW * 32 * TileCfg<96>::QB;
-    case 128: return TileCfg<128>::NW * 32 * TileCfg<128>::QB;
+    case 64: return TileCfg<64, false>::NW * 32 * TileCfg<64, false>::QB;
+    case 96: return TileCfg<96, false>::NW * 32 * TileCfg<96, false>::QB;
+    case 128: return TileCfg<128, false>::NW * 32 * TileCfg<128, false>::QB;
     default: return 0;
   }
 }
+static_assert(TileCfg<128, false>::NW * TileCfg<128, false>::QB ==
+              TileCfg<128, true>::NW * TileCfg<128, true>::QB, "rows per workgroup");
 
-template <int D, bool FIXED>
-static hipError_t launch_df(const AttnArgs& a, int rope_q, int rope_k, hipStream_t s) {
-  using T = TileCfg<D>;
+template <int D, bool RQ, bool RK, bool PK>
+static hipError_t launch_drk(const AttnArgs& a, hipStream_t s) {
+  using T = TileCfg<D, RK>;
   dim3 grid(a.total_tiles), block(T::NW * 64);
-#define OSP_LAUNCH(RQ, RK) \
-  hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, RQ, RK, FIXED>), grid, block, 0, s, a)
-  if (rope_q && rope_k) OSP_LAUNCH(true, true);
-  else if (rope_q) OSP_LAUNCH(true, false);
-  else if (rope_k) OSP_LAUNCH(false, true);
-  else OSP_LAUNCH(false, false);
-#undef OSP_LAUNCH
+  const bool fixed = a.mode != MODE_GROUP || T::BN % int(a.divk.d) == 0;
+  if (fixed)
+    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, RQ, RK, true, PK>),
+                       grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, RQ, RK, false, PK>),
+                       grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool PK>
 static hipError_t launch_d(const AttnArgs& a, int rope_q, int rope_k, hipStream_t s) {
-  const bool fixed = a.mode != MODE_GROUP || TileCfg<D>::BN % int(a.divk.d) == 0;
-  return fixed ? launch_df<D, true>(a, rope_q, rope_k, s) : launch_df<D, false>(a, rope_q, rope_k, s);
+  if (rope_q && rope_k) return launch_drk<D, true, true, PK>(a, s);
+  if (rope_q) return launch_drk<D, true, false, PK>(a, s);
+  if (rope_k) return launch_drk<D, false, true, PK>(a, s);
+  return launch_drk<D, false, false, PK>(a, s);
 }
 
 hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_q, int rope_k, hipStream_t s) {
   if (a.seq_len <= kShortRows) return launch_attn3d_short(a, head_dim, rope_q, rope_k, s);
   switch (head_dim) {
-    case 64: return launch_d<64>(a, rope_q, rope_k, s);
-    case 96: return launch_d<96>(a, rope_q, rope_k, s);
-    case 128: return launch_d<128>(a, rope_q, rope_k, s);
+    case 64: return launch_d<64, false>(a, rope_q, rope_k, s);
+    case 96: return launch_d<96, false>(a, rope_q, rope_k, s);
+    case 128: return launch_d<128, false>(a, rope_q, rope_k, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attn3d_packed(const AttnArgs& a, int head_dim, int rope_q, int rope_k,
+                                hipStream_t s) {
+  switch (head_dim) {
+    case 64: return launch_d<64, true>(a, rope_q, rope_k, s);
+    case 96: return launch_d<96, true>(a, rope_q, rope_k, s);
+    case 128: return launch_d<128, true>(a, rope_q, rope_k, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <string>
+#include <vector>
 
 #include "../../include/osp.h"
 #include "osp_internal.hpp"
@@ -236,6 +237,7 @@ void fill_fwd_args(const osp_attn3d_desc* desc, const Shape& s, int32_t mode, in
   a.q_tiles = (a.seq_len + bm - 1) / bm;
   a.total_tiles = a.batch * a.heads * groups * a.q_tiles;
   fill_rope(desc, &a.rope);
+  a.n_pack = 0;
 }
 
 // bytes of one of the two fp32 [B, H, N] workspace arrays, rounded up to 256
@@ -324,6 +326,67 @@ osp_status osp_rope3d_inv(const osp_attn3d_desc* desc, const void* x, void* y, v
   return rope3d_call(desc, x, y, stream, 1);
 }
 
+osp_status osp_rope3d_packed(const osp_attn3d_desc* desc, const osp_segment* segments,
+                             int32_t n_segments, const void* x, void* y, void* stream) {
+  if (!desc) return fail(OSP_ERR_NULL, "desc is NULL");
+  if (!segments) return fail(OSP_ERR_NULL, "segments is NULL");
+  if (n_segments < 1) return fail(OSP_ERR_PARAM, "n_segments (%d) must be >= 1", n_segments);
+  int64_t total = 0;
+  for (int32_t i = 0; i < n_segments; ++i) {
+    osp_attn3d_desc d = *desc;
+    d.n_text = segments[i].n_text;
+    d.grid_t = segments[i].grid_t;
+    d.grid_h = segments[i].grid_h;
+    d.grid_w = segments[i].grid_w;
+    Shape s;
+    osp_status st = check_desc(&d, false, &s);
+    if (st) {
+      const std::string why = g_last_error;
+      return fail(st, "segment %d: %s", i, why.c_str());
+    }
+    total += s.n_tokens;
+    if (total > 0x7fffffffLL)
+      return fail(OSP_ERR_SHAPE, "packed sequence of more than 2^31-1 tokens");
+  }
+  if (!x || !y) return fail(OSP_ERR_NULL, "x and y must be non-NULL");
+  if (!aligned16(x) || !aligned16(y)) return fail(OSP_ERR_PARAM, "x and y must be 16-byte aligned");
+  osp_attn3d_desc pd = *desc;
+  pd.n_text = 0;
+  pd.grid_t = 1;
+  pd.grid_h = 1;
+  pd.grid_w = int32_t(total);
+  Shape ps;
+  osp_status st = check_desc(&pd, false, &ps);
+  if (st) return st;
+  if (uint64_t(desc->batch) * uint64_t(total) * uint64_t(desc->heads) * uint64_t(desc->head_dim / 8) >
+      0xffffffffull - 2048ull * 256ull)
+    return fail(OSP_ERR_SHAPE, "tensor too large for one rope3d call");
+  int64_t start = 0;
+  for (int32_t i = 0; i < n_segments; ++i) {
+    osp_attn3d_desc d = *desc;
+    d.n_text = segments[i].n_text;
+    d.grid_t = segments[i].grid_t;
+    d.grid_h = segments[i].grid_h;
+    d.grid_w = segments[i].grid_w;
+    const int64_t n = int64_t(d.n_text) + int64_t(d.grid_t) * d.grid_h * d.grid_w;
+    osp::RopeArgs a;
+    a.x = static_cast<const uint16_t*>(x) + start * ps.sn;
+    a.y = static_cast<uint16_t*>(y) + start * ps.osn;
+    a.sb = ps.sb; a.sn = ps.sn; a.sh = ps.sh;
+    a.osb = ps.osb; a.osn = ps.osn; a.osh = ps.osh;
+    a.batch = desc->batch;
+    a.n_tokens = int32_t(n);
+    a.heads = desc->heads;
+    a.head_dim = desc->head_dim;
+    a.inverse = 0;
+    fill_rope(&d, &a.rope);
+    hipError_t e = osp::launch_rope3d(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_error(e, "rope3d launch");
+    start += n;
+  }
+  return ok();
+}
+
 osp_status osp_attn3d_fwd(const osp_attn3d_desc* desc, int32_t mode, int32_t sparse_k,
                           float sm_scale, int32_t flags, const void* q, const void* k,
                           const void* v, void* o, float* lse, void* stream) {
@@ -350,7 +413,7 @@ osp_status osp_attn3d_packed_fwd(const osp_attn3d_desc* desc, const osp_segment*
   if (!segments) return fail(OSP_ERR_NULL, "segments is NULL");
   if (n_segments < 1) return fail(OSP_ERR_PARAM, "n_segments (%d) must be >= 1", n_segments);
   // every segment is checked before anything is enqueued
-  int64_t total = 0;
+  int64_t total = 0, tiles = 0;
   for (int32_t i = 0; i < n_segments; ++i) {
     osp_attn3d_desc d = *desc;
     d.n_text = segments[i].n_text;
@@ -366,6 +429,11 @@ osp_status osp_attn3d_packed_fwd(const osp_attn3d_desc* desc, const osp_segment*
     total += s.n_tokens;
     if (total > 0x7fffffffLL)
       return fail(OSP_ERR_SHAPE, "packed sequence of more than 2^31-1 tokens");
+    const int64_t bm = osp::attn_rows_per_block(desc->head_dim);
+    const int64_t groups = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
+    tiles += (int64_t(desc->batch) * desc->heads * groups * ((s.n_tokens / groups + bm - 1) / bm) +
+              7) / 8 * 8;
+    if (tiles > 0x7fffffffLL) return fail(OSP_ERR_SHAPE, "too many tiles in the packed sequence");
   }
   osp_status st = check_fwd_pointers(q, k, v, o, lse, sm_scale);
   if (st) return st;
@@ -378,6 +446,19 @@ osp_status osp_attn3d_packed_fwd(const osp_attn3d_desc* desc, const osp_segment*
   Shape ps;
   st = check_desc(&pd, true, &ps);
   if (st) return st;
+  // Segments whose subsequences are short go to the short-subsequence
+  // kernel one launch each; the others share flash-kernel launches of up
+  // to kMaxPackSegs segments, whose workgroups find their segment in a
+  // table (so small segments do not leave the chip idle on their own),
+  // longest first so that the shorter ones fill the tail.
+  const int rq = (flags & OSP_FUSE_ROPE_Q) ? 1 : 0, rk = (flags & OSP_FUSE_ROPE_K) ? 1 : 0;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int32_t groups = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
+  struct Flash {
+    osp::AttnArgs a;
+    int64_t start;
+  };
+  std::vector<Flash> flash;
   int64_t start = 0;
   for (int32_t i = 0; i < n_segments; ++i) {
     osp_attn3d_desc d = *desc;
@@ -389,18 +470,49 @@ osp_status osp_attn3d_packed_fwd(const osp_attn3d_desc* desc, const osp_segment*
     check_desc(&d, true, &s);
     s.sb = ps.sb; s.sn = ps.sn; s.sh = ps.sh;
     s.osb = ps.osb; s.osn = ps.osn; s.osh = ps.osh;
-    osp::AttnArgs a;
-    fill_fwd_args(&d, s, mode, sparse_k, sm_scale,
-                  static_cast<const uint16_t*>(q) + start * s.sn,
-                  static_cast<const uint16_t*>(k) + start * s.sn,
-                  static_cast<const uint16_t*>(v) + start * s.sn,
-                  static_cast<uint16_t*>(o) + start * s.osn, lse ? lse + start : nullptr, total,
-                  &a);
-    hipError_t e = osp::launch_attn3d(a, desc->head_dim, (flags & OSP_FUSE_ROPE_Q) ? 1 : 0,
-                                      (flags & OSP_FUSE_ROPE_K) ? 1 : 0,
-                                      static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return device_error(e, "attn3d_packed_fwd launch");
+    const int64_t seg_start = start;
     start += s.n_tokens;
+    if (s.n_tokens / groups <= osp::kShortRows) {
+      osp::AttnArgs a;
+      fill_fwd_args(&d, s, mode, sparse_k, sm_scale,
+                    static_cast<const uint16_t*>(q) + seg_start * s.sn,
+                    static_cast<const uint16_t*>(k) + seg_start * s.sn,
+                    static_cast<const uint16_t*>(v) + seg_start * s.sn,
+                    static_cast<uint16_t*>(o) + seg_start * s.osn,
+                    lse ? lse + seg_start : nullptr, total, &a);
+      hipError_t e = osp::launch_attn3d_short(a, desc->head_dim, rq, rk, hs);
+      if (e != hipSuccess) return device_error(e, "attn3d_packed_fwd launch");
+      continue;
+    }
+    Flash f;
+    fill_fwd_args(&d, s, mode, sparse_k, sm_scale, q, k, v, o, lse, total, &f.a);
+    f.start = seg_start;
+    flash.push_back(f);
+  }
+  std::stable_sort(flash.begin(), flash.end(),
+                   [](const Flash& x, const Flash& y) { return x.a.seq_len > y.a.seq_len; });
+  for (size_t i0 = 0; i0 < flash.size(); i0 += osp::kMaxPackSegs) {
+    osp::AttnArgs pa = flash[i0].a;
+    pa.n_pack = 0;
+    pa.total_tiles = 0;
+    for (size_t i = i0; i < flash.size() && i < i0 + osp::kMaxPackSegs; ++i) {
+      const osp::AttnArgs& a = flash[i].a;
+      osp::PackSeg& sg = pa.pack[pa.n_pack++];
+      sg.tile0 = pa.total_tiles;
+      sg.tiles = a.total_tiles;
+      sg.start = int32_t(flash[i].start);
+      sg.seq_len = a.seq_len;
+      sg.q_tiles = a.q_tiles;
+      sg.n_text = a.rope.n_text;
+      sg.off1 = a.rope.off1;
+      sg.off2 = a.rope.off2;
+      sg.tab_entries = a.rope.tab_entries;
+      sg.div_hw = a.rope.div_hw;
+      sg.div_w = a.rope.div_w;
+      pa.total_tiles += (a.total_tiles + 7) / 8 * 8;
+    }
+    hipError_t e = osp::launch_attn3d_packed(pa, desc->head_dim, rq, rk, hs);
+    if (e != hipSuccess) return device_error(e, "attn3d_packed_fwd launch");
   }
   return ok();
 }

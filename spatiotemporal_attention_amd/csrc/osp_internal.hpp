@@ -9,6 +9,17 @@
 
 namespace osp {
 
+// Segments of a packed sequence served by one launch of the flash kernel.
+constexpr int kMaxPackSegs = 16;
+struct PackSeg {
+  int32_t tile0;                // first workgroup of the segment (a multiple of 8)
+  int32_t tiles;                // its tiles; tiles rounded up to 8 workgroups are launched
+  int32_t start;                // first token of the segment in the packed sequence
+  int32_t seq_len, q_tiles;     // subsequence length and query tiles of the segment
+  int32_t n_text, off1, off2, tab_entries;   // the segment's RopeGeom fields
+  FastDiv div_hw, div_w;
+};
+
 // One attention call, after validation.  Sequence of the call: N tokens,
 // split into `groups` subsequences of seq_len rows (groups = 1 for full).
 struct AttnArgs {
@@ -26,6 +37,11 @@ struct AttnArgs {
   FastDiv divk;                 // division by the Skiparse ratio
   float scale_log2;             // sm_scale * log2(e)
   RopeGeom rope;
+  // packed launches only: n_pack segments (workgroups from pack[s].tile0
+  // belong to segment s); the fields above that differ per segment are
+  // taken from the table
+  int32_t n_pack;
+  PackSeg pack[kMaxPackSegs];
 };
 
 // Rows of queries handled by one workgroup of the attention kernel, and
@@ -40,6 +56,9 @@ constexpr int kShortRows = 64;
 hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_q, int rope_k, hipStream_t s);
 hipError_t launch_attn3d_short(const AttnArgs& a, int head_dim, int rope_q, int rope_k,
                                hipStream_t s);
+// One flash-kernel launch over a.n_pack segments (each longer than kShortRows).
+hipError_t launch_attn3d_packed(const AttnArgs& a, int head_dim, int rope_q, int rope_k,
+                                hipStream_t s);
 
 struct RopeArgs {
   const uint16_t* x;

@@ -216,6 +216,21 @@ def test_packed_checks_every_segment_before_launch():
     assert call(good, desc=ctypes.byref(d80)) == UNSUP
 
 
+def test_rope3d_packed_errors():
+    lib = osp.lib()
+    d = _desc()
+    f = ctypes.c_void_p(4096)
+    arr = (osp.OspSegment * 2)()
+    arr[0].n_text, arr[0].grid_t, arr[0].grid_h, arr[0].grid_w = 3, 2, 3, 4
+    arr[1].n_text, arr[1].grid_t, arr[1].grid_h, arr[1].grid_w = 0, 0, 4, 5
+    assert lib.osp_rope3d_packed(ctypes.byref(d), arr, 2, f, f, None) == PARAM
+    assert b"segment 1" in lib.osp_last_error()
+    assert lib.osp_rope3d_packed(ctypes.byref(d), arr, 0, f, f, None) == PARAM
+    assert lib.osp_rope3d_packed(ctypes.byref(d), None, 1, f, f, None) == NULL
+    assert lib.osp_rope3d_packed(ctypes.byref(d), arr, 1, None, f, None) == NULL
+    assert lib.osp_rope3d_packed(ctypes.byref(d), arr, 1, f, ctypes.c_void_p(4100), None) == PARAM
+
+
 def test_success_clears_last_error():
     lib = osp.lib()
     osp.osp_attn3d_check(_desc())

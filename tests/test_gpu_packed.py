@@ -3,7 +3,9 @@ block-diagonal attention, RoPE from 0 on each video's own grid) against
 the fp64 oracle, through the C ABI: small packs element by element (both
 the short-subsequence and the flash kernel, Skiparse inside the segments,
 fused and unfused K rotation), each segment against a plain forward call on
-its slice, and the CogVideoX frame pack on sampled rows.  Needs an MI355X."""
+its slice (bit for bit: a packed launch runs the same arithmetic per
+segment), more segments than one launch's table holds, and the CogVideoX
+frame pack on sampled rows.  Needs an MI355X."""
 import numpy as np
 import pytest
 import torch
@@ -58,6 +60,17 @@ def test_packed_skiparse_per_segment(mode, k):
                  tag=f"{mode}-{k}")
 
 
+def test_packed_many_segments():
+    # 21 segments over 64 rows: two launches of the segment table (16 + 5),
+    # with short segments between them
+    segs = []
+    for i in range(21):
+        segs.append((i % 3, (1 + i % 2, 5 + i % 4, 16)))
+        if i % 7 == 3:
+            segs.append((0, (1, 3, 4)))
+    _packed_case(33, segs, heads=2, head_dim=64, split=(16, 24, 24), tag="many")
+
+
 def test_packed_segments_equal_plain_calls_and_fused_k():
     segs = [(7, (3, 6, 8)), (0, (1, 5, 5)), (11, (5, 4, 6))]
     split = (32, 32, 32)
@@ -80,8 +93,10 @@ def test_packed_segments_equal_plain_calls_and_fused_k():
         start = end
     o2, l2 = osp.osp_attn3d_packed_fwd(q, k_rot, v, segments=segs, rope_split=split,
                                        fuse_rope="q", return_lse=True)
+    k_rot2 = osp.osp_rope3d_packed(k, segments=segs, rope_split=split)
     torch.cuda.synchronize()
     assert torch.equal(o2, o) and torch.equal(l2, lse)
+    assert torch.equal(k_rot2, k_rot)
 
 
 def test_cogvideox_frame_pack_sampled_rows():
