@@ -210,8 +210,8 @@ __device__ __forceinline__ void load_row_operand(const uint16_t* row, bool valid
 //      -lse/scale for the P wave; dO rows, V, -delta for the dS wave);
 //      P wave: P = exp2(scale log2(e) X), written to the exchange buffer
 //      (fp32) and packed to bf16;
-//   2. dS wave: dS = P o X, packed; both: acc += T^T B (T = dO for the P
-//      wave with B = P, Q for the dS wave with B = dS; T^T read transposed).
+//   2. P wave: dV^T += dO^T P; dS wave: dS = P o X, packed, and its
+//      dK^T += Q^T dS in the next block's phase 1 (T^T read transposed).
 // The exchange buffer alternates between two halves from block to block:
 // a half is rewritten two blocks later, after the barrier that the reading
 // wave reaches only once it has used it.  KB = 2 (64 keys per pair) halves
@@ -383,28 +383,33 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     }
   };
-  auto phase2 = [&](auto role, auto sl, auto xh, int qb, f32x16_t (&x)[KB], bf16x8_t (&bop)[KB][2])
+  // dS wave, after the barrier of block qb: dS = P o (dP - delta) from the
+  // exchange half XH, packed as the B operand of its dK product
+  auto ds_make = [&](auto xh, f32x16_t (&x)[KB], bf16x8_t (&bop)[KB][2])
       __attribute__((always_inline)) {
-    constexpr bool R = decltype(role)::value;
-    if constexpr (!R) {
-      const float4* xi = xslot(xh) + pr * KB * 4 * 64 + lane;
+    const float4* xi = xslot(xh) + pr * KB * 4 * 64 + lane;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 p = xi[(kb * 4 + i) * 64];
-          x[kb][4 * i + 0] *= p.x; x[kb][4 * i + 1] *= p.y;
-          x[kb][4 * i + 2] *= p.z; x[kb][4 * i + 3] *= p.w;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float4 p = xi[(kb * 4 + i) * 64];
+        x[kb][4 * i + 0] *= p.x; x[kb][4 * i + 1] *= p.y;
+        x[kb][4 * i + 2] *= p.z; x[kb][4 * i + 3] *= p.w;
+      }
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          uint32_t w[4];
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t w[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) w[t] = pack_bf16(x[kb][8 * hh + 2 * t], x[kb][8 * hh + 2 * t + 1]);
-          bop[kb][hh] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-        }
+        for (int t = 0; t < 4; ++t) w[t] = pack_bf16(x[kb][8 * hh + 2 * t], x[kb][8 * hh + 2 * t + 1]);
+        bop[kb][hh] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
       }
     }
+  };
+  // acc += T^T B for block qb of the tile in slot SL (T = dO for the P
+  // wave, Q for the dS wave; T^T read transposed)
+  auto mma_t = [&](auto role, auto sl, int qb, const bf16x8_t (&bop)[KB][2])
+      __attribute__((always_inline)) {
+    constexpr bool R = decltype(role)::value;
     const char* tsl = reinterpret_cast<const char*>(R ? dslot(sl) : qslot(sl)) + 32 * qb * KCH * 16;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -420,37 +425,51 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
     }
     __builtin_amdgcn_s_setprio(0);
   };
-  // end of a tile: this wave's DMA has landed, then every wave's has (and
-  // every wave is done reading the tile slot that the next DMA refills)
+  // end of a tile: this wave's DMA has landed, then every wave's has
   auto tile_end = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     barrier();
   };
-  // the whole query loop of one role (the two roles run the same sequence
-  // of barriers)
+  // The whole query loop of one role; the two roles pass the same sequence
+  // of barriers.  The dS wave runs its dK product one block late, in the
+  // phase where the P wave exponentiates (and its dS arithmetic beside the
+  // P wave's dV product), so that on each SIMD one wave's VALU work meets
+  // the other's MFMAs.  The next tile's DMA is therefore issued only after
+  // the first barrier of a tile, when the late dK product of the previous
+  // tile has read its slot.
   auto run = [&](auto role) __attribute__((always_inline)) {
+    constexpr bool R = decltype(role)::value;
     f32x16_t x[KB];
     bf16x8_t bop[KB][2];
-    // the two blocks of the tile in slot SL
-    auto tile = [&](auto sl) __attribute__((always_inline)) {
+    const int nqt = (L + kBwdRows - 1) / kBwdRows;
+    auto tile = [&](auto sl, auto osl, int t) __attribute__((always_inline)) {
+      // block 0
+      if constexpr (!R) {
+        if (t > 0) mma_t(role, osl, 1, bop);    // block 1 of the previous tile
+      }
       phase1(role, sl, int_c<0>{}, 0, x, bop);
       barrier();
-      phase2(role, sl, int_c<0>{}, 0, x, bop);
+      if (t + 1 < nqt) issue(t + 1, osl);
+      if constexpr (R) mma_t(role, sl, 0, bop);
+      else ds_make(int_c<0>{}, x, bop);
+      // block 1
+      if constexpr (!R) mma_t(role, sl, 0, bop);
       phase1(role, sl, int_c<1>{}, 1, x, bop);
       barrier();
-      phase2(role, sl, int_c<1>{}, 1, x, bop);
+      if constexpr (R) mma_t(role, sl, 1, bop);
+      else ds_make(int_c<1>{}, x, bop);
+      tile_end();
     };
-    const int nqt = (L + kBwdRows - 1) / kBwdRows;
     issue(0, int_c<0>{});
     tile_end();
     for (int t = 0; t < nqt; t += 2) {
-      if (t + 1 < nqt) issue(t + 1, int_c<1>{});
-      tile(int_c<0>{});
-      tile_end();
+      tile(int_c<0>{}, int_c<1>{}, t);
       if (t + 1 >= nqt) break;
-      if (t + 2 < nqt) issue(t + 2, int_c<0>{});
-      tile(int_c<1>{});
-      tile_end();
+      tile(int_c<1>{}, int_c<0>{}, t + 1);
+    }
+    if constexpr (!R) {
+      if ((nqt - 1) & 1) mma_t(role, int_c<1>{}, 1, bop);
+      else mma_t(role, int_c<0>{}, 1, bop);
     }
   };
   if (pw) run(bool_c<true>{});
