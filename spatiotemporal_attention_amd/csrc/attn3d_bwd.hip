@@ -57,7 +57,7 @@ template <int D> struct BwdCfg {
   static constexpr int DPW = kBwdRows * KCH / 64 / LW;    // DMA loads per wave and tensor
   static_assert((kBwdRows * KCH / 64) % LW == 0, "every loading wave has the same share");
   // dK/dV: 4 pairs of waves, each pair owning KB blocks of 32 keys
-  static constexpr int KB = (D == 64) ? 2 : 1;
+  static constexpr int KB = (D == 128) ? 1 : 2;
   static constexpr int KV_ROWS = 4 * KB * 32;
   // dQ: 4 waves of 32 queries each
   static constexpr int NW_Q = 4;
@@ -215,8 +215,11 @@ __device__ __forceinline__ void load_row_operand(const uint16_t* row, bool valid
 // The exchange buffer alternates between two halves from block to block:
 // a half is rewritten two blocks later, after the barrier that the reading
 // wave reaches only once it has used it.  KB = 2 (64 keys per pair) halves
-// the LDS reads per product but needs more than the 256 registers a wave
-// gets at two waves per SIMD for head_dim 96 and 128, so those take KB = 1.
+// the LDS reads and the barriers per product; at head_dim 96 it needs a
+// few more than the 256 registers a wave gets at two waves per SIMD and
+// spills some loop-invariant values, which still runs 10% faster than
+// KB = 1 (forming them again in every phase instead costs more); head_dim
+// 128 takes KB = 1.
 template <int D>
 __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
