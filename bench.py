@@ -71,9 +71,11 @@ def parse():
     p.add_argument("--no-backward", action="store_true", help="skip the backward line")
     p.add_argument("--no-packed", action="store_true", help="skip the frame-pack line")
     p.add_argument("--profile-mode", default="full",
-                   choices=("full", "skiparse_single", "skiparse_group", "bwd"),
-                   help="attention mode of --profile (Skiparse with k=4; bwd: the full-attention "
-                        "backward)")
+                   choices=("full", "skiparse_single", "skiparse_group", "bwd", "temporal",
+                            "packed"),
+                   help="what --profile runs: attention over the 28,800-token workload (Skiparse "
+                        "with k=4; temporal: Single Skip with k = H*W), its backward (bwd), or the "
+                        "CogVideoX frame pack (packed)")
     p.add_argument("--copy", type=int, default=0,
                    help="instead: time a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -164,11 +166,35 @@ def main():
             osp.osp_rope3d_inv(t, grid=grid, n_text=wl.n_text, rope_split=wl.rope_split,
                                theta=wl.theta, out=t)
 
+    def packed_setup():
+        # CogVideoX Multi-Resolution Frame Pack: four clips with their text
+        # in one sequence, block-diagonal attention
+        pk = workloads.COGVIDEOX_PACK
+        wlc = workloads.WORKLOADS[pk["base"]]
+        segs = [(pk["n_text"], osp.osp_latent_grid(*c, wlc.c_t, wlc.c_s, wlc.p_t, wlc.p_s))
+                for c in pk["clips"]]
+        lens = [nt + g[0] * g[1] * g[2] for nt, g in segs]
+        pshape = (1, sum(lens), wlc.heads, wlc.head_dim)
+        qp, kp, vp = (t.to(dev) for t in workloads.make_qkv(pk["seed"], pshape))
+        op = torch.empty_like(qp)
+        kp_rot = torch.empty_like(kp)
+
+        def runp():
+            # as in the step above: K rotated by its own pass, Q in the loader
+            osp.osp_rope3d_packed(kp, segments=segs, rope_split=wlc.rope_split, out=kp_rot)
+            osp.osp_attn3d_packed_fwd(qp, kp_rot, vp, segments=segs, rope_split=wlc.rope_split,
+                                      fuse_rope="q", out=op)
+        return runp, segs, lens, wlc
+
     if args.profile:
         pm = args.profile_mode
         if pm == "bwd":
             bwd_setup()
             run = bwd_step
+        elif pm == "packed":
+            run = packed_setup()[0]
+        elif pm == "temporal":
+            run = lambda: step("skiparse_single", grid[1] * grid[2])   # noqa: E731
         else:
             pk = 1 if pm == "full" else 4
             run = lambda: step(pm, pk)   # noqa: E731
@@ -232,23 +258,7 @@ def main():
 
     packed = None
     if not args.no_packed:
-        # CogVideoX Multi-Resolution Frame Pack: four clips with their text
-        # in one sequence, block-diagonal attention
-        pk = workloads.COGVIDEOX_PACK
-        wlc = workloads.WORKLOADS[pk["base"]]
-        segs = [(pk["n_text"], osp.osp_latent_grid(*c, wlc.c_t, wlc.c_s, wlc.p_t, wlc.p_s))
-                for c in pk["clips"]]
-        lens = [nt + g[0] * g[1] * g[2] for nt, g in segs]
-        pshape = (1, sum(lens), wlc.heads, wlc.head_dim)
-        qp, kp, vp = (t.to(dev) for t in workloads.make_qkv(pk["seed"], pshape))
-        op = torch.empty_like(qp)
-        kp_rot = torch.empty_like(kp)
-
-        def runp():
-            # as in the step above: K rotated by its own pass, Q in the loader
-            osp.osp_rope3d_packed(kp, segments=segs, rope_split=wlc.rope_split, out=kp_rot)
-            osp.osp_attn3d_packed_fwd(qp, kp_rot, vp, segments=segs, rope_split=wlc.rope_split,
-                                      fuse_rope="q", out=op)
+        runp, segs, lens, wlc = packed_setup()
         for _ in range(args.warmup):
             runp()
         torch.cuda.synchronize()
@@ -297,7 +307,7 @@ def main():
                "ms_per_step_with_rope_transpose": round(b_step, 4),
                "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                "flop_per_call": f_bwd, "executed_mfma_tflops": round(tf * 7 / 5, 2),
-               "kernels": "bwd_prep + bwd_dkdv_kernel (8 waves, pairs, KB=1) + bwd_dq_kernel (4 waves), D=96",
+               "kernels": "bwd_prep + bwd_dkdv_kernel (8 waves in pairs, 64 keys per pair) + bwd_dq_kernel (4 waves), D=96",
                "fwd_plus_bwd_ms": round(ms_launch + b_launch, 4)}
 
     cpu = None
