@@ -191,7 +191,10 @@ osp_status osp_rope3d_inv(const osp_attn3d_desc* desc, const void* x, void* y,
    share that one rounding, without it the already rotated bf16 Q is
    rounded a second time.  OSP_FUSE_ROPE_K needs the per-axis cos/sin
    table in LDS: grid_t*rope_t + grid_h*rope_h + grid_w*rope_w <= 6144
-   (else OSP_ERR_UNSUPPORTED; rotate K with osp_rope3d instead).
+   (else OSP_ERR_UNSUPPORTED; rotate K with osp_rope3d instead).  It is
+   slower than rotating K once with osp_rope3d and passing OSP_FUSE_ROPE_Q
+   alone, since every query tile rotates the same K again: use it where a
+   rotated copy of K cannot be held.
    q, k, v: [B, N, H, D] bf16 read with stride_*; o: written with ostride_*,
    must not overlap q, k or v.  lse: NULL, or [B, H, N] fp32 contiguous,
    receives ln(sum_j exp(sm_scale * q_i . k_j)) over the row's subsequence,

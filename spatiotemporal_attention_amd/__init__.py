@@ -191,7 +191,9 @@ def osp_attn3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid,
     """Attention forward over [B, N, H, D] bf16 q, k, v on the GPU.
 
     fuse_rope: True (rotate Q and K in the loaders), False (both already
-    rotated), "q" or "k" (rotate only that one in its loader).
+    rotated), "q" or "k" (rotate only that one in its loader).  Rotating K
+    in the loader repeats the rotation for every query tile; where a rotated
+    copy of K fits, osp_rope3d on K and fuse_rope="q" is faster.
     Returns o (and lse [B, H, N] fp32 when return_lse or lse is given)."""
     b, n, h, d = q.shape
     st = _bnhd(q, "q")
@@ -209,15 +211,9 @@ def osp_attn3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid,
     desc = make_desc(batch=b, n_text=n_text, grid=grid, heads=h, head_dim=d,
                      rope_split=rope_split, theta=theta, pos_offset=pos_offset,
                      strides=st, ostrides=_bnhd(out, "out"))
-    if fuse_rope is True:
-        flags = OSP_FUSE_ROPE
-    elif fuse_rope is False or fuse_rope is None:
-        flags = 0
-    else:
-        flags = {"q": OSP_FUSE_ROPE_Q, "k": OSP_FUSE_ROPE_K, "qk": OSP_FUSE_ROPE}[fuse_rope]
     _check(lib().osp_attn3d_fwd(
         ctypes.byref(desc), _mode(mode), int(sparse_k),
-        float(sm_scale) if sm_scale is not None else 0.0, flags,
+        float(sm_scale) if sm_scale is not None else 0.0, _flags(fuse_rope),
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
         ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
         ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), _stream(q)))
