@@ -59,8 +59,9 @@ template <int D> struct BwdCfg {
   // dK/dV: 4 pairs of waves, each pair owning KB blocks of 32 keys
   static constexpr int KB = (D == 128) ? 1 : 2;
   static constexpr int KV_ROWS = 4 * KB * 32;
-  // dQ: 4 waves of 32 queries each
-  static constexpr int NW_Q = 4;
+  // dQ: waves of 32 queries each; with 8, waves 0-3 load K and 4-7 load V,
+  // with 4 every wave loads both
+  static constexpr int NW_Q = (D == 128) ? 4 : 8;
   static constexpr int OCC_Q = (D == 128) ? 1 : 2;
   static constexpr int Q_ROWS = NW_Q * 32;
 };
@@ -527,7 +528,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
   bf16x8_t qreg[D / 16], oreg[D / 16];
   load_row_operand<D>(a.q + in_off + int64_t(qi) * sn, qvalid, g, qreg);
   load_row_operand<D>(a.dout + in_off + int64_t(qi) * sn, qvalid, g, oreg);
-  const float nl = qvalid ? a.neg_lse_s[bhn + qi] : 0.f;
+  const float nlc2 = (qvalid ? a.neg_lse_s[bhn + qi] : 0.f) * c2;
   const float ne = qvalid ? a.neg_delta[bhn + qi] : 0.f;
 
   f32x16_t dq[D / 32];
@@ -540,8 +541,10 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
   int t_off[2][D / 32];
   tr_read_offsets<D>(lane, t_off);
 
+  static_assert(NW == C::LW || NW == 2 * C::LW, "one or two loading wave groups");
+  const int lw = wave % C::LW;       // rank among the waves loading a tensor
   TileDma<D> dma;
-  dma.init(wave, lane);
+  dma.init(lw, lane);
   const uint16_t* kg = a.k + in_off;
   const uint16_t* vg = a.v + in_off;
   auto load = [&](const uint16_t* src, uint32_t i0, uint16_t* dst) __attribute__((always_inline)) {
@@ -550,22 +553,28 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
 #pragma unroll
     for (int u = 0; u < C::DPW; ++u) {
       const int32_t off = dma.off[u];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(dst + 512 * (wave + C::LW * u)),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(dst + 512 * (lw + C::LW * u)),
                                                16, off, 0, 0, 0);
     }
   };
   auto issue = [&](int t, auto sl) __attribute__((always_inline)) {
     const uint32_t i0 = dma.at(t, mode, wb.j, divk, L, sn);
-    load(kg, i0, kslot(sl));
-    load(vg, i0, vslot(sl));
+    if constexpr (NW == C::LW) {
+      load(kg, i0, kslot(sl));
+      load(vg, i0, vslot(sl));
+    } else if (wave < C::LW) {
+      load(kg, i0, kslot(sl));
+    } else {
+      load(vg, i0, vslot(sl));
+    }
   };
 
   auto compute = [&](int t, auto sl) __attribute__((always_inline)) {
     const char* ks = reinterpret_cast<const char*>(kslot(sl));
     const char* vs = reinterpret_cast<const char*>(vslot(sl));
-    // keys past the end of the subsequence get P = 0 (their K and V rows
-    // are zero; the select keeps an overflowing exp2 out of dQ)
-    const bool tail = (t + 1) * kBwdRows > L;
+    // Keys past the end of the subsequence have zero K and V rows, so they
+    // add dS * 0 to dQ; P is clamped to [0, 1] (its true range), which
+    // keeps their exp2(-lse) finite without a branch per element.
 #pragma unroll
     for (int kb = 0; kb < kBwdRows / 32; ++kb) {
       const char* kblk = ks + 32 * kb * KCH * 16;
@@ -573,7 +582,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
       f32x16_t s, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        s[e] = nl;
+        s[e] = 0.f;
         dp[e] = ne;
       }
 #pragma unroll
@@ -590,13 +599,10 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const int e0 = 8 * hh + 2 * tt, e1 = e0 + 1;
-          float p0 = __builtin_amdgcn_exp2f(s[e0] * c2);
-          float p1 = __builtin_amdgcn_exp2f(s[e1] * c2);
-          if (tail) {
-            const int key0 = t * kBwdRows + 32 * kb + 8 * (e0 >> 2) + 4 * g + (e0 & 3);
-            p0 = (key0 < L) ? p0 : 0.f;
-            p1 = (key0 + 1 < L) ? p1 : 0.f;
-          }
+          const float p0 = __builtin_amdgcn_fmed3f(
+              __builtin_amdgcn_exp2f(__builtin_fmaf(s[e0], c2, nlc2)), 0.f, 1.f);
+          const float p1 = __builtin_amdgcn_fmed3f(
+              __builtin_amdgcn_exp2f(__builtin_fmaf(s[e1], c2, nlc2)), 0.f, 1.f);
           sw[tt] = pack_bf16(p0 * dp[e0], p1 * dp[e1]);
         }
         sb[hh] = __builtin_bit_cast(bf16x8_t, make_uint4(sw[0], sw[1], sw[2], sw[3]));
