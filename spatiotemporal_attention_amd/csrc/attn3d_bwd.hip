@@ -585,12 +585,26 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
         s[e] = 0.f;
         dp[e] = ne;
       }
+      // At head_dim 128 (one wave per SIMD) nothing else hides the LDS
+      // latency: the S and dP products keep three reads in flight.
+      constexpr int PFD = 3;
+      if constexpr (NW == C::LW) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kblk + r_off[c]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[c], s, 0, 0, 0);
         const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vblk + r_off[c]);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, oreg[c], dp, 0, 0, 0);
+      }
+      if constexpr (NW == C::LW) {
+        __builtin_amdgcn_sched_group_barrier(0x100, PFD, 0);      // LDS reads
+#pragma unroll
+        for (int c = 0; c < 2 * (D / 16) - PFD; ++c) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PFD, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
       bf16x8_t sb[2];
 #pragma unroll
