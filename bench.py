@@ -307,7 +307,7 @@ def main():
                "ms_per_step_with_rope_transpose": round(b_step, 4),
                "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                "flop_per_call": f_bwd, "executed_mfma_tflops": round(tf * 7 / 5, 2),
-               "kernels": "bwd_prep + bwd_dkdv_kernel (8 waves in pairs, 64 keys per pair) + bwd_dq_kernel (4 waves), D=96",
+               "kernels": "bwd_prep + bwd_dkdv_kernel (8 waves in pairs, 64 keys per pair) + bwd_dq_kernel (8 waves), D=96",
                "fwd_plus_bwd_ms": round(ms_launch + b_launch, 4)}
 
     cpu = None

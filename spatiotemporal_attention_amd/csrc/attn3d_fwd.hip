@@ -205,40 +205,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   const uint16_t* __restrict__ vg = a.v + in_off;
   const float c2 = a.scale_log2;
 
-  if constexpr (ROPE_Q || ROPE_K) {
-    stage_rope_rates<C::NT>(a.rope.omega, rl, tid);
-    __syncthreads();
-    fill_rope_table(rg, rl, tid, C::NT);
-    __syncthreads();
-  }
   const bool fast_rope = rg.aligned8 && rg.tab_entries;
 
   // ---- Q^T operand: lane holds query (block, l32), channels 16c + 8g .. +7
+  // (loaded in the prologue below)
   bf16x8_t qreg[QB][D / 16];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int r = int(qt) * C::BM + (wave * QB + qb) * 32 + l32;
-    const bool valid = r < L;
-    const uint32_t i = skiparse_token(mode, uint32_t(valid ? r : 0), j, divk, uint32_t(L));
-    const uint16_t* p = qg + int64_t(i) * a_sn;
-    const bool video = ROPE_Q && is_video(rg, i);
-    const Coord3 cc = video_coords(rg, i);
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      uint4 raw = valid ? ld16(p + 16 * c + 8 * g) : make_uint4(0, 0, 0, 0);
-      // times scale * log2(e) so that the score products come out in log2
-      // units; a rotated row is rotated and scaled in fp32, rounded once
-      if (ROPE_Q && video) {
-        raw = rotate_chunk_scaled(rg, rl, 8 * c + 4 * g, cc, raw, c2);
-      } else {
-        raw.x = pack_bf16(bf16lo(raw.x) * c2, bf16hi(raw.x) * c2);
-        raw.y = pack_bf16(bf16lo(raw.y) * c2, bf16hi(raw.y) * c2);
-        raw.z = pack_bf16(bf16lo(raw.z) * c2, bf16hi(raw.z) * c2);
-        raw.w = pack_bf16(bf16lo(raw.w) * c2, bf16hi(raw.w) * c2);
-      }
-      qreg[qb][c] = __builtin_bit_cast(bf16x8_t, raw);
-    }
-  }
 
   // ---- loaders.  Tile kt's first row r0 = kt*BN maps to token i0(kt); the
   // remap is increasing in the row, and with FIXED_ROWS row r0 + row maps
@@ -514,6 +485,69 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     }
   };
 
+  // ---- prologue, part 1.  Without K rotation in the loader the first two
+  // K and V tiles are requested first, then the Q rows, so that all these
+  // latencies overlap each other and the RoPE table.  The LDS barriers
+  // here wait for LDS stores only, not for those loads.
+  auto lds_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // (the rates are staged first, and their load waited for, so that no
+  // later wait for it also waits for the tiles)
+  if constexpr (ROPE_Q || ROPE_K) {
+    static_assert(C::NT >= kMaxPairs, "one rate per thread");
+    if (tid < kMaxPairs) rl->omega[tid] = a.rope.omega[tid];
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (!ROPE_K) {
+    issue_tile(0, int_c<0>{});
+    issue_tile(1, int_c<1>{});
+  }
+  // Q rows: every chunk is requested before any is used (a row past the end
+  // reads the last row and is zeroed afterwards, so the loads need no
+  // branch); the table is built while they are in flight.
+  uint4 qraw[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = int(qt) * C::BM + (wave * QB + qb) * 32 + l32;
+    const uint32_t i = skiparse_token(mode, uint32_t(min(r, L - 1)), j, divk, uint32_t(L));
+    const uint16_t* p = qg + int64_t(i) * a_sn;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) qraw[qb][c] = ld16(p + 16 * c + 8 * g);
+  }
+  if constexpr (ROPE_Q || ROPE_K) {
+    lds_barrier();
+    fill_rope_table(rg, rl, tid, C::NT);
+    lds_barrier();
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = int(qt) * C::BM + (wave * QB + qb) * 32 + l32;
+    const bool valid = r < L;
+    const uint32_t i = skiparse_token(mode, uint32_t(valid ? r : 0), j, divk, uint32_t(L));
+    const bool video = ROPE_Q && is_video(rg, i);
+    const Coord3 cc = video_coords(rg, i);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      uint4 raw = valid ? qraw[qb][c] : make_uint4(0, 0, 0, 0);
+      // times scale * log2(e) so that the score products come out in log2
+      // units; a rotated row is rotated and scaled in fp32, rounded once
+      if (ROPE_Q && video) {
+        raw = rotate_chunk_scaled(rg, rl, 8 * c + 4 * g, cc, raw, c2);
+      } else {
+        raw.x = pack_bf16(bf16lo(raw.x) * c2, bf16hi(raw.x) * c2);
+        raw.y = pack_bf16(bf16lo(raw.y) * c2, bf16hi(raw.y) * c2);
+        raw.z = pack_bf16(bf16lo(raw.z) * c2, bf16hi(raw.z) * c2);
+        raw.w = pack_bf16(bf16lo(raw.w) * c2, bf16hi(raw.w) * c2);
+      }
+      qreg[qb][c] = __builtin_bit_cast(bf16x8_t, raw);
+    }
+  }
+
   // ---- ping-pong schedule.  The waves form two halves, one wave of each
   // on every SIMD.  Per key tile t a wave runs a matrix phase M(t) (S(t) =
   // K(t) Q^T, then O += P(t-1) V(t-1)) and a softmax phase V(t) (max,
@@ -584,8 +618,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     barrier();
   };
 
-  // prologue: K(0), K(1), V(0), V(1) into slots 0 and 1; V slot 2 (read
-  // as "V(-1)" by the first matrix phase, with P = 0) cleared
+  // prologue, part 2: K(0), K(1), V(0), V(1) into slots 0 and 1 (with K
+  // rotation in the loader: here); V slot 2 (read as "V(-1)" by the first
+  // matrix phase, with P = 0) cleared
   for (int e = tid; e < C::TILE / 8; e += C::NT)
     reinterpret_cast<uint4*>(v_s2)[e] = make_uint4(0, 0, 0, 0);
 #pragma unroll
@@ -595,10 +630,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       pb[qb][kb][0] = bf16x8_t{};
       pb[qb][kb][1] = bf16x8_t{};
     }
-  issue_tile(0, int_c<0>{});
-  finish_tile(0, int_c<0>{});
-  issue_tile(1, int_c<1>{});
-  finish_tile(1, int_c<1>{});
+  if constexpr (ROPE_K) {
+    issue_tile(0, int_c<0>{});
+    finish_tile(0, int_c<0>{});
+    issue_tile(1, int_c<1>{});
+    finish_tile(1, int_c<1>{});
+  }
   __syncthreads();
   if (!lead) barrier();
   int t = 0;
