@@ -236,6 +236,7 @@ def main():
 
     extra = {}
     sep = None
+    suv = None
     if not args.no_skiparse:
         for mode in ("skiparse_single", "skiparse_group"):
             s_step, s_launch, s_med, s_min, _ = timed(mode, 4, max(args.steps, 5), args.warmup)
@@ -255,6 +256,20 @@ def main():
         sep["ms_spatial_plus_temporal"] = round(sep["spatial"]["ms_per_launch"] +
                                                 sep["temporal"]["ms_per_launch"], 4)
         sep["vs_full_3d"] = round(sep["ms_spatial_plus_temporal"] / ms_launch, 4)
+        # a U-shaped per-layer sparsity schedule over the same tensors: the
+        # attention time of one pass through its layers against every layer
+        # full (each distinct (mode, k) timed once)
+        per = {}
+        for mode, kk in workloads.SUV_SCHEDULE:
+            if (mode, kk) not in per:
+                per[(mode, kk)] = timed(mode, kk, max(args.steps // 2, 5), args.warmup)[1]
+        ms_pass = sum(per[mk] for mk in workloads.SUV_SCHEDULE)
+        f_pass = sum(flops(kk) for _, kk in workloads.SUV_SCHEDULE)
+        suv = {"schedule": [[m, kk] for m, kk in workloads.SUV_SCHEDULE],
+               "ms_per_pass": round(ms_pass, 4),
+               "ms_all_full": round(len(workloads.SUV_SCHEDULE) * ms_launch, 4),
+               "vs_all_full": round(ms_pass / (len(workloads.SUV_SCHEDULE) * ms_launch), 4),
+               "tflops": round(f_pass / (ms_pass * 1e-3) / 1e12, 2)}
 
     packed = None
     if not args.no_packed:
@@ -358,6 +373,7 @@ def main():
                      "ms_median": round(ms_med, 4), "ms_min": round(ms_min, 4)},
         "skiparse": extra,
         "separated_2d1d": sep,
+        "suv_schedule": suv,
         "backward": bwd,
         "packed": packed,
         "cpu_baseline": cpu,

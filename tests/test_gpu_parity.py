@@ -136,6 +136,14 @@ def test_multitile_d96(variant, mode, k):
              tol=4.0 if variant == "sharp" else 1.0)
 
 
+def test_suv_schedule_layers():
+    # every layer of the U-shaped schedule on one 768-token grid (a multiple
+    # of 8^2, so that group skip at k = 8 divides it), each against the oracle
+    for mode, k in workloads.SUV_SCHEDULE:
+        run_case(12, grid=(3, 16, 16), n_text=0, heads=2, head_dim=96, rope_split=(32, 32, 32),
+                 mode=mode, sparse_k=k, tag=f"suv-{mode}-{k}")
+
+
 def test_text_tokens_d64():
     run_case(11, grid=(3, 10, 12), n_text=37, heads=2, head_dim=64, rope_split=(16, 24, 24),
              tag="text-d64")

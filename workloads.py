@@ -22,6 +22,10 @@ Workloads (clip sizes from the pages; latent-grid arithmetic is done elsewhere):
   8x8x8 VAE and 1x2x2 patchify, full and k=4; the pages give no head shape
   for that model, so 24 heads of D=128 (split 32/48/48) are taken, which
   also exercises the third head size.  Checked on 256 seeded query rows.
+* ``SUV_SCHEDULE`` -- a U-shaped per-layer sparsity schedule (the SUV sparse
+  DiT on the OSP blog page, v1.5.0 entry, names U-shaped sparsity but gives
+  no schedule): full attention in the outer layers, k rising to 8 toward the
+  middle and back, single and group skip alternating at each k.
 * ``COGVIDEOX_PACK`` -- a Multi-Resolution Frame Pack (CogVideoX section 3.1):
   clips of 49, 25 and 1 frames at 480x720 and one of 33 frames at 256x384
   (Table 8's smallest resolution), each with its 226 text tokens, in one
@@ -129,3 +133,9 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 # through the cogvideox workload's VAE and patchify factors
 COGVIDEOX_PACK = {"clips": ((49, 480, 720), (25, 480, 720), (1, 480, 720), (33, 256, 384)),
                   "n_text": 226, "base": "cogvideox", "seed": 6, "sample_rows": 192}
+
+# U-shaped sparsity over 12 layer positions: (mode, k) per layer
+SUV_SCHEDULE = (("full", 1), ("skiparse_single", 2), ("skiparse_group", 2),
+                ("skiparse_single", 4), ("skiparse_group", 4), ("skiparse_single", 8),
+                ("skiparse_group", 8), ("skiparse_single", 4), ("skiparse_group", 4),
+                ("skiparse_single", 2), ("skiparse_group", 2), ("full", 1))
