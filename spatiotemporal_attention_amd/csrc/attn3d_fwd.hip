@@ -684,8 +684,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
 // Tile shape per head_dim: 32-row query blocks per wave (QB), keys per
 // tile (BN), waves per workgroup (NW), waves per SIMD (OCC).  Build-time
 // overridable for tuning.
+// D=64: two 32-row query blocks per wave over 32-key tiles; each K or V
+// fragment read from LDS then feeds two MFMAs, and the matrix phase is as
+// long as at D=128 with half the registers per block (7% faster on
+// CogVideoX's 17,776 tokens than one block over 64-key tiles)
 #ifndef OSP_D64_TILE
-#define OSP_D64_TILE 1, 64, 8, 2
+#define OSP_D64_TILE 2, 32, 8, 2
 #endif
 #ifndef OSP_D96_TILE
 #define OSP_D96_TILE 1, 64, 8, 2
