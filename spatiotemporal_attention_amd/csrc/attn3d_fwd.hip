@@ -99,13 +99,13 @@ template <int NMK, int NMV, int L> __device__ constexpr int m_first_reads() {
   for (int m = 0; m < L; ++m) r += m_reads<NMK, NMV>(m);
   return r;
 }
-template <int NMK, int NMV, int L, int I = 0>
+template <int NMK, int NMV, int L, int G, int I = 0>
 __device__ __forceinline__ void m_phase_order() {
   if constexpr (I < NMK + NMV) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x008, G, 0);        // the G MFMAs of one read
     constexpr int r = m_reads<NMK, NMV>(I + L);
     if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);   // DS read
-    m_phase_order<NMK, NMV, L, I + 1>();
+    m_phase_order<NMK, NMV, L, G, I + 1>();
   }
 }
 
@@ -587,8 +587,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     else __builtin_amdgcn_s_waitcnt((C::DPW & 15) | ((C::DPW >> 4) << 14) | 0x0F70);
   };
   // matrix phase of tile t: QK(t) from K slot P (QK) and PV(t-1) from V
-  // slot (P + 2) % 3 (PV).  Instruction order inside it: the LDS reads run
-  // OSP_M_LEAD MFMAs ahead of the MFMAs that use them.
+  // slot (P + 2) % 3 (PV).  Instruction order inside it (one query block
+  // per wave): the LDS reads run OSP_M_LEAD MFMAs ahead of the MFMAs that
+  // use them.  With two blocks the compiler's own order was as fast.
   auto m_phase = [&](int t, auto slot, auto do_qk, auto do_pv, auto masked) __attribute__((always_inline)) {
     constexpr int P = decltype(slot)::value;
     constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
@@ -598,7 +599,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     if constexpr (QB == 1) {
       constexpr int NMV = PV ? NKB * 2 * (D / 32) : 0, NMK = QK ? NKB * (D / 16) : 0;
       __builtin_amdgcn_sched_group_barrier(0x100, m_first_reads<NMK, NMV, OSP_M_LEAD>(), 0);
-      m_phase_order<NMK, NMV, OSP_M_LEAD>();
+      m_phase_order<NMK, NMV, OSP_M_LEAD, QB>();
     }
     __builtin_amdgcn_s_setprio(0);
   };
