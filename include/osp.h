@@ -141,8 +141,9 @@ osp_status osp_rope3d(const osp_attn3d_desc* desc, const void* x, void* y,
    contiguous default strides use the packed length N = sum of the
    segment lengths.  q, k, v, o: [B, N, H, D]; lse: NULL or [B, H, N] fp32
    contiguous over the packed N.  segments: host array, read during the
-   call only.  Every segment is checked before anything is enqueued; the
-   segments then run one launch each, in order, on the stream. */
+   call only.  Every segment is checked before anything is enqueued.
+   Segments whose subsequences have at most 64 rows run one launch each;
+   the others share flash launches of up to 16 segments, longest first. */
 osp_status osp_attn3d_packed_fwd(const osp_attn3d_desc* desc,
                                  const osp_segment* segments,
                                  int32_t n_segments, int32_t mode,
@@ -159,6 +160,16 @@ osp_status osp_attn3d_packed_fwd(const osp_attn3d_desc* desc,
 osp_status osp_rope3d_packed(const osp_attn3d_desc* desc,
                              const osp_segment* segments, int32_t n_segments,
                              const void* x, void* y, void* stream);
+
+/* osp_rope3d_inv over a packed sequence: each segment's rows rotated back
+   (by the negative angle) on its own grid.  It maps the gradients that
+   osp_attn3d_packed_bwd returns for the rotated q and k to the tensors
+   before osp_rope3d_packed.  One launch per segment; y == x works in
+   place. */
+osp_status osp_rope3d_packed_inv(const osp_attn3d_desc* desc,
+                                 const osp_segment* segments,
+                                 int32_t n_segments, const void* x, void* y,
+                                 void* stream);
 
 /* Transpose (= inverse) of osp_rope3d: y = rotate(x) by the negative
    angle for every video [b, n, h] row, text rows copied, same strides,
@@ -244,6 +255,37 @@ osp_status osp_attn3d_bwd(const osp_attn3d_desc* desc, int32_t mode,
                           const float* lse, const void* dout, void* dq,
                           void* dk, void* dv, void* workspace,
                           int64_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace osp_attn3d_packed_bwd needs: two fp32
+   [B, H, N] arrays over the packed N, each rounded up to 256 bytes.
+   Checks every segment as osp_attn3d_packed_bwd does.  Host only. */
+osp_status osp_attn3d_packed_bwd_workspace(const osp_attn3d_desc* desc,
+                                           const osp_segment* segments,
+                                           int32_t n_segments, int32_t mode,
+                                           int32_t sparse_k, int64_t* bytes);
+
+/* Attention backward over a packed sequence (CogVideoX section 3.1,
+   "Multi-Resolution Frame Pack"; segments, desc and strides as in
+   osp_attn3d_packed_fwd): for each segment s, exactly what osp_attn3d_bwd
+   gives on its slice of the tensors with desc's grid and n_text set to the
+   segment's.  q and k are the rotated tensors (osp_rope3d_packed output);
+   dq and dk are gradients with respect to them (osp_rope3d_packed_inv maps
+   them back).  lse: [B, H, N] fp32 contiguous over the packed N, from
+   osp_attn3d_packed_fwd.  workspace: at least
+   osp_attn3d_packed_bwd_workspace() bytes, 256-byte aligned, owned by the
+   caller; segment s uses its own part of it.  Every segment is checked
+   before anything is enqueued; the segments then run one backward each
+   (three launches), in order, on the stream.  Other rules as in
+   osp_attn3d_bwd. */
+osp_status osp_attn3d_packed_bwd(const osp_attn3d_desc* desc,
+                                 const osp_segment* segments,
+                                 int32_t n_segments, int32_t mode,
+                                 int32_t sparse_k, float sm_scale,
+                                 const void* q, const void* k, const void* v,
+                                 const void* o, const float* lse,
+                                 const void* dout, void* dq, void* dk, void* dv,
+                                 void* workspace, int64_t workspace_bytes,
+                                 void* stream);
 
 /* Index maps of the subsequences of an N-token sequence (Skiparse,
    Open-Sora Plan section 2.2.2; BLOCK as above).

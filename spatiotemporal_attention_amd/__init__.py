@@ -77,6 +77,11 @@ def lib() -> ctypes.CDLL:
             "osp_attn3d_packed_fwd": (I32, [D, ctypes.POINTER(OspSegment), I32, I32, I32, F32,
                                             I32, P, P, P, P, P, P]),
             "osp_rope3d_packed": (I32, [D, ctypes.POINTER(OspSegment), I32, P, P, P]),
+            "osp_rope3d_packed_inv": (I32, [D, ctypes.POINTER(OspSegment), I32, P, P, P]),
+            "osp_attn3d_packed_bwd_workspace": (I32, [D, ctypes.POINTER(OspSegment), I32, I32,
+                                                      I32, ctypes.POINTER(I64)]),
+            "osp_attn3d_packed_bwd": (I32, [D, ctypes.POINTER(OspSegment), I32, I32, I32, F32,
+                                            P, P, P, P, P, P, P, P, P, P, I64, P]),
             "osp_attn3d_bwd_workspace": (I32, [D, I32, I32, ctypes.POINTER(I64)]),
             "osp_attn3d_bwd": (I32, [D, I32, I32, F32, P, P, P, P, P, P, P, P, P, P, I64, P]),
             "osp_skiparse_index": (I32, [I32, I32, I64, P, P, I32, P]),
@@ -93,8 +98,9 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("osp_abi_version", "osp_status_string", "osp_last_error", "osp_latent_grid",
             "osp_attn3d_check", "osp_rope3d", "osp_rope3d_inv", "osp_attn3d_fwd",
-            "osp_attn3d_packed_fwd", "osp_rope3d_packed",
-            "osp_attn3d_bwd_workspace", "osp_attn3d_bwd", "osp_skiparse_index")
+            "osp_attn3d_packed_fwd", "osp_rope3d_packed", "osp_rope3d_packed_inv",
+            "osp_attn3d_bwd_workspace", "osp_attn3d_bwd", "osp_attn3d_packed_bwd_workspace",
+            "osp_attn3d_packed_bwd", "osp_skiparse_index")
 
 
 def _check(status: int):
@@ -235,7 +241,7 @@ def _segments(segments, n):
         segs[i].n_text = int(n_text)
         segs[i].grid_t, segs[i].grid_h, segs[i].grid_w = (int(x) for x in grid)
         total += int(n_text) + int(grid[0]) * int(grid[1]) * int(grid[2])
-    if total != n:
+    if n is not None and total != n:
         raise ValueError(f"segments cover {total} tokens, the tensors hold {n}")
     return segs
 
@@ -243,6 +249,18 @@ def _segments(segments, n):
 def osp_rope3d_packed(x: torch.Tensor, *, segments, rope_split, theta: float = 1e4,
                       pos_offset=(0, 0, 0), out: torch.Tensor | None = None) -> torch.Tensor:
     """3D RoPE of a packed [B, N, H, D] sequence, each segment on its own grid."""
+    return _rope_packed_call("osp_rope3d_packed", x, segments=segments, rope_split=rope_split,
+                             theta=theta, pos_offset=pos_offset, out=out)
+
+
+def osp_rope3d_packed_inv(x: torch.Tensor, *, segments, rope_split, theta: float = 1e4,
+                          pos_offset=(0, 0, 0), out: torch.Tensor | None = None) -> torch.Tensor:
+    """Transpose of osp_rope3d_packed (each segment rotated back on its grid)."""
+    return _rope_packed_call("osp_rope3d_packed_inv", x, segments=segments,
+                             rope_split=rope_split, theta=theta, pos_offset=pos_offset, out=out)
+
+
+def _rope_packed_call(name, x, *, segments, rope_split, theta, pos_offset, out):
     if out is None:
         out = torch.empty_like(x)
     b, n, h, d = x.shape
@@ -252,9 +270,9 @@ def osp_rope3d_packed(x: torch.Tensor, *, segments, rope_split, theta: float = 1
     desc = make_desc(batch=b, n_text=0, grid=(1, 1, n), heads=h, head_dim=d,
                      rope_split=rope_split, theta=theta, pos_offset=pos_offset,
                      strides=_bnhd(x, "x"), ostrides=_bnhd(out, "out"))
-    _check(lib().osp_rope3d_packed(ctypes.byref(desc), segs, len(segments),
-                                   ctypes.c_void_p(x.data_ptr()),
-                                   ctypes.c_void_p(out.data_ptr()), _stream(x)))
+    _check(getattr(lib(), name)(ctypes.byref(desc), segs, len(segments),
+                                ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                _stream(x)))
     return out
 
 
@@ -330,6 +348,56 @@ def osp_attn3d_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
         raise ValueError(f"workspace of {need} bytes needed")
     _check(lib().osp_attn3d_bwd(
         ctypes.byref(desc), _mode(mode), int(sparse_k),
+        float(sm_scale) if sm_scale is not None else 0.0,
+        *(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o, lse, dout, *outs, workspace)),
+        int(workspace.numel() * workspace.element_size()), _stream(q)))
+    return tuple(outs)
+
+
+def osp_attn3d_packed_bwd_workspace(desc: OspAttn3dDesc, segments, mode="full",
+                                    sparse_k: int = 1) -> int:
+    """Bytes of workspace osp_attn3d_packed_bwd needs (host-only query)."""
+    out = ctypes.c_int64(0)
+    segs = _segments(segments, None)
+    _check(lib().osp_attn3d_packed_bwd_workspace(ctypes.byref(desc), segs, len(segments),
+                                                 _mode(mode), int(sparse_k), ctypes.byref(out)))
+    return int(out.value)
+
+
+def osp_attn3d_packed_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                          lse: torch.Tensor, dout: torch.Tensor, *, segments, mode="full",
+                          sparse_k: int = 1, sm_scale: float | None = None,
+                          dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                          dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Attention backward over a packed [B, N, H, D] sequence (segments as in
+    osp_attn3d_packed_fwd).  q and k are the rotated tensors; dq and dk are
+    gradients with respect to them (osp_rope3d_packed_inv maps them back).
+    lse is the packed forward's [B, H, N] fp32 log-sum-exp.  Returns
+    (dq, dk, dv)."""
+    b, n, h, d = q.shape
+    st = _bnhd(q, "q")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if _bnhd(t, name) != st or t.shape != q.shape:
+            raise ValueError("q, k, v, o and dout must share shape and strides")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (b, h, n) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    outs = []
+    for t in (dq, dk, dv):
+        outs.append(torch.empty((b, n, h, d), dtype=torch.bfloat16, device=q.device)
+                    if t is None else t)
+    ost = _bnhd(outs[0], "dq")
+    if any(_bnhd(t, "dk/dv") != ost or tuple(t.shape) != (b, n, h, d) for t in outs):
+        raise ValueError("dq, dk and dv must share the shape of q and one set of strides")
+    segs = _segments(segments, n)
+    desc = make_desc(batch=b, n_text=0, grid=(1, 1, n), heads=h, head_dim=d,
+                     rope_split=(d, 0, 0), strides=st, ostrides=ost)
+    need = osp_attn3d_packed_bwd_workspace(desc, segments, mode, sparse_k)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace of {need} bytes needed")
+    _check(lib().osp_attn3d_packed_bwd(
+        ctypes.byref(desc), segs, len(segments), _mode(mode), int(sparse_k),
         float(sm_scale) if sm_scale is not None else 0.0,
         *(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o, lse, dout, *outs, workspace)),
         int(workspace.numel() * workspace.element_size()), _stream(q)))

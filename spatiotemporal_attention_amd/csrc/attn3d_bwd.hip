@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdArgs a,
     }
   }
   a.neg_delta[idx] = -((acc[0] + acc[1]) + (acc[2] + acc[3]));
-  a.neg_lse_s[idx] = -a.lse[idx] / a.scale;
+  a.neg_lse_s[idx] = -a.lse[int64_t(bh) * a.lse_ld + n] / a.scale;
 }
 
 // ---------------------------------------------------------------------------

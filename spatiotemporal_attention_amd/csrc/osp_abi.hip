@@ -240,10 +240,97 @@ void fill_fwd_args(const osp_attn3d_desc* desc, const Shape& s, int32_t mode, in
   a.n_pack = 0;
 }
 
+// Checks of a packed backward: every segment as a backward call of its
+// own, then the packed length; *total = the packed N.
+osp_status check_packed_bwd(const osp_attn3d_desc* desc, const osp_segment* segments,
+                            int32_t n_segments, int32_t mode, int32_t sparse_k, int64_t* total) {
+  if (!desc) return fail(OSP_ERR_NULL, "desc is NULL");
+  if (!segments) return fail(OSP_ERR_NULL, "segments is NULL");
+  if (n_segments < 1) return fail(OSP_ERR_PARAM, "n_segments (%d) must be >= 1", n_segments);
+  int64_t n = 0;
+  for (int32_t i = 0; i < n_segments; ++i) {
+    osp_attn3d_desc d = *desc;
+    d.n_text = segments[i].n_text;
+    d.grid_t = segments[i].grid_t;
+    d.grid_h = segments[i].grid_h;
+    d.grid_w = segments[i].grid_w;
+    Shape s;
+    osp_status st = check_bwd(&d, mode, sparse_k, &s);
+    if (st) {
+      const std::string why = g_last_error;
+      return fail(st, "segment %d: %s", i, why.c_str());
+    }
+    n += s.n_tokens;
+    if (n > 0x7fffffffLL || int64_t(desc->batch) * desc->heads * n > 0x7fffffffLL)
+      return fail(OSP_ERR_SHAPE, "packed batch*heads*N exceeds 2^31-1");
+  }
+  *total = n;
+  return OSP_OK;
+}
+
 // bytes of one of the two fp32 [B, H, N] workspace arrays, rounded up to 256
-int64_t bwd_ws_half(const osp_attn3d_desc* d, const Shape& s) {
-  const int64_t b = int64_t(d->batch) * d->heads * s.n_tokens * 4;
+int64_t bwd_ws_half(int64_t batch, int64_t heads, int64_t n_tokens) {
+  const int64_t b = batch * heads * n_tokens * 4;
   return (b + 255) / 256 * 256;
+}
+
+osp_status check_bwd_pointers(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              void* workspace, float sm_scale) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+    return fail(OSP_ERR_NULL, "q, k, v, o, lse, dout, dq, dk, dv and workspace must be non-NULL");
+  const void* bf[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : bf)
+    if (!aligned16(p)) return fail(OSP_ERR_PARAM, "bf16 tensors must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(OSP_ERR_PARAM, "lse must be 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(OSP_ERR_PARAM, "workspace must be 256-byte aligned");
+  if (isnan(sm_scale) || isinf(sm_scale)) return fail(OSP_ERR_PARAM, "sm_scale must be finite");
+  return OSP_OK;
+}
+
+// The three backward launches for one (checked) sequence: tensors at the
+// given bases with the strides of s, lse rows lse_ld apart, and the two
+// workspace arrays of B*H*N_s floats each.
+osp_status enqueue_bwd(const osp_attn3d_desc* desc, const Shape& s, int32_t mode,
+                       int32_t sparse_k, float sm_scale, const void* q, const void* k,
+                       const void* v, const void* o, const float* lse, int64_t lse_ld,
+                       const void* dout, void* dq, void* dk, void* dv, float* ws_delta,
+                       float* ws_lse, hipStream_t stream) {
+  const int D = desc->head_dim;
+  const double scale = sm_scale > 0.f ? double(sm_scale) : 1.0 / sqrt(double(D));
+  const int32_t groups = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
+  osp::BwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.lse_ld = lse_ld;
+  a.neg_delta = ws_delta;
+  a.neg_lse_s = ws_lse;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.sb = s.sb; a.sn = s.sn; a.sh = s.sh;
+  a.osb = s.osb; a.osn = s.osn; a.osh = s.osh;
+  a.batch = desc->batch;
+  a.heads = desc->heads;
+  a.n_tokens = int32_t(s.n_tokens);
+  a.groups = groups;
+  a.seq_len = int32_t(s.n_tokens / groups);
+  a.mode = mode;
+  a.divk = osp::make_fastdiv(uint32_t(groups));
+  a.scale = float(scale);
+  a.scale_log2 = float(scale * 1.4426950408889634);
+  const int kvr = osp::bwd_kv_rows_per_block(D), qr = osp::bwd_q_rows_per_block(D);
+  a.kv_blocks = (a.seq_len + kvr - 1) / kvr;
+  a.q_blocks = (a.seq_len + qr - 1) / qr;
+  if (a.seq_len == 0) return OSP_OK;
+  hipError_t e = osp::launch_attn3d_bwd(a, D, stream);
+  if (e != hipSuccess) return device_error(e, "attn3d_bwd launch");
+  return OSP_OK;
 }
 
 }  // namespace
@@ -326,8 +413,9 @@ osp_status osp_rope3d_inv(const osp_attn3d_desc* desc, const void* x, void* y, v
   return rope3d_call(desc, x, y, stream, 1);
 }
 
-osp_status osp_rope3d_packed(const osp_attn3d_desc* desc, const osp_segment* segments,
-                             int32_t n_segments, const void* x, void* y, void* stream) {
+static osp_status rope3d_packed_call(const osp_attn3d_desc* desc, const osp_segment* segments,
+                                     int32_t n_segments, const void* x, void* y, void* stream,
+                                     int32_t inverse) {
   if (!desc) return fail(OSP_ERR_NULL, "desc is NULL");
   if (!segments) return fail(OSP_ERR_NULL, "segments is NULL");
   if (n_segments < 1) return fail(OSP_ERR_PARAM, "n_segments (%d) must be >= 1", n_segments);
@@ -378,13 +466,23 @@ osp_status osp_rope3d_packed(const osp_attn3d_desc* desc, const osp_segment* seg
     a.n_tokens = int32_t(n);
     a.heads = desc->heads;
     a.head_dim = desc->head_dim;
-    a.inverse = 0;
+    a.inverse = inverse;
     fill_rope(&d, &a.rope);
     hipError_t e = osp::launch_rope3d(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_error(e, "rope3d launch");
     start += n;
   }
   return ok();
+}
+
+osp_status osp_rope3d_packed(const osp_attn3d_desc* desc, const osp_segment* segments,
+                             int32_t n_segments, const void* x, void* y, void* stream) {
+  return rope3d_packed_call(desc, segments, n_segments, x, y, stream, 0);
+}
+
+osp_status osp_rope3d_packed_inv(const osp_attn3d_desc* desc, const osp_segment* segments,
+                                 int32_t n_segments, const void* x, void* y, void* stream) {
+  return rope3d_packed_call(desc, segments, n_segments, x, y, stream, 1);
 }
 
 osp_status osp_attn3d_fwd(const osp_attn3d_desc* desc, int32_t mode, int32_t sparse_k,
@@ -523,7 +621,7 @@ osp_status osp_attn3d_bwd_workspace(const osp_attn3d_desc* desc, int32_t mode, i
   Shape s;
   osp_status st = check_bwd(desc, mode, sparse_k, &s);
   if (st) return st;
-  *bytes = 2 * bwd_ws_half(desc, s);
+  *bytes = 2 * bwd_ws_half(desc->batch, desc->heads, s.n_tokens);
   return ok();
 }
 
@@ -534,51 +632,79 @@ osp_status osp_attn3d_bwd(const osp_attn3d_desc* desc, int32_t mode, int32_t spa
   Shape s;
   osp_status st = check_bwd(desc, mode, sparse_k, &s);
   if (st) return st;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
-    return fail(OSP_ERR_NULL, "q, k, v, o, lse, dout, dq, dk, dv and workspace must be non-NULL");
-  const void* bf[] = {q, k, v, o, dout, dq, dk, dv};
-  for (const void* p : bf)
-    if (!aligned16(p)) return fail(OSP_ERR_PARAM, "bf16 tensors must be 16-byte aligned");
-  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(OSP_ERR_PARAM, "lse must be 4-byte aligned");
-  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-    return fail(OSP_ERR_PARAM, "workspace must be 256-byte aligned");
-  const int64_t half = bwd_ws_half(desc, s);
+  st = check_bwd_pointers(q, k, v, o, lse, dout, dq, dk, dv, workspace, sm_scale);
+  if (st) return st;
+  const int64_t half = bwd_ws_half(desc->batch, desc->heads, s.n_tokens);
   if (workspace_bytes < 2 * half)
     return fail(OSP_ERR_PARAM, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
                 (long long)(2 * half));
-  if (isnan(sm_scale) || isinf(sm_scale)) return fail(OSP_ERR_PARAM, "sm_scale must be finite");
-  const int D = desc->head_dim;
-  const double scale = sm_scale > 0.f ? double(sm_scale) : 1.0 / sqrt(double(D));
-  const int32_t groups = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
-  osp::BwdArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.o = static_cast<const uint16_t*>(o);
-  a.dout = static_cast<const uint16_t*>(dout);
-  a.lse = lse;
-  a.neg_delta = static_cast<float*>(workspace);
-  a.neg_lse_s = reinterpret_cast<float*>(static_cast<char*>(workspace) + half);
-  a.dq = static_cast<uint16_t*>(dq);
-  a.dk = static_cast<uint16_t*>(dk);
-  a.dv = static_cast<uint16_t*>(dv);
-  a.sb = s.sb; a.sn = s.sn; a.sh = s.sh;
-  a.osb = s.osb; a.osn = s.osn; a.osh = s.osh;
-  a.batch = desc->batch;
-  a.heads = desc->heads;
-  a.n_tokens = int32_t(s.n_tokens);
-  a.groups = groups;
-  a.seq_len = int32_t(s.n_tokens / groups);
-  a.mode = mode;
-  a.divk = osp::make_fastdiv(uint32_t(groups));
-  a.scale = float(scale);
-  a.scale_log2 = float(scale * 1.4426950408889634);
-  const int kvr = osp::bwd_kv_rows_per_block(D), qr = osp::bwd_q_rows_per_block(D);
-  a.kv_blocks = (a.seq_len + kvr - 1) / kvr;
-  a.q_blocks = (a.seq_len + qr - 1) / qr;
-  if (a.seq_len == 0) return ok();
-  hipError_t e = osp::launch_attn3d_bwd(a, D, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return device_error(e, "attn3d_bwd launch");
+  float* ws = static_cast<float*>(workspace);
+  return enqueue_bwd(desc, s, mode, sparse_k, sm_scale, q, k, v, o, lse, s.n_tokens, dout, dq, dk,
+                     dv, ws, reinterpret_cast<float*>(static_cast<char*>(workspace) + half),
+                     static_cast<hipStream_t>(stream));
+}
+
+osp_status osp_attn3d_packed_bwd_workspace(const osp_attn3d_desc* desc,
+                                           const osp_segment* segments, int32_t n_segments,
+                                           int32_t mode, int32_t sparse_k, int64_t* bytes) {
+  if (!bytes) return fail(OSP_ERR_NULL, "bytes is NULL");
+  int64_t total = 0;
+  osp_status st = check_packed_bwd(desc, segments, n_segments, mode, sparse_k, &total);
+  if (st) return st;
+  *bytes = 2 * bwd_ws_half(desc->batch, desc->heads, total);
+  return ok();
+}
+
+osp_status osp_attn3d_packed_bwd(const osp_attn3d_desc* desc, const osp_segment* segments,
+                                 int32_t n_segments, int32_t mode, int32_t sparse_k,
+                                 float sm_scale, const void* q, const void* k, const void* v,
+                                 const void* o, const float* lse, const void* dout, void* dq,
+                                 void* dk, void* dv, void* workspace, int64_t workspace_bytes,
+                                 void* stream) {
+  int64_t total = 0;
+  osp_status st = check_packed_bwd(desc, segments, n_segments, mode, sparse_k, &total);
+  if (st) return st;
+  st = check_bwd_pointers(q, k, v, o, lse, dout, dq, dk, dv, workspace, sm_scale);
+  if (st) return st;
+  const int64_t half = bwd_ws_half(desc->batch, desc->heads, total);
+  if (workspace_bytes < 2 * half)
+    return fail(OSP_ERR_PARAM, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                (long long)(2 * half));
+  // strides of the packed tensors (contiguous defaults use the total length)
+  osp_attn3d_desc pd = *desc;
+  pd.n_text = 0;
+  pd.grid_t = 1;
+  pd.grid_h = 1;
+  pd.grid_w = int32_t(total);
+  Shape ps;
+  st = check_desc(&pd, true, &ps);
+  if (st) return st;
+  // one backward per segment, in order on the stream; segment s takes its
+  // own B*H*N_s floats of each workspace array
+  float* ws_delta = static_cast<float*>(workspace);
+  float* ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + half);
+  int64_t start = 0, ws_off = 0;
+  for (int32_t i = 0; i < n_segments; ++i) {
+    osp_attn3d_desc d = *desc;
+    d.n_text = segments[i].n_text;
+    d.grid_t = segments[i].grid_t;
+    d.grid_h = segments[i].grid_h;
+    d.grid_w = segments[i].grid_w;
+    Shape s;
+    check_desc(&d, true, &s);
+    s.sb = ps.sb; s.sn = ps.sn; s.sh = ps.sh;
+    s.osb = ps.osb; s.osn = ps.osn; s.osh = ps.osh;
+    const int64_t in = start * s.sn, out = start * s.osn;
+    st = enqueue_bwd(&d, s, mode, sparse_k, sm_scale, static_cast<const uint16_t*>(q) + in,
+                     static_cast<const uint16_t*>(k) + in, static_cast<const uint16_t*>(v) + in,
+                     static_cast<const uint16_t*>(o) + in, lse + start, total,
+                     static_cast<const uint16_t*>(dout) + in, static_cast<uint16_t*>(dq) + out,
+                     static_cast<uint16_t*>(dk) + out, static_cast<uint16_t*>(dv) + out,
+                     ws_delta + ws_off, ws_lse + ws_off, static_cast<hipStream_t>(stream));
+    if (st) return st;
+    start += s.n_tokens;
+    ws_off += int64_t(desc->batch) * desc->heads * s.n_tokens;
+  }
   return ok();
 }
 

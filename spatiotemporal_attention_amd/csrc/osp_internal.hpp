@@ -79,7 +79,8 @@ struct BwdArgs {
   const uint16_t* v;
   const uint16_t* o;
   const uint16_t* dout;
-  const float* lse;             // [B, H, N] natural-log units
+  const float* lse;             // [B, H, lse_ld], token n at lse[(b H + h) lse_ld + n], natural log
+  int64_t lse_ld;
   float* neg_delta;             // workspace [B, H, N]: -sum_d o * dout
   float* neg_lse_s;             // workspace [B, H, N]: -lse / sm_scale
   uint16_t* dq;

@@ -231,6 +231,46 @@ def test_rope3d_packed_errors():
     assert lib.osp_rope3d_packed(ctypes.byref(d), arr, 1, f, ctypes.c_void_p(4100), None) == PARAM
 
 
+def test_packed_bwd_workspace_and_errors_before_launch():
+    lib = osp.lib()
+    d = _desc()
+    f = ctypes.c_void_p(4096)
+    segs = [(3, (2, 3, 4)), (0, (1, 4, 5)), (0, (2, 8, 10))]          # 27 + 20 + 160 tokens
+    half = (2 * 207 * 4 + 255) // 256 * 256
+    assert osp.osp_attn3d_packed_bwd_workspace(d, segs) == 2 * half
+    assert osp.osp_attn3d_packed_bwd_workspace(d, segs[1:], "skiparse_single", 4) == \
+        2 * ((2 * 180 * 4 + 255) // 256 * 256)
+    with pytest.raises(osp.OspError) as e:              # Skiparse with text tokens
+        osp.osp_attn3d_packed_bwd_workspace(d, segs, "skiparse_single", 2)
+    assert e.value.code == UNSUP and "segment 0" in e.value.message
+    with pytest.raises(osp.OspError) as e:              # 20 tokens, k = 3
+        osp.osp_attn3d_packed_bwd_workspace(d, segs[1:], "skiparse_single", 3)
+    assert e.value.code == SHAPE and "segment 0" in e.value.message
+    ws = osp.osp_attn3d_packed_bwd_workspace(d, segs)
+    arr = (osp.OspSegment * 3)()
+    for i, (nt, g) in enumerate(segs):
+        arr[i].n_text = nt
+        arr[i].grid_t, arr[i].grid_h, arr[i].grid_w = g
+
+    def call(segments=arr, n=3, q=f, lse=f, ws_ptr=f, ws_bytes=ws, scale=0.0):
+        return lib.osp_attn3d_packed_bwd(ctypes.byref(d), segments, n, 0, 1, scale, q, f, f, f,
+                                         lse, f, f, f, f, ws_ptr, ws_bytes, None)
+    assert call(segments=None) == NULL
+    assert call(n=0) == PARAM
+    assert call(q=None) == NULL
+    assert call(lse=ctypes.c_void_p(4098)) == PARAM
+    assert call(ws_ptr=ctypes.c_void_p(4096 + 64)) == PARAM
+    assert call(ws_bytes=ws - 4) == PARAM
+    assert b"workspace" in lib.osp_last_error()
+    assert call(scale=float("nan")) == PARAM
+    bad = (osp.OspSegment * 1)()
+    bad[0].grid_t, bad[0].grid_h, bad[0].grid_w = 0, 4, 4
+    assert call(segments=bad, n=1) == PARAM
+    assert b"segment 0" in lib.osp_last_error()
+    assert lib.osp_rope3d_packed_inv(ctypes.byref(d), arr, 3, None, f, None) == NULL
+    assert lib.osp_rope3d_packed_inv(ctypes.byref(d), bad, 1, f, f, None) == PARAM
+
+
 def test_success_clears_last_error():
     lib = osp.lib()
     osp.osp_attn3d_check(_desc())

@@ -4,8 +4,10 @@ the fp64 oracle, through the C ABI: small packs element by element (both
 the short-subsequence and the flash kernel, Skiparse inside the segments,
 fused and unfused K rotation), each segment against a plain forward call on
 its slice (bit for bit: a packed launch runs the same arithmetic per
-segment), more segments than one launch's table holds, and the CogVideoX
-frame pack on sampled rows.  Needs an MI355X."""
+segment), more segments than one launch's table holds, the CogVideoX
+frame pack on sampled rows, and the packed backward through the RoPE
+chain (against plain backward calls per segment and the oracle).  Needs an
+MI355X."""
 import numpy as np
 import pytest
 import torch
@@ -119,3 +121,56 @@ def test_cogvideox_frame_pack_sampled_rows():
     got_l = to_np(lse[:, hs][:, :, rows])
     assert np.abs(got_l - want_l).max() <= LSE_ABS
     assert not torch.isnan(o).any()
+
+
+# ------------------------------------------------------------------ backward
+BWD_REL_L2 = 5e-3        # the backward's bars (tests/test_gpu_bwd.py derives them)
+BWD_REL_L2_ROPE = 8e-3
+BWD_MAX_REL = 2e-2
+
+
+@pytest.mark.parametrize("mode,k,segs", [
+    ("full", 1, [(7, (3, 6, 8)), (0, (1, 5, 5)), (11, (5, 4, 6))]),
+    ("skiparse_single", 2, [(0, (2, 6, 8)), (0, (1, 4, 6)), (0, (3, 8, 10))]),
+])
+def test_packed_bwd_equals_plain_calls_and_oracle(mode, k, segs):
+    """rope3d_packed -> packed forward -> packed backward -> rope3d_packed_inv:
+    each segment's gradients equal a plain backward on its slice bit for bit
+    (a packed backward runs the same launches per segment), and match the
+    oracle's gradients with respect to q and k before the rotation."""
+    split, heads, d = (32, 32, 32), 2, 96
+    n = sum(nt + int(np.prod(g)) for nt, g in segs)
+    shape = (2, n, heads, d)
+    note(f"packed bwd mode={mode} k={k} segments={segs}")
+    cpu, (q, k_, v) = qkv_for(40, shape)
+    do_cpu = workloads.make_dout(40, shape)
+    do = do_cpu.cuda()
+    qr = osp.osp_rope3d_packed(q, segments=segs, rope_split=split)
+    kr = osp.osp_rope3d_packed(k_, segments=segs, rope_split=split)
+    o, lse = osp.osp_attn3d_packed_fwd(qr, kr, v, segments=segs, mode=mode, sparse_k=k,
+                                       rope_split=split, fuse_rope=False, return_lse=True)
+    dq, dk, dv = osp.osp_attn3d_packed_bwd(qr, kr, v, o, lse, do, segments=segs, mode=mode,
+                                           sparse_k=k)
+    start = 0
+    for nt, g in segs:
+        end = start + nt + int(np.prod(g))
+        sl = slice(start, end)
+        pq, pk, pv = osp.osp_attn3d_bwd(qr[:, sl], kr[:, sl], v[:, sl], o[:, sl],
+                                        lse[:, :, sl].contiguous(), do[:, sl], grid=g,
+                                        n_text=nt, mode=mode, sparse_k=k)
+        torch.cuda.synchronize()
+        assert torch.equal(pq, dq[:, sl]) and torch.equal(pk, dk[:, sl]) and torch.equal(pv, dv[:, sl])
+        start = end
+    gq = osp.osp_rope3d_packed_inv(dq, segments=segs, rope_split=split)
+    gk = osp.osp_rope3d_packed_inv(dk, segments=segs, rope_split=split)
+    torch.cuda.synchronize()
+    start = 0
+    for i, (nt, g) in enumerate(segs):
+        end = start + nt + int(np.prod(g))
+        want = oracle.attn3d_bwd(*(workloads.to_f64(t[:, start:end]) for t in (*cpu, do_cpu)),
+                                 grid=g, n_text=nt, mode=mode, sparse_k=k, rope_split=split)
+        for name, got, w in zip(("dq", "dk", "dv"), (gq, gk, dv), want):
+            assert_parity(to_np(got[:, start:end]), w, f"{name} segment {i}",
+                          BWD_MAX_REL * float(np.abs(w).max()),
+                          BWD_REL_L2 if name == "dv" else BWD_REL_L2_ROPE)
+        start = end
