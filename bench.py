@@ -184,6 +184,32 @@ def main():
             osp.osp_rope3d_packed(kp, segments=segs, rope_split=wlc.rope_split, out=kp_rot)
             osp.osp_attn3d_packed_fwd(qp, kp_rot, vp, segments=segs, rope_split=wlc.rope_split,
                                       fuse_rope="q", out=op)
+
+        def packed_bwd_setup():
+            # the backward of the same pack: q and k rotated, o and lse from
+            # one forward, a seeded dO; one call is the packed backward plus
+            # the two packed RoPE transposes
+            qr = osp.osp_rope3d_packed(qp, segments=segs, rope_split=wlc.rope_split)
+            kr = osp.osp_rope3d_packed(kp, segments=segs, rope_split=wlc.rope_split)
+            o2, lse2 = osp.osp_attn3d_packed_fwd(qr, kr, vp, segments=segs,
+                                                 rope_split=wlc.rope_split, fuse_rope=False,
+                                                 return_lse=True)
+            dop = workloads.make_dout(pk["seed"], pshape).to(dev)
+            grads = tuple(torch.empty_like(qp) for _ in range(3))
+            desc = osp.make_desc(batch=1, n_text=0, grid=(1, 1, sum(lens)), heads=wlc.heads,
+                                 head_dim=wlc.head_dim, rope_split=wlc.rope_split)
+            ws = torch.empty(osp.osp_attn3d_packed_bwd_workspace(desc, segs), dtype=torch.uint8,
+                             device=dev)
+
+            def runb():
+                osp.osp_attn3d_packed_bwd(qr, kr, vp, o2, lse2, dop, segments=segs, dq=grads[0],
+                                          dk=grads[1], dv=grads[2], workspace=ws)
+                osp.osp_rope3d_packed_inv(grads[0], segments=segs, rope_split=wlc.rope_split,
+                                          out=grads[0])
+                osp.osp_rope3d_packed_inv(grads[1], segments=segs, rope_split=wlc.rope_split,
+                                          out=grads[1])
+            return runb
+        runp.bwd_setup = packed_bwd_setup
         return runp, segs, lens, wlc
 
     if args.profile:
@@ -294,6 +320,21 @@ def main():
                   "flop_per_call": f_pack,
                   "launches": f"rope3d of K per segment ({len(segs)}), then one flash "
                               "launch over the segment table, Q rotated in its loader"}
+        runb = runp.bwd_setup()
+        for _ in range(args.warmup):
+            runb()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(npk):
+            runb()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        pb_ms = t0.elapsed_time(t1) / npk
+        tfb = 2.5 * f_pack / (pb_ms * 1e-3) / 1e12
+        packed["backward"] = {"ms_per_call": round(pb_ms, 4), "tflops": round(tfb, 2),
+                              "frac_of_peak": round(tfb / PEAK_BF16_TFLOPS, 4),
+                              "launches": "three backward kernels per segment, then the "
+                                          "packed RoPE transpose of dq and dk"}
 
     bwd = None
     if not args.no_backward:
