@@ -196,10 +196,11 @@ def osp_attn3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid,
                    return_lse: bool = False):
     """Attention forward over [B, N, H, D] bf16 q, k, v on the GPU.
 
-    fuse_rope: True (rotate Q and K in the loaders), False (both already
-    rotated), "q" or "k" (rotate only that one in its loader).  Rotating K
-    in the loader repeats the rotation for every query tile; where a rotated
-    copy of K fits, osp_rope3d on K and fuse_rope="q" is faster.
+    fuse_rope: True (q and k unrotated: k is rotated by osp_rope3d into a
+    temporary of k's strides, q in the attention loader), False (both
+    already rotated), "q" or "k" (only that one unrotated, rotated in its
+    loader), "qk" (both rotated in the loaders, no temporary; slower, since
+    every query tile rotates the same K again).  All give the same bits.
     Returns o (and lse [B, H, N] fp32 when return_lse or lse is given)."""
     b, n, h, d = q.shape
     st = _bnhd(q, "q")
@@ -217,6 +218,9 @@ def osp_attn3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid,
     desc = make_desc(batch=b, n_text=n_text, grid=grid, heads=h, head_dim=d,
                      rope_split=rope_split, theta=theta, pos_offset=pos_offset,
                      strides=st, ostrides=_bnhd(out, "out"))
+    if fuse_rope is True:
+        k = osp_rope3d(k, grid=grid, n_text=n_text, rope_split=rope_split, theta=theta,
+                       pos_offset=pos_offset, out=_like_strided(k))
     _check(lib().osp_attn3d_fwd(
         ctypes.byref(desc), _mode(mode), int(sparse_k),
         float(sm_scale) if sm_scale is not None else 0.0, _flags(fuse_rope),
@@ -227,11 +231,18 @@ def osp_attn3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid,
 
 
 def _flags(fuse_rope) -> int:
+    # True: K is rotated by its own pass before the call, Q in the loader
     if fuse_rope is True:
-        return OSP_FUSE_ROPE
+        return OSP_FUSE_ROPE_Q
     if fuse_rope is False or fuse_rope is None:
         return 0
     return {"q": OSP_FUSE_ROPE_Q, "k": OSP_FUSE_ROPE_K, "qk": OSP_FUSE_ROPE}[fuse_rope]
+
+
+def _like_strided(t: torch.Tensor) -> torch.Tensor:
+    """An uninitialised tensor with t's shape and strides (q, k and v of one
+    call must share strides)."""
+    return torch.empty_strided(t.size(), t.stride(), dtype=t.dtype, device=t.device)
 
 
 def _segments(segments, n):
@@ -282,7 +293,9 @@ def osp_attn3d_packed_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, 
                           out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                           return_lse: bool = False):
     """Attention forward over a packed [B, N, H, D] sequence of several
-    videos; ``segments`` lists (n_text, (T, H, W)) in order along N."""
+    videos; ``segments`` lists (n_text, (T, H, W)) in order along N.
+    fuse_rope as in osp_attn3d_fwd (True rotates k with osp_rope3d_packed
+    into a temporary first)."""
     b, n, h, d = q.shape
     st = _bnhd(q, "q")
     if _bnhd(k, "k") != st or _bnhd(v, "v") != st or k.shape != q.shape or v.shape != q.shape:
@@ -298,6 +311,9 @@ def osp_attn3d_packed_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, 
     desc = make_desc(batch=b, n_text=0, grid=(1, 1, n), heads=h, head_dim=d,
                      rope_split=rope_split, theta=theta, pos_offset=pos_offset, strides=st,
                      ostrides=_bnhd(out, "out"))
+    if fuse_rope is True:
+        k = osp_rope3d_packed(k, segments=segments, rope_split=rope_split, theta=theta,
+                              pos_offset=pos_offset, out=_like_strided(k))
     _check(lib().osp_attn3d_packed_fwd(
         ctypes.byref(desc), segs, len(segments), _mode(mode), int(sparse_k),
         float(sm_scale) if sm_scale is not None else 0.0, _flags(fuse_rope),

@@ -1,7 +1,8 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times (one osp_attn3d_fwd call with fused RoPE over the whole
-tensor), checked against the fp64 oracle on seeded sampled query rows.
-Needs an MI355X."""
+benchmark times (K rotated by osp_rope3d, then one osp_attn3d_fwd call
+that rotates Q in its loader, over the whole tensor; and once with K
+rotated in the loader too), checked against the fp64 oracle on seeded
+sampled query rows.  Needs an MI355X."""
 import math
 
 import numpy as np
@@ -17,18 +18,19 @@ pytestmark = pytest.mark.gpu
 SAMPLE = 256
 
 
-def run_sampled(name, mode, sparse_k, variant="as-specified"):
+def run_sampled(name, mode, sparse_k, variant="as-specified", fuse_rope=True):
     wl = workloads.WORKLOADS[name]
     grid = grid_of(wl)
     n = wl.n_text + int(np.prod(grid))
     shape = (wl.batch, n, wl.heads, wl.head_dim)
     scale = wl.input_scale if variant == "as-specified" else None
     seed = wl.seed if variant == "as-specified" else (wl.seed, 7)
-    note(f"full-size {name} grid={grid} shape={shape} mode={mode} k={sparse_k} variant={variant}")
+    note(f"full-size {name} grid={grid} shape={shape} mode={mode} k={sparse_k} variant={variant} "
+         f"fuse={fuse_rope}")
     cpu, (q, k, v) = qkv_for(seed, shape, scale)
     o, lse = osp.osp_attn3d_fwd(q, k, v, grid=grid, n_text=wl.n_text, mode=mode,
                                 sparse_k=sparse_k, rope_split=wl.rope_split, theta=wl.theta,
-                                return_lse=True)
+                                fuse_rope=fuse_rope, return_lse=True)
     torch.cuda.synchronize()
     rows = workloads.sample_rows(wl.seed, n, SAMPLE)
     want_o, want_l = oracle_attn(cpu, grid=grid, n_text=wl.n_text, mode=mode, sparse_k=sparse_k,
@@ -39,6 +41,10 @@ def run_sampled(name, mode, sparse_k, variant="as-specified"):
     assert_parity(got_o, want_o, f"{name} {mode} k={sparse_k} {variant} ({len(rows)} rows)")
     assert np.abs(got_l - want_l).max() <= LSE_ABS
     assert not torch.isnan(o).any()
+
+
+def test_osp480_full_k_rotated_in_loader():
+    run_sampled("osp480", "full", 1, fuse_rope="qk")
 
 
 @pytest.mark.parametrize("variant", ["as-specified", "unscaled"])

@@ -29,7 +29,7 @@ def _gpu():
 
 
 def _packed_case(seed, segments, *, heads, head_dim, split, mode="full", sparse_k=1, batch=1,
-                 fuse_rope=True, tag=""):
+                 fuse_rope="qk", tag=""):
     n = sum(nt + int(np.prod(g)) for nt, g in segments)
     shape = (batch, n, heads, head_dim)
     note(f"packed {tag} seed={seed} shape={shape} segments={segments} mode={mode} k={sparse_k}")

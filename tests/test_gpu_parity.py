@@ -27,7 +27,7 @@ def _gpu():
 
 def run_case(seed, *, grid, n_text, heads, head_dim, rope_split, mode="full", sparse_k=1,
              scale=None, q_mult=None, theta=1e4, sm_scale=None, pos_offset=(0, 0, 0),
-             batch=1, lse=True, fuse_rope=True, tag="", tol=1.0):
+             batch=1, lse=True, fuse_rope="qk", tag="", tol=1.0):
     n = n_text + int(np.prod(grid))
     shape = (batch, n, heads, head_dim)
     note(f"case {tag} seed={seed} shape={shape} grid={grid} n_text={n_text} mode={mode} "
@@ -188,6 +188,8 @@ def test_fused_equals_unfused_bitwise(args):
     a, la = run_case(16, **args, tag="fused")
     b, lb = run_case(16, **args, fuse_rope="q", tag="fuse=q")
     assert torch.equal(a, b) and torch.equal(la, lb)
+    c, lc = run_case(16, **args, fuse_rope=True, tag="fuse=True")   # K by its own pass
+    assert torch.equal(c, b) and torch.equal(lc, lb)
     a, la = run_case(16, **args, fuse_rope="k", tag="fuse=k")
     b, lb = run_case(16, **args, fuse_rope=False, tag="fuse=none")
     assert torch.equal(a, b) and torch.equal(la, lb)
