@@ -48,8 +48,9 @@ constexpr int kBwdRows = 64;         // rows of one streamed LDS tile
 constexpr int kPrepThreads = 256;
 
 // Geometry of the blocked kernels.  Both stream 64-row tiles through LDS,
-// each loaded by 4 waves (the dQ kernel's 4 waves load K and V; in the
-// dK/dV kernel the 4 waves of each role load their tensor).
+// each loaded by 4 waves (in the dQ kernel waves 0-3 load K and 4-7 load V,
+// or with 4 waves each loads both; in the dK/dV kernel the 4 waves of each
+// role load their tensor).
 template <int D> struct BwdCfg {
   static constexpr int KCH = D / 8;                       // 16-byte chunks per row
   static constexpr int TILE = kBwdRows * D;               // bf16 elements of a tile
@@ -489,7 +490,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ.
+// 3. dQ.  Each wave owns 32 queries: Q and dO rows in registers, the
+// row's -lse/scale and -delta from the workspace.  Per streamed tile of 64
+// keys (K and V through LDS, double-buffered): S^T and dP^T - delta per
+// 32-key block (C operand layout: keys are rows, the lane's query the
+// column), P = exp2 of one fma, dS^T = P o (dP^T - delta) packed to bf16,
+// and dQ^T += K^T dS^T with K^T read transposed.
 template <int D>
 __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
