@@ -275,3 +275,32 @@ def test_success_clears_last_error():
     lib = osp.lib()
     osp.osp_attn3d_check(_desc())
     assert lib.osp_last_error() == b""
+
+
+def test_last_error_is_per_thread():
+    # the error text is thread-local: threads failing different calls at the
+    # same time each read back their own message
+    import threading
+    lib = osp.lib()
+    out = (ctypes.c_int32 * 3)()
+    failures = []
+
+    def grid_errors():
+        for _ in range(300):
+            if lib.osp_latent_grid(0, 480, 640, 4, 8, 1, 2, out) == OK or \
+                    b"sizes and factors" not in lib.osp_last_error():
+                failures.append(("grid", lib.osp_last_error()))
+
+    def index_errors():
+        perm = (ctypes.c_int32 * 10)()
+        for _ in range(300):
+            if lib.osp_skiparse_index(1, 3, 10, perm, None, 0, None) == OK or \
+                    b"divisible" not in lib.osp_last_error():
+                failures.append(("index", lib.osp_last_error()))
+
+    threads = [threading.Thread(target=f) for f in (grid_errors, index_errors) * 2]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not failures, failures[:3]
