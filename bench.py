@@ -333,8 +333,9 @@ def main():
         tfb = 2.5 * f_pack / (pb_ms * 1e-3) / 1e12
         packed["backward"] = {"ms_per_call": round(pb_ms, 4), "tflops": round(tfb, 2),
                               "frac_of_peak": round(tfb / PEAK_BF16_TFLOPS, 4),
-                              "launches": "three backward kernels per segment, then the "
-                                          "packed RoPE transpose of dq and dk"}
+                              "launches": "one workspace pass, dK/dV and dQ launches over "
+                                          "the segment table, then the packed RoPE transpose "
+                                          "of dq and dk"}
 
     bwd = None
     if not args.no_backward:

@@ -273,10 +273,10 @@ osp_status osp_attn3d_packed_bwd_workspace(const osp_attn3d_desc* desc,
    them back).  lse: [B, H, N] fp32 contiguous over the packed N, from
    osp_attn3d_packed_fwd.  workspace: at least
    osp_attn3d_packed_bwd_workspace() bytes, 256-byte aligned, owned by the
-   caller; segment s uses its own part of it.  Every segment is checked
-   before anything is enqueued; the segments then run one backward each
-   (three launches), in order, on the stream.  Other rules as in
-   osp_attn3d_bwd. */
+   caller.  Every segment is checked before anything is enqueued; then one
+   workspace pass runs over all tokens, and dK/dV and dQ launches of up to
+   16 segments each, whose workgroups find their segment in a table.
+   Other rules as in osp_attn3d_bwd. */
 osp_status osp_attn3d_packed_bwd(const osp_attn3d_desc* desc,
                                  const osp_segment* segments,
                                  int32_t n_segments, int32_t mode,

@@ -109,8 +109,9 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdArgs a,
       acc[t] = fmaf(bf16hi(xs[t]), bf16hi(ys[t]), acc[t]);
     }
   }
-  a.neg_delta[idx] = -((acc[0] + acc[1]) + (acc[2] + acc[3]));
-  a.neg_lse_s[idx] = -a.lse[int64_t(bh) * a.lse_ld + n] / a.scale;
+  const int64_t w = int64_t(bh) * a.ws_ld + n;
+  a.neg_delta[w] = -((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  a.neg_lse_s[w] = -a.lse[int64_t(bh) * a.lse_ld + n] / a.scale;
 }
 
 // ---------------------------------------------------------------------------
@@ -118,18 +119,47 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdArgs a,
 
 // Which (b, h, subsequence j, row block) a workgroup takes: consecutive
 // row blocks of one (b, h, j) share their streamed tiles and stay on one
-// XCD (workgroups are dealt to the 8 XCDs round robin).
+// XCD (workgroups are dealt to the 8 XCDs round robin).  In a packed
+// launch the workgroup first finds its segment (every index a constant, no
+// dynamic indexing into the argument block); each segment starts at a
+// multiple of 8 workgroups and is spread over the 8 XCDs on its own, and
+// its padding workgroups are not live.
 struct BwdBlock {
   uint32_t b, h, j, blk;
+  int L;                        // rows of a subsequence
+  int64_t tok0;                 // first token of the sequence
+  bool live;
 };
-__device__ __forceinline__ BwdBlock bwd_block(const BwdArgs& a, uint32_t blocks_per_seq) {
-  const uint32_t total = gridDim.x;
-  const uint32_t t8 = total & ~7u;
+template <bool PACKED, bool KV>
+__device__ __forceinline__ BwdBlock bwd_block(const BwdArgs& a) {
   const uint32_t x = blockIdx.x;
-  uint32_t u = (x < t8) ? (x & 7u) * (t8 >> 3) + (x >> 3) : x;
   BwdBlock r;
-  r.blk = u % blocks_per_seq;
-  u /= blocks_per_seq;
+  uint32_t u, blocks;
+  r.live = true;
+  if constexpr (PACKED) {
+    BwdPackSeg ps = a.pack[0];
+#pragma unroll
+    for (int sg = 1; sg < kMaxPackSegs; ++sg)
+      if (sg < a.n_pack && x >= uint32_t(KV ? a.pack[sg].kv_tile0 : a.pack[sg].q_tile0))
+        ps = a.pack[sg];
+    const uint32_t tiles = uint32_t(KV ? ps.kv_tiles : ps.q_tiles);
+    const uint32_t xs = x - uint32_t(KV ? ps.kv_tile0 : ps.q_tile0);
+    u = (xs & 7u) * ((tiles + 7u) >> 3) + (xs >> 3);
+    r.live = u < tiles;
+    if (!r.live) u = 0;
+    blocks = uint32_t(KV ? ps.kv_blocks : ps.q_blocks);
+    r.L = ps.seq_len;
+    r.tok0 = ps.start;
+  } else {
+    const uint32_t total = gridDim.x;
+    const uint32_t t8 = total & ~7u;
+    u = (x < t8) ? (x & 7u) * (t8 >> 3) + (x >> 3) : x;
+    blocks = uint32_t(KV ? a.kv_blocks : a.q_blocks);
+    r.L = a.seq_len;
+    r.tok0 = 0;
+  }
+  r.blk = u % blocks;
+  u /= blocks;
   r.j = u % uint32_t(a.groups);
   u /= uint32_t(a.groups);
   r.h = u % uint32_t(a.heads);
@@ -222,7 +252,7 @@ __device__ __forceinline__ void load_row_operand(const uint16_t* row, bool valid
 // spills some loop-invariant values, which still runs 10% faster than
 // KB = 1 (forming them again in every phase instead costs more); head_dim
 // 128 takes KB = 1.
-template <int D>
+template <int D, bool PACKED>
 __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int KCH = C::KCH, KB = C::KB;
@@ -263,13 +293,14 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
-  const BwdBlock wb = bwd_block(a, uint32_t(a.kv_blocks));
+  const BwdBlock wb = bwd_block<PACKED, true>(a);
+  if (!wb.live) return;              // padding of a packed launch, before any barrier
   const int mode = a.mode;
   const FastDiv divk = a.divk;
-  const int L = a.seq_len;
+  const int L = wb.L;
   const int64_t sn = a.sn;
-  const int64_t in_off = int64_t(wb.b) * a.sb + int64_t(wb.h) * a.sh;
-  const int64_t bhn = (int64_t(wb.b) * a.heads + wb.h) * a.n_tokens;
+  const int64_t in_off = int64_t(wb.b) * a.sb + int64_t(wb.h) * a.sh + wb.tok0 * sn;
+  const int64_t bhn = (int64_t(wb.b) * a.heads + wb.h) * a.ws_ld + wb.tok0;
   const float c2 = a.scale_log2;
 
   // ---- this lane's keys (one per key block): K rows (P wave) or V rows
@@ -483,7 +514,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
     if (kval[kb]) {
-      const int64_t out = int64_t(wb.b) * a.osb + int64_t(wb.h) * a.osh + int64_t(ktok[kb]) * a.osn;
+      const int64_t out = int64_t(wb.b) * a.osb + int64_t(wb.h) * a.osh +
+                          (wb.tok0 + int64_t(ktok[kb])) * a.osn;
       if (pw) store_rows_t<D>(a.dv + out, acc[kb], 1.0f, g);
       else store_rows_t<D>(a.dk + out, acc[kb], a.scale, g);
     }
@@ -496,7 +528,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
 // 32-key block (C operand layout: keys are rows, the lane's query the
 // column), P = exp2 of one fma, dS^T = P o (dP^T - delta) packed to bf16,
 // and dQ^T += K^T dS^T with K^T read transposed.
-template <int D>
+template <int D, bool PACKED>
 __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int NW = C::NW_Q;
@@ -518,13 +550,14 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
-  const BwdBlock wb = bwd_block(a, uint32_t(a.q_blocks));
+  const BwdBlock wb = bwd_block<PACKED, false>(a);
+  if (!wb.live) return;              // padding of a packed launch, before any barrier
   const int mode = a.mode;
   const FastDiv divk = a.divk;
-  const int L = a.seq_len;
+  const int L = wb.L;
   const int64_t sn = a.sn;
-  const int64_t in_off = int64_t(wb.b) * a.sb + int64_t(wb.h) * a.sh;
-  const int64_t bhn = (int64_t(wb.b) * a.heads + wb.h) * a.n_tokens;
+  const int64_t in_off = int64_t(wb.b) * a.sb + int64_t(wb.h) * a.sh + wb.tok0 * sn;
+  const int64_t bhn = (int64_t(wb.b) * a.heads + wb.h) * a.ws_ld + wb.tok0;
   const float c2 = a.scale_log2;
 
   // ---- this lane's query: Q and dO rows as B operands, its two workspace values
@@ -654,28 +687,44 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
   }
 
   if (qvalid) {
-    const int64_t out = int64_t(wb.b) * a.osb + int64_t(wb.h) * a.osh + int64_t(qi) * a.osn;
+    const int64_t out = int64_t(wb.b) * a.osb + int64_t(wb.h) * a.osh + (wb.tok0 + int64_t(qi)) * a.osn;
     store_rows_t<D>(a.dq + out, dq, a.scale, g);
   }
 }
 
 // ---------------------------------------------------------------------------
 template <int D>
-static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
-  using C = BwdCfg<D>;
+static hipError_t launch_prep_d(const BwdArgs& a, hipStream_t s) {
   const uint64_t rows = uint64_t(a.batch) * uint64_t(a.heads) * uint64_t(a.n_tokens);
   const uint32_t prep_blocks = uint32_t((rows + kPrepThreads - 1) / kPrepThreads);
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(prep_blocks), dim3(kPrepThreads), 0, s, a,
                      uint32_t(rows), make_fastdiv(uint32_t(a.n_tokens)),
                      make_fastdiv(uint32_t(a.heads)));
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
+  using C = BwdCfg<D>;
+  hipError_t e = launch_prep_d<D>(a, s);
   if (e != hipSuccess) return e;
   const uint32_t seqs = uint32_t(a.batch) * uint32_t(a.heads) * uint32_t(a.groups);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(seqs * uint32_t(a.kv_blocks)), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(seqs * uint32_t(a.kv_blocks)), dim3(512), 0,
+                     s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(seqs * uint32_t(a.q_blocks)), dim3(C::NW_Q * 64),
-                     0, s, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(seqs * uint32_t(a.q_blocks)),
+                     dim3(C::NW_Q * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_packed_d(const BwdArgs& pa, int kv_grid, int q_grid, hipStream_t s) {
+  using C = BwdCfg<D>;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(kv_grid), dim3(512), 0, s, pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(q_grid), dim3(C::NW_Q * 64), 0, s, pa);
   return hipGetLastError();
 }
 
@@ -684,6 +733,25 @@ hipError_t launch_attn3d_bwd(const BwdArgs& a, int head_dim, hipStream_t s) {
     case 64: return launch_bwd_d<64>(a, s);
     case 96: return launch_bwd_d<96>(a, s);
     case 128: return launch_bwd_d<128>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn3d_bwd_prep(const BwdArgs& a, int head_dim, hipStream_t s) {
+  switch (head_dim) {
+    case 64: return launch_prep_d<64>(a, s);
+    case 96: return launch_prep_d<96>(a, s);
+    case 128: return launch_prep_d<128>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn3d_bwd_packed(const BwdArgs& pa, int kv_grid, int q_grid, int head_dim,
+                                    hipStream_t s) {
+  switch (head_dim) {
+    case 64: return launch_packed_d<64>(pa, kv_grid, q_grid, s);
+    case 96: return launch_packed_d<96>(pa, kv_grid, q_grid, s);
+    case 128: return launch_packed_d<128>(pa, kv_grid, q_grid, s);
   }
   return hipErrorInvalidValue;
 }

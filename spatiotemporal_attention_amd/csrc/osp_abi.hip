@@ -247,7 +247,7 @@ osp_status check_packed_bwd(const osp_attn3d_desc* desc, const osp_segment* segm
   if (!desc) return fail(OSP_ERR_NULL, "desc is NULL");
   if (!segments) return fail(OSP_ERR_NULL, "segments is NULL");
   if (n_segments < 1) return fail(OSP_ERR_PARAM, "n_segments (%d) must be >= 1", n_segments);
-  int64_t n = 0;
+  int64_t n = 0, grid = 0;
   for (int32_t i = 0; i < n_segments; ++i) {
     osp_attn3d_desc d = *desc;
     d.n_text = segments[i].n_text;
@@ -263,6 +263,12 @@ osp_status check_packed_bwd(const osp_attn3d_desc* desc, const osp_segment* segm
     n += s.n_tokens;
     if (n > 0x7fffffffLL || int64_t(desc->batch) * desc->heads * n > 0x7fffffffLL)
       return fail(OSP_ERR_SHAPE, "packed batch*heads*N exceeds 2^31-1");
+    // workgroups of one packed launch (at most every segment in it)
+    const int64_t groups = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
+    const int64_t rb = std::min(osp::bwd_kv_rows_per_block(d.head_dim),
+                                osp::bwd_q_rows_per_block(d.head_dim));
+    grid += (int64_t(d.batch) * d.heads * groups * ((s.n_tokens / groups + rb - 1) / rb) + 7) / 8 * 8;
+    if (grid > 0x7fffffffLL) return fail(OSP_ERR_SHAPE, "too many workgroups in the packed sequence");
   }
   *total = n;
   return OSP_OK;
@@ -291,12 +297,14 @@ osp_status check_bwd_pointers(const void* q, const void* k, const void* v, const
 
 // The three backward launches for one (checked) sequence: tensors at the
 // given bases with the strides of s, lse rows lse_ld apart, and the two
-// workspace arrays of B*H*N_s floats each.
+// workspace arrays of B*H*N_s floats each.  launch == false only fills
+// *out with the arguments.
 osp_status enqueue_bwd(const osp_attn3d_desc* desc, const Shape& s, int32_t mode,
                        int32_t sparse_k, float sm_scale, const void* q, const void* k,
                        const void* v, const void* o, const float* lse, int64_t lse_ld,
                        const void* dout, void* dq, void* dk, void* dv, float* ws_delta,
-                       float* ws_lse, hipStream_t stream) {
+                       float* ws_lse, hipStream_t stream, bool launch = true,
+                       osp::BwdArgs* out = nullptr) {
   const int D = desc->head_dim;
   const double scale = sm_scale > 0.f ? double(sm_scale) : 1.0 / sqrt(double(D));
   const int32_t groups = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
@@ -327,7 +335,12 @@ osp_status enqueue_bwd(const osp_attn3d_desc* desc, const Shape& s, int32_t mode
   const int kvr = osp::bwd_kv_rows_per_block(D), qr = osp::bwd_q_rows_per_block(D);
   a.kv_blocks = (a.seq_len + kvr - 1) / kvr;
   a.q_blocks = (a.seq_len + qr - 1) / qr;
-  if (a.seq_len == 0) return OSP_OK;
+  a.ws_ld = s.n_tokens;
+  a.n_pack = 0;
+  if (a.seq_len == 0 || !launch) {
+    if (out) *out = a;
+    return OSP_OK;
+  }
   hipError_t e = osp::launch_attn3d_bwd(a, D, stream);
   if (e != hipSuccess) return device_error(e, "attn3d_bwd launch");
   return OSP_OK;
@@ -679,31 +692,59 @@ osp_status osp_attn3d_packed_bwd(const osp_attn3d_desc* desc, const osp_segment*
   Shape ps;
   st = check_desc(&pd, true, &ps);
   if (st) return st;
-  // one backward per segment, in order on the stream; segment s takes its
-  // own B*H*N_s floats of each workspace array
+  // The workspace pass once over all tokens ([B, H, N] arrays over the
+  // packed N), then dK/dV and dQ launches of up to kMaxPackSegs segments
+  // each, whose workgroups look their segment up in a table, longest
+  // segment first (so that the shorter ones fill the tail).
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
   float* ws_delta = static_cast<float*>(workspace);
   float* ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + half);
-  int64_t start = 0, ws_off = 0;
+  osp::BwdArgs base;
+  st = enqueue_bwd(&pd, ps, OSP_MODE_FULL, 1, sm_scale, q, k, v, o, lse, total, dout, dq, dk, dv,
+                   ws_delta, ws_lse, hs, false, &base);
+  if (st) return st;
+  hipError_t e = osp::launch_attn3d_bwd_prep(base, desc->head_dim, hs);
+  if (e != hipSuccess) return device_error(e, "attn3d_bwd prep launch");
+  const int32_t groups = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
+  base.mode = mode;
+  base.groups = groups;
+  base.divk = osp::make_fastdiv(uint32_t(groups));
+  const int kvr = osp::bwd_kv_rows_per_block(desc->head_dim);
+  const int qr = osp::bwd_q_rows_per_block(desc->head_dim);
+  std::vector<osp::BwdPackSeg> segs;
+  int64_t start = 0;
   for (int32_t i = 0; i < n_segments; ++i) {
-    osp_attn3d_desc d = *desc;
-    d.n_text = segments[i].n_text;
-    d.grid_t = segments[i].grid_t;
-    d.grid_h = segments[i].grid_h;
-    d.grid_w = segments[i].grid_w;
-    Shape s;
-    check_desc(&d, true, &s);
-    s.sb = ps.sb; s.sn = ps.sn; s.sh = ps.sh;
-    s.osb = ps.osb; s.osn = ps.osn; s.osh = ps.osh;
-    const int64_t in = start * s.sn, out = start * s.osn;
-    st = enqueue_bwd(&d, s, mode, sparse_k, sm_scale, static_cast<const uint16_t*>(q) + in,
-                     static_cast<const uint16_t*>(k) + in, static_cast<const uint16_t*>(v) + in,
-                     static_cast<const uint16_t*>(o) + in, lse + start, total,
-                     static_cast<const uint16_t*>(dout) + in, static_cast<uint16_t*>(dq) + out,
-                     static_cast<uint16_t*>(dk) + out, static_cast<uint16_t*>(dv) + out,
-                     ws_delta + ws_off, ws_lse + ws_off, static_cast<hipStream_t>(stream));
-    if (st) return st;
-    start += s.n_tokens;
-    ws_off += int64_t(desc->batch) * desc->heads * s.n_tokens;
+    const int64_t n = int64_t(segments[i].n_text) +
+                      int64_t(segments[i].grid_t) * segments[i].grid_h * segments[i].grid_w;
+    osp::BwdPackSeg g;
+    g.start = int32_t(start);
+    g.seq_len = int32_t(n / groups);
+    g.kv_blocks = (g.seq_len + kvr - 1) / kvr;
+    g.q_blocks = (g.seq_len + qr - 1) / qr;
+    const int32_t seqs = desc->batch * desc->heads * groups;
+    g.kv_tiles = seqs * g.kv_blocks;
+    g.q_tiles = seqs * g.q_blocks;
+    segs.push_back(g);
+    start += n;
+  }
+  std::stable_sort(segs.begin(), segs.end(), [](const osp::BwdPackSeg& x,
+                                                const osp::BwdPackSeg& y) {
+    return x.seq_len > y.seq_len;
+  });
+  for (size_t i0 = 0; i0 < segs.size(); i0 += osp::kMaxPackSegs) {
+    osp::BwdArgs pa = base;
+    pa.n_pack = 0;
+    int64_t kv_grid = 0, q_grid = 0;
+    for (size_t i = i0; i < segs.size() && i < i0 + osp::kMaxPackSegs; ++i) {
+      osp::BwdPackSeg g = segs[i];
+      g.kv_tile0 = int32_t(kv_grid);
+      g.q_tile0 = int32_t(q_grid);
+      kv_grid += (int64_t(g.kv_tiles) + 7) / 8 * 8;
+      q_grid += (int64_t(g.q_tiles) + 7) / 8 * 8;
+      pa.pack[pa.n_pack++] = g;
+    }
+    e = osp::launch_attn3d_bwd_packed(pa, int(kv_grid), int(q_grid), desc->head_dim, hs);
+    if (e != hipSuccess) return device_error(e, "attn3d_packed_bwd launch");
   }
   return ok();
 }

@@ -73,6 +73,15 @@ hipError_t launch_rope3d(const RopeArgs& a, hipStream_t s);
 
 // One attention backward call, after validation.  q, k, v, o, dout are
 // read with the input strides, dq, dk, dv written with the output strides.
+// One segment of a packed backward launch: its dK/dV and dQ workgroups
+// start at kv_tile0 / q_tile0 of their launches (multiples of 8) and
+// number kv_tiles / q_tiles (B*H*groups*blocks, before padding).
+struct BwdPackSeg {
+  int32_t kv_tile0, kv_tiles, q_tile0, q_tiles;
+  int32_t start;                // first token of the segment in the packed sequence
+  int32_t seq_len, kv_blocks, q_blocks;
+};
+
 struct BwdArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -94,6 +103,9 @@ struct BwdArgs {
   FastDiv divk;
   float scale;                  // sm_scale
   float scale_log2;             // sm_scale * log2(e)
+  int64_t ws_ld;                // token stride of a (b, h) row of the workspace arrays
+  int32_t n_pack;               // packed launches: segments in pack[]
+  BwdPackSeg pack[kMaxPackSegs];
 };
 
 // Rows handled by one workgroup of the dK/dV and of the dQ kernel, and the
@@ -103,6 +115,12 @@ int bwd_q_rows_per_block(int head_dim);
 int bwd_tile_rows(int head_dim);
 
 hipError_t launch_attn3d_bwd(const BwdArgs& a, int head_dim, hipStream_t s);
+// The packed backward: the workspace pass over every token (a as for a
+// plain call over the packed length), then dK/dV and dQ launches whose
+// workgroups find their segment in pa.pack (pa.n_pack <= kMaxPackSegs).
+hipError_t launch_attn3d_bwd_prep(const BwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_attn3d_bwd_packed(const BwdArgs& pa, int kv_grid, int q_grid, int head_dim,
+                                    hipStream_t s);
 
 hipError_t launch_skiparse_index(int32_t mode, int32_t k, int32_t n, int32_t* perm,
                                  int32_t* inv, hipStream_t s);
