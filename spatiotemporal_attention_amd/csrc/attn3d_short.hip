@@ -212,8 +212,41 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(blk, v_off, db), pb[kb][hh],
                                                           o[db], 0, 0, 0);
       }
-    // O / l at the query's token row
     const int r = 32 * qb + l32;
+    if constexpr (NB == 1) {
+      // One block: the wave's V tile is free once its MFMAs have read it.
+      // O / l goes there row-major (bf16), then each row is stored as 16-byte
+      // chunks by consecutive lanes (12 lanes per 192-byte row at D=96)
+      // instead of 8-byte pieces of 32 rows per instruction.
+      const float inv = 1.0f / lt;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const uint32_t w0 = pack_bf16(o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv);
+          const uint32_t w1 = pack_bf16(o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv);
+          *reinterpret_cast<uint2*>(vs + l32 * D + 32 * db + 8 * r4 + 4 * g) = make_uint2(w0, w1);
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's own stores landed
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        const int idx = lane + 64 * e;
+        const int row = idx / KCH, col = idx % KCH;
+        if (row < L) {
+          const uint32_t i = skiparse_token(mode, uint32_t(row), j, divk, uint32_t(L));
+          *reinterpret_cast<uint4*>(og + int64_t(i) * a.osn + 8 * col) =
+              *reinterpret_cast<const uint4*>(vs + row * D + 8 * col);
+        }
+      }
+      if (r < L && a.lse && g == 0) {
+        const uint32_t i = skiparse_token(mode, uint32_t(r), j, divk, uint32_t(L));
+        a.lse[(int64_t(b) * a.heads + h) * a.lse_ld + i] = (m + __log2f(lt)) * 0.69314718055994530942f;
+      }
+      continue;
+    }
+    // O / l at the query's token row
     if (r < L) {
       const float inv = 1.0f / lt;
       const uint32_t i = skiparse_token(mode, uint32_t(r), j, divk, uint32_t(L));
