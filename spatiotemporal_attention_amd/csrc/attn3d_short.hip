@@ -89,18 +89,33 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
     const uint32_t i = skiparse_token(mode, uint32_t(row < L ? row : 0), j, divk, uint32_t(L ? L : 1));
     vraw[e] = row < L ? ld16(a.v + in_off + int64_t(i) * sn + 8 * col) : make_uint4(0, 0, 0, 0);
   }
+  // (one 32-row block: K and Q rows load as whole-row chunks too, like V,
+  // and reach the operand layout through the wave's LDS tile below)
   uint32_t tok[NB];
-  uint4 kraw[NB][D / 16], qraw[NB][D / 16];
+  uint4 kraw[NB][NB == 1 ? 1 : D / 16], qraw[NB][NB == 1 ? 1 : D / 16];
+  uint4 kc[NB == 1 ? CPL : 1], qc[NB == 1 ? CPL : 1];
+  if constexpr (NB == 1) {
 #pragma unroll
-  for (int rb = 0; rb < NB; ++rb) {
-    const int r = 32 * rb + l32;
-    const bool on = r < L;
-    tok[rb] = skiparse_token(mode, uint32_t(on ? r : 0), j, divk, uint32_t(L ? L : 1));
-    const int64_t off = in_off + int64_t(tok[rb]) * sn + 8 * g;
+    for (int e = 0; e < CPL; ++e) {
+      const int idx = lane + 64 * e;
+      const int row = idx / KCH, col = idx % KCH;
+      const uint32_t i = skiparse_token(mode, uint32_t(row < L ? row : 0), j, divk, uint32_t(L ? L : 1));
+      kc[e] = row < L ? ld16(a.k + in_off + int64_t(i) * sn + 8 * col) : make_uint4(0, 0, 0, 0);
+      qc[e] = row < L ? ld16(a.q + in_off + int64_t(i) * sn + 8 * col) : make_uint4(0, 0, 0, 0);
+    }
+    tok[0] = skiparse_token(mode, uint32_t(l32 < L ? l32 : 0), j, divk, uint32_t(L ? L : 1));
+  } else {
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      kraw[rb][c] = on ? ld16(a.k + off + 16 * c) : make_uint4(0, 0, 0, 0);
-      qraw[rb][c] = on ? ld16(a.q + off + 16 * c) : make_uint4(0, 0, 0, 0);
+    for (int rb = 0; rb < NB; ++rb) {
+      const int r = 32 * rb + l32;
+      const bool on = r < L;
+      tok[rb] = skiparse_token(mode, uint32_t(on ? r : 0), j, divk, uint32_t(L ? L : 1));
+      const int64_t off = in_off + int64_t(tok[rb]) * sn + 8 * g;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        kraw[rb][c] = on ? ld16(a.k + off + 16 * c) : make_uint4(0, 0, 0, 0);
+        qraw[rb][c] = on ? ld16(a.q + off + 16 * c) : make_uint4(0, 0, 0, 0);
+      }
     }
   }
 
@@ -112,19 +127,67 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
   }
   if (!live) return;               // whole wave; no workgroup barrier follows
 
-  // V -> this wave's LDS tile (swizzled; rows past L are zero)
   uint16_t* vs = v_s[wave];
+  // whole-row chunks idx = lane + 64 e -> this wave's LDS tile (swizzled)
+  auto put_rows = [&](const uint4 (&x)[CPL]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) {
-    const int idx = lane + 64 * e;
-    const int row = idx / KCH, col = idx % KCH;
-    *reinterpret_cast<uint4*>(vs + 8 * (row * KCH + (col ^ chunk_swz<D>(row)))) = vraw[e];
-  }
+    for (int e = 0; e < CPL; ++e) {
+      const int idx = lane + 64 * e;
+      const int row = idx / KCH, col = idx % KCH;
+      *reinterpret_cast<uint4*>(vs + 8 * (row * KCH + (col ^ chunk_swz<D>(row)))) = x[e];
+    }
+  };
 
   // K rotated as osp_rope3d rotates it (then bf16); Q rotated and scaled by
   // scale*log2(e) with one rounding
   bf16x8_t kreg[NB][D / 16], qreg[NB][D / 16];
   const bool fast_rope = rg.aligned8 && rg.tab_entries;
+  if constexpr (NB == 1) {
+    // rotate each whole-row chunk (pairs 4 col .. 4 col + 3 of its row's
+    // token), then through the LDS tile into the operand layout: K first,
+    // then Q over it (the wave's LDS operations run in order), then V
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      const int idx = lane + 64 * e;
+      const int row = idx / KCH, col = idx % KCH;
+      if (row < L) {
+        const uint32_t i = skiparse_token(mode, uint32_t(row), j, divk, uint32_t(L));
+        const bool video = is_video(rg, i);
+        const Coord3 cc = video_coords(rg, i);
+        if (ROPE_K && video)
+          kc[e] = fast_rope ? rotate_chunk_col(rl, chunk_col(rg, 4 * col), cc, kc[e])
+                            : rotate_chunk_tab(rg, rl, 4 * col, cc, kc[e]);
+        uint4 raw = qc[e];
+        if (ROPE_Q && video) {
+          raw = rotate_chunk_scaled(rg, rl, 4 * col, cc, raw, c2);
+        } else {
+          raw.x = pack_bf16(bf16lo(raw.x) * c2, bf16hi(raw.x) * c2);
+          raw.y = pack_bf16(bf16lo(raw.y) * c2, bf16hi(raw.y) * c2);
+          raw.z = pack_bf16(bf16lo(raw.z) * c2, bf16hi(raw.z) * c2);
+          raw.w = pack_bf16(bf16lo(raw.w) * c2, bf16hi(raw.w) * c2);
+        }
+        qc[e] = raw;
+      }
+    }
+    int r_off[D / 16];
+    row_read_offsets<D>(lane, r_off);
+    const char* vsb = reinterpret_cast<const char*>(vs);
+    auto get_rows = [&](bf16x8_t (&y)[D / 16]) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's stores landed
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) y[c] = *reinterpret_cast<const bf16x8_t*>(vsb + r_off[c]);
+    };
+    put_rows(kc);
+    get_rows(kreg[0]);
+    __builtin_amdgcn_wave_barrier();
+    put_rows(qc);
+    get_rows(qreg[0]);
+    __builtin_amdgcn_wave_barrier();
+    put_rows(vraw);
+  } else {
+  // V -> this wave's LDS tile (swizzled; rows past L are zero)
+  put_rows(vraw);
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) {
     const bool video = is_video(rg, tok[rb]);
@@ -147,6 +210,7 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
       }
       qreg[rb][c] = __builtin_bit_cast(bf16x8_t, raw);
     }
+  }
   }
   // the V tile is this wave's own: its stores land before its reads
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
