@@ -25,6 +25,13 @@
 #include "osp_internal.hpp"
 #include "osp_mfma.hpp"
 
+// K and Q loaded as whole-row chunks and moved to the operand layout
+// through LDS (see the kernel); build-time switch per block count, for
+// comparing with loads straight into the operand layout.
+#ifndef OSP_SHORT_ROWS_LDS
+#define OSP_SHORT_ROWS_LDS(NB) (true)
+#endif
+
 namespace osp {
 
 template <bool R> struct ShortRope {
@@ -89,12 +96,13 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
     const uint32_t i = skiparse_token(mode, uint32_t(row < L ? row : 0), j, divk, uint32_t(L ? L : 1));
     vraw[e] = row < L ? ld16(a.v + in_off + int64_t(i) * sn + 8 * col) : make_uint4(0, 0, 0, 0);
   }
-  // (one 32-row block: K and Q rows load as whole-row chunks too, like V,
-  // and reach the operand layout through the wave's LDS tile below)
+  // (K and Q rows load as whole-row chunks too, like V, and reach the
+  // operand layout through the wave's LDS tile below)
   uint32_t tok[NB];
-  uint4 kraw[NB][NB == 1 ? 1 : D / 16], qraw[NB][NB == 1 ? 1 : D / 16];
-  uint4 kc[NB == 1 ? CPL : 1], qc[NB == 1 ? CPL : 1];
-  if constexpr (NB == 1) {
+  constexpr bool ROWS_LDS = OSP_SHORT_ROWS_LDS(NB);
+  uint4 kraw[NB][ROWS_LDS ? 1 : D / 16], qraw[NB][ROWS_LDS ? 1 : D / 16];
+  uint4 kc[ROWS_LDS ? CPL : 1], qc[ROWS_LDS ? CPL : 1];
+  if constexpr (ROWS_LDS) {
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
       const int idx = lane + 64 * e;
@@ -103,7 +111,11 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
       kc[e] = row < L ? ld16(a.k + in_off + int64_t(i) * sn + 8 * col) : make_uint4(0, 0, 0, 0);
       qc[e] = row < L ? ld16(a.q + in_off + int64_t(i) * sn + 8 * col) : make_uint4(0, 0, 0, 0);
     }
-    tok[0] = skiparse_token(mode, uint32_t(l32 < L ? l32 : 0), j, divk, uint32_t(L ? L : 1));
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      const int r = 32 * rb + l32;
+      tok[rb] = skiparse_token(mode, uint32_t(r < L ? r : 0), j, divk, uint32_t(L ? L : 1));
+    }
   } else {
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
@@ -142,7 +154,7 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
   // scale*log2(e) with one rounding
   bf16x8_t kreg[NB][D / 16], qreg[NB][D / 16];
   const bool fast_rope = rg.aligned8 && rg.tab_entries;
-  if constexpr (NB == 1) {
+  if constexpr (ROWS_LDS) {
     // rotate each whole-row chunk (pairs 4 col .. 4 col + 3 of its row's
     // token), then through the LDS tile into the operand layout: K first,
     // then Q over it (the wave's LDS operations run in order), then V
@@ -172,17 +184,20 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
     int r_off[D / 16];
     row_read_offsets<D>(lane, r_off);
     const char* vsb = reinterpret_cast<const char*>(vs);
-    auto get_rows = [&](bf16x8_t (&y)[D / 16]) __attribute__((always_inline)) {
+    auto get_rows = [&](bf16x8_t (&y)[NB][D / 16]) __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's stores landed
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) y[c] = *reinterpret_cast<const bf16x8_t*>(vsb + r_off[c]);
+      for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+          y[rb][c] = *reinterpret_cast<const bf16x8_t*>(vsb + 32 * rb * KCH * 16 + r_off[c]);
     };
     put_rows(kc);
-    get_rows(kreg[0]);
+    get_rows(kreg);
     __builtin_amdgcn_wave_barrier();
     put_rows(qc);
-    get_rows(qreg[0]);
+    get_rows(qreg);
     __builtin_amdgcn_wave_barrier();
     put_rows(vraw);
   } else {
