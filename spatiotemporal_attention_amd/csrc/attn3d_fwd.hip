@@ -495,12 +495,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // (the rates are staged first, and their load waited for, so that no
-  // later wait for it also waits for the tiles)
+  // (the rate load is issued first: loads complete in order, so waiting
+  // for it does not wait for the tiles or the Q rows behind it)
+  static_assert(C::NT >= kMaxPairs, "one rate per thread");
+  float omega = 0.f;
   if constexpr (ROPE_Q || ROPE_K) {
-    static_assert(C::NT >= kMaxPairs, "one rate per thread");
-    if (tid < kMaxPairs) rl->omega[tid] = a.rope.omega[tid];
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    if (tid < kMaxPairs) omega = a.rope.omega[tid];
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (!ROPE_K) {
@@ -520,6 +520,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     for (int c = 0; c < D / 16; ++c) qraw[qb][c] = ld16(p + 16 * c + 8 * g);
   }
   if constexpr (ROPE_Q || ROPE_K) {
+    if (tid < kMaxPairs) rl->omega[tid] = omega;
     lds_barrier();
     fill_rope_table(rg, rl, tid, C::NT);
     lds_barrier();
@@ -537,7 +538,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       // times scale * log2(e) so that the score products come out in log2
       // units; a rotated row is rotated and scaled in fp32, rounded once
       if (ROPE_Q && video) {
-        raw = rotate_chunk_scaled(rg, rl, 8 * c + 4 * g, cc, raw, c2);
+        raw = fast_rope ? rotate_chunk_col_scaled(rl, chunk_col(rg, 8 * c + 4 * g), cc, raw, c2)
+                        : rotate_chunk_scaled(rg, rl, 8 * c + 4 * g, cc, raw, c2);
       } else {
         raw.x = pack_bf16(bf16lo(raw.x) * c2, bf16hi(raw.x) * c2);
         raw.y = pack_bf16(bf16lo(raw.y) * c2, bf16hi(raw.y) * c2);

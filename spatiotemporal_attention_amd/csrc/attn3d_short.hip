@@ -84,10 +84,17 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
   const float c2 = a.scale_log2;
   const RopeGeom rg = rope_scalars(a.rope);
 
-  // ---- every global load first (their latency overlaps the table fill):
-  // V chunks idx = lane + 64 e of the tile; K rows (key 32kb + l32) and Q
-  // rows (query 32qb + l32) at channels 16c + 8g .. +7, the A and B
-  // operand layouts of S^T = K Q^T
+  // ---- every global load first (their latency overlaps the table fill),
+  // the RoPE rate first of all: loads complete in order, so waiting for it
+  // does not wait for the rows behind it.  V, K and Q as chunks idx = lane
+  // + 64 e of whole rows (or K and Q in the operand layouts of S^T = K Q^T,
+  // rows 32 rb + l32 at channels 16 c + 8 g .. +7, where that path is built)
+  static_assert(W * 64 >= kMaxPairs, "one rate per thread");
+  float omega = 0.f;
+  if constexpr (ROPE_Q || ROPE_K) {
+    if (tid < kMaxPairs) omega = a.rope.omega[tid];
+    __builtin_amdgcn_sched_barrier(0);
+  }
   uint4 vraw[CPL];
 #pragma unroll
   for (int e = 0; e < CPL; ++e) {
@@ -132,10 +139,17 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
   }
 
   if constexpr (ROPE_Q || ROPE_K) {
-    stage_rope_rates<W * 64>(a.rope.omega, rl, tid);
-    __syncthreads();
+    // workgroup barriers that wait for LDS stores only, not for the loads
+    auto lds_barrier = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (tid < kMaxPairs) rl->omega[tid] = omega;
+    lds_barrier();
     fill_rope_table(rg, rl, tid, W * 64);
-    __syncthreads();
+    lds_barrier();
   }
   if (!live) return;               // whole wave; no workgroup barrier follows
 
@@ -171,7 +185,8 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
                             : rotate_chunk_tab(rg, rl, 4 * col, cc, kc[e]);
         uint4 raw = qc[e];
         if (ROPE_Q && video) {
-          raw = rotate_chunk_scaled(rg, rl, 4 * col, cc, raw, c2);
+          raw = fast_rope ? rotate_chunk_col_scaled(rl, chunk_col(rg, 4 * col), cc, raw, c2)
+                           : rotate_chunk_scaled(rg, rl, 4 * col, cc, raw, c2);
         } else {
           raw.x = pack_bf16(bf16lo(raw.x) * c2, bf16hi(raw.x) * c2);
           raw.y = pack_bf16(bf16lo(raw.y) * c2, bf16hi(raw.y) * c2);
@@ -216,7 +231,8 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
       kreg[rb][c] = __builtin_bit_cast(bf16x8_t, kv);
       uint4 raw = qraw[rb][c];
       if (ROPE_Q && video) {
-        raw = rotate_chunk_scaled(rg, rl, 8 * c + 4 * g, cc, raw, c2);
+        raw = fast_rope ? rotate_chunk_col_scaled(rl, chunk_col(rg, 8 * c + 4 * g), cc, raw, c2)
+                        : rotate_chunk_scaled(rg, rl, 8 * c + 4 * g, cc, raw, c2);
       } else {
         raw.x = pack_bf16(bf16lo(raw.x) * c2, bf16hi(raw.x) * c2);
         raw.y = pack_bf16(bf16lo(raw.y) * c2, bf16hi(raw.y) * c2);

@@ -198,6 +198,20 @@ __device__ __forceinline__ uint4 rotate_chunk_col(const RopeLds* s, const ChunkC
   return x;
 }
 
+// rotate_chunk_col with the result multiplied by `scale` before rounding
+// (the same table entries as rotate_chunk_scaled reads, so the same bits).
+__device__ __forceinline__ uint4 rotate_chunk_col_scaled(const RopeLds* s, const ChunkCol& k,
+                                                         const Coord3& c, uint4 x, float scale) {
+  const int pos = int(sel3(k.axis, c.t, c.h, c.w));
+  const float4* t = reinterpret_cast<const float4*>(s->tab + k.base + pos * k.stride);
+  const float4 a = t[0], b = t[1];
+  x.x = rotate_pair_scaled(x.x, make_float2(a.x, a.y), scale);
+  x.y = rotate_pair_scaled(x.y, make_float2(a.z, a.w), scale);
+  x.z = rotate_pair_scaled(x.z, make_float2(b.x, b.y), scale);
+  x.w = rotate_pair_scaled(x.w, make_float2(b.z, b.w), scale);
+  return x;
+}
+
 // Is token i a video token (text tokens come first and are not rotated).
 __device__ __forceinline__ bool is_video(const RopeGeom& g, uint32_t i) {
   return int32_t(i) >= g.n_text;
