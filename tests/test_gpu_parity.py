@@ -220,9 +220,14 @@ def test_strided_packed_qkv():
     qkv = cpu.cuda()
     note("strided packed qkv")
     o = torch.empty((1, n, 2, 64), dtype=torch.bfloat16, device="cuda")
+    # the default rotates K by its own pass into a temporary with K's strides
     osp.osp_attn3d_fwd(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], grid=grid, rope_split=split,
                        out=o)
+    o2 = osp.osp_attn3d_fwd(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], grid=grid, rope_split=split,
+                            fuse_rope="qk")
     torch.cuda.synchronize()
+    assert torch.equal(qkv.cpu(), cpu)                  # the inputs are not touched
+    assert torch.equal(o, o2)
     f = workloads.to_f64(cpu)
     want, _ = oracle.attn3d(f[:, :, 0], f[:, :, 1], f[:, :, 2], grid=grid, rope_split=split)
     assert_parity(to_np(o), want, "O strided")
