@@ -174,3 +174,46 @@ def test_packed_bwd_equals_plain_calls_and_oracle(mode, k, segs):
                           BWD_MAX_REL * float(np.abs(w).max()),
                           BWD_REL_L2 if name == "dv" else BWD_REL_L2_ROPE)
         start = end
+
+
+def test_packed_bwd_frame_pack_sampled_rows():
+    """The CogVideoX frame pack's backward at full size (the launches the
+    benchmark times): sampled dQ rows of every segment, each exact in the
+    oracle from the same bf16 rotated inputs (a row's dQ needs only its own
+    scores), and per segment the column identities of dK (sum 0) and dV
+    (sum of dO), for two of the 48 heads."""
+    pk = workloads.COGVIDEOX_PACK
+    wl = workloads.WORKLOADS[pk["base"]]
+    segs = [(pk["n_text"], osp.osp_latent_grid(*clip, wl.c_t, wl.c_s, wl.p_t, wl.p_s))
+            for clip in pk["clips"]]
+    n = sum(nt + int(np.prod(g)) for nt, g in segs)
+    shape = (1, n, wl.heads, wl.head_dim)
+    note(f"frame pack backward segments={segs} n={n}")
+    cpu, (q, k, v) = qkv_for(pk["seed"], shape)
+    do_cpu = workloads.make_dout(pk["seed"], shape)
+    qr = osp.osp_rope3d_packed(q, segments=segs, rope_split=wl.rope_split)
+    kr = osp.osp_rope3d_packed(k, segments=segs, rope_split=wl.rope_split)
+    o, lse = osp.osp_attn3d_packed_fwd(qr, kr, v, segments=segs, rope_split=wl.rope_split,
+                                       fuse_rope=False, return_lse=True)
+    dq, dk, dv = osp.osp_attn3d_packed_bwd(qr, kr, v, o, lse, do_cpu.cuda(), segments=segs)
+    torch.cuda.synchronize()
+    hs = slice(0, 2)
+    qw, kw = to_np(qr[:, :, hs]), to_np(kr[:, :, hs])
+    vw, dow = workloads.to_f64(cpu[2][:, :, hs]), workloads.to_f64(do_cpu[:, :, hs])
+    got_q, got_k, got_v = to_np(dq[:, :, hs]), to_np(dk[:, :, hs]), to_np(dv[:, :, hs])
+    start = 0
+    for s_i, (nt, g) in enumerate(segs):
+        end = start + nt + int(np.prod(g))
+        rows = start + workloads.sample_rows(pk["seed"] + s_i, end - start, 16)
+        for h in range(2):
+            want_q, _, _ = oracle.softmax_attention_bwd(qw[0, rows, h], kw[0, start:end, h],
+                                                        vw[0, start:end, h], dow[0, rows, h],
+                                                        1.0 / np.sqrt(wl.head_dim))
+            assert_parity(got_q[0, rows, h], want_q, f"dq segment {s_i} h={h}",
+                          BWD_MAX_REL * float(np.abs(want_q).max()), BWD_REL_L2)
+            gk, gv = got_k[0, start:end, h], got_v[0, start:end, h]
+            assert (np.abs(gk.sum(axis=0)) <= 1e-2 * np.abs(gk).sum(axis=0)).all()
+            want_dv = dow[0, start:end, h].sum(axis=0)
+            assert (np.abs(gv.sum(axis=0) - want_dv) <= 1e-2 * np.abs(gv).sum(axis=0)).all()
+        start = end
+    assert not torch.isnan(dq).any() and not torch.isnan(dk).any() and not torch.isnan(dv).any()
