@@ -42,7 +42,12 @@ design notes):
     k = H*W;
 13. a packed sequence (several videos in one sequence) attends block
     diagonally, each video within itself, with RoPE positions from 0 on its
-    own grid.
+    own grid;
+14. Skiparse-2D applies the two Skiparse rules along the latent's h and w
+    axes, with factor s = sqrt(k) on each, in every frame: subsequence
+    j = jh*s + jw holds the tokens with h = jh, w = jw (mod s) (single), or
+    those of the s x s patches whose patch row and column are jh, jw
+    (mod s) (group).
 
 Parity status: grid arithmetic, rotation and attention are pinned by closed
 forms, invariants, a library routine and brute force (tests/test_oracle_*.py).
@@ -56,7 +61,8 @@ import math
 
 import numpy as np
 
-MODES = ("full", "skiparse_single", "skiparse_group", "block")
+MODES = ("full", "skiparse_single", "skiparse_group", "block", "skiparse2d_single",
+         "skiparse2d_group")
 
 
 # --------------------------------------------------------------------------
@@ -136,7 +142,7 @@ def rope3d(x: np.ndarray, grid, n_text: int, rope_split, theta: float = 1e4,
 # --------------------------------------------------------------------------
 # Skiparse regrouping (row a3)
 # --------------------------------------------------------------------------
-def skiparse_groups(mode: str, k: int, n: int) -> list:
+def skiparse_groups(mode: str, k: int, n: int, grid=None) -> list:
     """Token indices of each subsequence, by membership predicate.
 
     Open-Sora Plan section 2.2.2: a Skiparse step cuts the attended sequence
@@ -152,6 +158,15 @@ def skiparse_groups(mode: str, k: int, n: int) -> list:
     attention that Open-Sora Plan section 2.2.2 contrasts with Group Skip
     (k = N / window).  The temporal half (tokens with the same (h, w)) is
     Single Skip with k = H*W.
+
+    "skiparse2d_single" / "skiparse2d_group" need ``grid`` (reading 14).
+    The Open-Sora Plan blog page lists Skiparse-2D for OSP-Next as a fixed
+    sparse rule along H and W that stays FlashAttention-compatible, and
+    gives no more.  Here k = s*s: the single rule keeps the tokens whose h
+    and w are jh and jw modulo s; the group rule cuts each frame into s x s
+    patches and keeps the patches whose patch row and patch column are jh
+    and jw modulo s.  Every frame takes part, so each subsequence holds N/k
+    tokens.  Single needs H and W divisible by s, group by s*s.
     """
     idx = np.arange(n, dtype=np.int64)
     if mode == "full":
@@ -170,15 +185,29 @@ def skiparse_groups(mode: str, k: int, n: int) -> list:
         if n % k:
             raise ValueError("block attention needs N divisible by k")
         key = idx // (n // k)
+    elif mode in ("skiparse2d_single", "skiparse2d_group"):
+        if grid is None or int(np.prod(grid)) != n:
+            raise ValueError("Skiparse-2D needs the latent grid of the N tokens")
+        s = math.isqrt(k)
+        if s * s != k:
+            raise ValueError("Skiparse-2D needs k = s*s")
+        step = s if mode == "skiparse2d_single" else s * s
+        if grid[1] % step or grid[2] % step:
+            raise ValueError(f"Skiparse-2D needs H and W divisible by {step}")
+        c = video_coords(grid)
+        hh, ww = c[:, 1], c[:, 2]
+        if mode == "skiparse2d_group":
+            hh, ww = hh // s, ww // s
+        key = (hh % s) * s + (ww % s)
     else:
         raise ValueError(f"unknown mode {mode!r}")
     return [np.nonzero(key == j)[0] for j in range(k)]
 
 
-def skiparse_index(mode: str, k: int, n: int):
+def skiparse_index(mode: str, k: int, n: int, grid=None):
     """perm[r'] = token at regrouped position r' (subsequences by j, each in
     increasing token order; reading 10); inv is its inverse permutation."""
-    perm = np.concatenate(skiparse_groups(mode, k, n)).astype(np.int64)
+    perm = np.concatenate(skiparse_groups(mode, k, n, grid)).astype(np.int64)
     inv = np.empty_like(perm)
     inv[perm] = np.arange(n, dtype=np.int64)
     return perm.astype(np.int32), inv.astype(np.int32)
@@ -272,7 +301,7 @@ def attn3d(q, k, v, *, grid, n_text: int = 0, mode: str = "full",
     if rope:
         q = rope3d(q, grid, n_text, rope_split, theta, pos_offset)
         k = rope3d(k, grid, n_text, rope_split, theta, pos_offset)
-    groups = skiparse_groups(mode, sparse_k, n)
+    groups = skiparse_groups(mode, sparse_k, n, grid)
     if rows is None:
         out_rows = np.arange(n, dtype=np.int64)
     else:
@@ -406,7 +435,7 @@ def attn3d_bwd(q, k, v, do, *, grid, n_text: int = 0, mode: str = "full",
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for g in skiparse_groups(mode, sparse_k, n):
+    for g in skiparse_groups(mode, sparse_k, n, grid):
         for b in range(b_sz):
             for h in range(h_sz):
                 gq, gk, gv = softmax_attention_bwd(q[b, g, h, :], k[b, g, h, :], v[b, g, h, :],

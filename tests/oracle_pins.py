@@ -207,6 +207,66 @@ def pin_skiparse_structure(o):
             raise AssertionError("accepted a length that does not divide")
 
 
+def pin_skiparse2d_reshape(o):
+    """Skiparse-2D as a reshape of the [T, H, W] token grid: single splits h
+    and w into (h', jh) and (w', jw), the factor s last, and moves (jh, jw)
+    to the front; group splits them into (a, jh, u) and (b, jw, v) -- s x s
+    patches, s - 1 patches apart -- and moves (jh, jw) to the front."""
+    for grid, k in (((2, 4, 6), 4), ((3, 6, 6), 9), ((2, 4, 8), 4), ((1, 2, 2), 4),
+                    ((2, 3, 5), 1), ((1, 9, 9), 9)):
+        t, h, w = grid
+        n = t * h * w
+        s = math.isqrt(k)
+        want = np.arange(n).reshape(t, h // s, s, w // s, s).transpose(2, 4, 0, 1, 3).reshape(-1)
+        perm, inv = o.skiparse_index("skiparse2d_single", k, n, grid)
+        assert np.array_equal(perm, want), (grid, k)
+        assert np.array_equal(inv[perm], np.arange(n))
+        if h % (s * s) == 0 and w % (s * s) == 0:
+            want = (np.arange(n).reshape(t, h // (s * s), s, s, w // (s * s), s, s)
+                    .transpose(2, 5, 0, 1, 3, 4, 6).reshape(-1))
+            perm, inv = o.skiparse_index("skiparse2d_group", k, n, grid)
+            assert np.array_equal(perm, want), (grid, k)
+            assert np.array_equal(inv[perm], np.arange(n))
+
+
+def pin_skiparse2d_relations(o):
+    """Skiparse-2D against the 1D rules: with W divisible by s, the union
+    over jh of the 2D single subsequences (jh, jw) is 1D Single Skip
+    subsequence jw at k = s; with H and W divisible by s*s, the same holds
+    between 2D group and 1D Group Skip; s = H = W makes 2D single the
+    temporal half of separated attention (Single Skip, k = H*W); k = 1 is
+    full attention; shapes that do not divide, k not a square and a
+    missing grid are rejected."""
+    for grid, s in (((2, 4, 4), 2), ((3, 6, 9), 3), ((2, 8, 4), 2)):
+        n, k = int(np.prod(grid)), s * s
+        for m2, m1, step in (("skiparse2d_single", "skiparse_single", s),
+                             ("skiparse2d_group", "skiparse_group", s * s)):
+            if grid[1] % step or grid[2] % step:
+                continue
+            g2 = o.skiparse_groups(m2, k, n, grid)
+            g1 = o.skiparse_groups(m1, s, n)
+            assert len(g2) == k and all(len(g) == n // k for g in g2)
+            for jw in range(s):
+                union = sorted(np.concatenate([g2[jh * s + jw] for jh in range(s)]).tolist())
+                assert union == g1[jw].tolist(), (m2, grid, jw)
+    grid = (3, 2, 2)
+    a = o.skiparse_groups("skiparse2d_single", 4, 12, grid)
+    b = o.skiparse_groups("skiparse_single", 4, 12)
+    assert [g.tolist() for g in a] == [g.tolist() for g in b]
+    for mode in ("skiparse2d_single", "skiparse2d_group"):
+        g = o.skiparse_groups(mode, 1, 24, (2, 3, 4))
+        assert len(g) == 1 and g[0].tolist() == list(range(24))
+    for mode, k, grid in (("skiparse2d_single", 4, (2, 3, 4)), ("skiparse2d_group", 4, (2, 4, 2)),
+                          ("skiparse2d_group", 4, (1, 2, 4)), ("skiparse2d_single", 2, (2, 4, 4)),
+                          ("skiparse2d_single", 4, None)):
+        n = 32 if grid is None else int(np.prod(grid))
+        try:
+            o.skiparse_groups(mode, k, n, grid)
+        except ValueError:
+            continue
+        raise AssertionError(f"accepted {mode} k={k} grid={grid}")
+
+
 def pin_spatial_temporal(o):
     """Separated spatial / temporal attention (CogVideoX 2.2, Table 8) in
     terms of the latent coordinates: block attention with k = T groups the
@@ -262,10 +322,19 @@ def pin_attention_sdpa(o):
     kr = o.rope3d(k, grid, 0, split)
     for mode, kk in (("full", 1), ("skiparse_single", 4), ("skiparse_group", 4),
                      ("skiparse_single", 2), ("skiparse_group", 2), ("skiparse_single", 8),
-                     ("block", 4), ("block", 16), ("block", 1)):
+                     ("block", 4), ("block", 16), ("block", 1), ("skiparse2d_single", 4),
+                     ("skiparse2d_group", 4)):
         idx = np.arange(n)
         if mode == "full":
             lab = np.zeros(n, dtype=np.int64)
+        elif mode == "skiparse2d_single":
+            # (t, h', jh, w', jw) with s = 2: the label is (jh, jw)
+            lab = np.empty(n, dtype=np.int64)
+            lab[idx.reshape(4, 2, 2, 2, 2)] = (2 * np.arange(2)[:, None] + np.arange(2)[None, :])[None, None, :, None, :]
+        elif mode == "skiparse2d_group":
+            # (t, jh, u, jw, v): 2 x 2 patches, label (jh, jw)
+            lab = np.empty(n, dtype=np.int64)
+            lab[idx.reshape(4, 2, 2, 2, 2)] = (2 * np.arange(2)[:, None] + np.arange(2)[None, :])[None, :, None, :, None]
         elif mode == "block":
             lab = np.repeat(np.arange(kk), n // kk)
         elif mode == "skiparse_single":
@@ -326,10 +395,11 @@ def pin_attention_special(o):
     const = np.full_like(v, 1.75)
     out, _ = o.attn3d(q, k, const, grid=grid, rope_split=split)
     assert np.allclose(out, 1.75, atol=1e-13)
-    for mode, kk in (("full", 1), ("skiparse_single", 4), ("skiparse_group", 2), ("block", 4)):
+    for mode, kk in (("full", 1), ("skiparse_single", 4), ("skiparse_group", 2), ("block", 4),
+                     ("skiparse2d_single", 4), ("skiparse2d_group", 4)):
         out, lse = o.attn3d(np.zeros_like(q), k, v, grid=grid, mode=mode, sparse_k=kk,
                             rope_split=split)
-        for g in o.skiparse_groups(mode, kk, n):
+        for g in o.skiparse_groups(mode, kk, n, grid):
             assert np.allclose(out[:, g], v[:, g].mean(axis=1, keepdims=True), atol=1e-13)
             assert np.allclose(lse[:, :, g], math.log(len(g)), atol=1e-13)
     out, _ = o.attn3d(q, k, v, grid=grid, mode="skiparse_single", sparse_k=n, rope_split=split)
@@ -413,9 +483,10 @@ def pin_bwd_autograd(o):
     q, k, v, do = (rng.standard_normal((2, n, 3, 64)) for _ in range(4))
     qr = o.rope3d(q, grid, 0, split)
     kr = o.rope3d(k, grid, 0, split)
-    for mode, kk in (("full", 1), ("skiparse_single", 4), ("skiparse_group", 2), ("block", 4)):
+    for mode, kk in (("full", 1), ("skiparse_single", 4), ("skiparse_group", 2), ("block", 4),
+                     ("skiparse2d_single", 4), ("skiparse2d_group", 4)):
         lab = np.zeros(n, dtype=np.int64)
-        for j, g in enumerate(o.skiparse_groups(mode, kk, n)):
+        for j, g in enumerate(o.skiparse_groups(mode, kk, n, grid)):
             lab[g] = j
         mask = torch.from_numpy(lab[:, None] == lab[None, :])
         tq, tk, tv = (torch.from_numpy(a).permute(0, 2, 1, 3).clone().requires_grad_(True)
@@ -436,7 +507,8 @@ def pin_bwd_finite_differences(o):
     rng = _rng(33)
     cases = (((2, 2, 3), 0, "full", 1), ((1, 2, 3), 2, "full", 1),
              ((2, 2, 3), 0, "skiparse_single", 2), ((2, 2, 3), 0, "block", 3),
-             ((2, 2, 4), 0, "skiparse_group", 2))
+             ((2, 2, 4), 0, "skiparse_group", 2), ((2, 2, 4), 0, "skiparse2d_single", 4),
+             ((1, 4, 4), 0, "skiparse2d_group", 4))
     split, eps = (2, 2, 4), 1e-6
     for grid, n_text, mode, kk in cases:
         n = n_text + int(np.prod(grid))
@@ -498,7 +570,8 @@ def pin_packed_block_diagonal(o):
 ALL_PINS = [
     pin_latent_grids, pin_video_coords, pin_rope_closed_form, pin_rope_complex,
     pin_rope_invariants, pin_rope_axis_chunks, pin_skiparse_reshape,
-    pin_skiparse_structure, pin_spatial_temporal, pin_attention_sdpa, pin_attention_bruteforce,
+    pin_skiparse_structure, pin_skiparse2d_reshape, pin_skiparse2d_relations,
+    pin_spatial_temporal, pin_attention_sdpa, pin_attention_bruteforce,
     pin_attention_special, pin_attention_text, pin_rows_subset,
     pin_rope_transpose, pin_bwd_autograd, pin_bwd_finite_differences,
     pin_packed_block_diagonal,

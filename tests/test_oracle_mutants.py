@@ -38,6 +38,10 @@ MUTANTS = {
     "default_scale_wrong": ("sm_scale = 1.0 / math.sqrt(d)", "sm_scale = 1.0 / d"),
     "k_not_rotated": ("k = rope3d(k, grid, n_text, rope_split, theta, pos_offset)", "pass"),
     "block_strided": ("key = idx // (n // k)", "key = idx % k"),
+    "skiparse2d_axes_swapped": ("key = (hh % s) * s + (ww % s)", "key = (ww % s) * s + (hh % s)"),
+    "skiparse2d_flat_index": ("key = (hh % s) * s + (ww % s)", "key = idx % k"),
+    "skiparse2d_group_as_single": ("hh, ww = hh // s, ww // s", "hh, ww = hh, ww"),
+    "skiparse2d_group_patch_s2": ("hh, ww = hh // s, ww // s", "hh, ww = hh // k, ww // k"),
     "block_runs_of_k": ("key = idx // (n // k)", "key = idx // k % k"),
     "bwd_no_row_term": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp"),
     "bwd_dk_from_ds_not_transposed": ("dk = sm_scale * (ds.T @ q)", "dk = sm_scale * (ds @ q)"),
