@@ -60,10 +60,29 @@ typedef enum {
   OSP_MODE_SKIPARSE_GROUP = 2,   /* subsequence j = tokens i with
                                     floor(i/k) mod k = j (groups of k
                                     adjacent tokens, k-1 groups apart)       */
-  OSP_MODE_BLOCK = 3             /* subsequence j = tokens i with
+  OSP_MODE_BLOCK = 3,            /* subsequence j = tokens i with
                                     floor(i/(N/k)) = j (k runs of N/k
                                     adjacent tokens)                         */
+  OSP_MODE_SKIPARSE2D_SINGLE = 4,/* Skiparse-2D, k = s*s: subsequence
+                                    j = jh*s + jw = video tokens (t, h, w)
+                                    with h mod s = jh and w mod s = jw       */
+  OSP_MODE_SKIPARSE2D_GROUP = 5  /* Skiparse-2D, k = s*s: s x s patches of
+                                    each frame, s-1 patches apart;
+                                    subsequence j = jh*s + jw = tokens with
+                                    floor(h/s) mod s = jh and
+                                    floor(w/s) mod s = jw                    */
 } osp_mode;
+
+/* The two Skiparse-2D modes follow the Open-Sora Plan blog page, which
+   names Skiparse-2D for OSP-Next as a fixed sparse rule along H and W that
+   stays FlashAttention-compatible and gives no formula.  They are read as
+   the single and group rules of Skiparse (Open-Sora Plan section 2.2.2)
+   applied to the h and w axes with factor s = sqrt(k), in every frame:
+   k subsequences of N/k tokens, rows in increasing token order.  They need
+   n_text == 0, sparse_k a square, and grid_h, grid_w divisible by s
+   (single) or s*s (group), else OSP_ERR_UNSUPPORTED, OSP_ERR_PARAM or
+   OSP_ERR_SHAPE.  The packed entry points do not take them
+   (OSP_ERR_UNSUPPORTED): the lattice depends on each segment's grid. */
 
 /* flags of osp_attn3d_fwd */
 #define OSP_FUSE_ROPE_Q 1  /* rotate Q inside the attention loader; without it
@@ -298,6 +317,14 @@ osp_status osp_attn3d_packed_bwd(const osp_attn3d_desc* desc,
 osp_status osp_skiparse_index(int32_t mode, int32_t sparse_k, int64_t n_tokens,
                               int32_t* perm, int32_t* inv, int32_t on_device,
                               void* stream);
+/* The Skiparse-2D modes depend on the latent grid, so osp_skiparse_index
+   rejects them (OSP_ERR_PARAM).  osp_skiparse_index3d takes the grid
+   (N = grid_t*grid_h*grid_w, no text tokens) and accepts every mode, with
+   the same perm/inv, on_device and stream conventions and the same
+   errors as the attention calls for that grid. */
+osp_status osp_skiparse_index3d(int32_t mode, int32_t sparse_k, int32_t grid_t,
+                                int32_t grid_h, int32_t grid_w, int32_t* perm,
+                                int32_t* inv, int32_t on_device, void* stream);
 
 #ifdef __cplusplus
 }

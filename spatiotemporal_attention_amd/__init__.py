@@ -17,7 +17,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libosp.so")
 
-MODES = {"full": 0, "skiparse_single": 1, "skiparse_group": 2, "block": 3}
+MODES = {"full": 0, "skiparse_single": 1, "skiparse_group": 2, "block": 3, "skiparse2d_single": 4,
+         "skiparse2d_group": 5}
 OSP_FUSE_ROPE_Q = 1
 OSP_FUSE_ROPE_K = 2
 OSP_FUSE_ROPE = 3
@@ -85,6 +86,7 @@ def lib() -> ctypes.CDLL:
             "osp_attn3d_bwd_workspace": (I32, [D, I32, I32, ctypes.POINTER(I64)]),
             "osp_attn3d_bwd": (I32, [D, I32, I32, F32, P, P, P, P, P, P, P, P, P, P, I64, P]),
             "osp_skiparse_index": (I32, [I32, I32, I64, P, P, I32, P]),
+            "osp_skiparse_index3d": (I32, [I32, I32, I32, I32, I32, P, P, I32, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(h, name)
@@ -100,7 +102,7 @@ EXPORTED = ("osp_abi_version", "osp_status_string", "osp_last_error", "osp_laten
             "osp_attn3d_check", "osp_rope3d", "osp_rope3d_inv", "osp_attn3d_fwd",
             "osp_attn3d_packed_fwd", "osp_rope3d_packed", "osp_rope3d_packed_inv",
             "osp_attn3d_bwd_workspace", "osp_attn3d_bwd", "osp_attn3d_packed_bwd_workspace",
-            "osp_attn3d_packed_bwd", "osp_skiparse_index")
+            "osp_attn3d_packed_bwd", "osp_skiparse_index", "osp_skiparse_index3d")
 
 
 def _check(status: int):
@@ -423,17 +425,27 @@ def osp_attn3d_packed_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
 def osp_skiparse_index(mode, sparse_k: int, n_tokens: int, device=None):
     """(perm, inv) int32 maps.  device=None: numpy arrays filled by the
     library's host path; else torch tensors filled by its device kernel."""
-    m = _mode(mode)
+    return _index_call(lambda *ptrs: lib().osp_skiparse_index(
+        _mode(mode), int(sparse_k), int(n_tokens), *ptrs), int(n_tokens), device)
+
+
+def osp_skiparse_index3d(mode, sparse_k: int, grid, device=None):
+    """(perm, inv) int32 maps of the N = T*H*W video tokens of ``grid``; the
+    only index call that takes the Skiparse-2D modes."""
+    t, h, w = (int(x) for x in grid)
+    return _index_call(lambda *ptrs: lib().osp_skiparse_index3d(
+        _mode(mode), int(sparse_k), t, h, w, *ptrs), t * h * w, device)
+
+
+def _index_call(call, n_tokens: int, device):
     if device is None:
         perm = np.empty(n_tokens, dtype=np.int32)
         inv = np.empty(n_tokens, dtype=np.int32)
-        _check(lib().osp_skiparse_index(
-            m, int(sparse_k), int(n_tokens), perm.ctypes.data_as(ctypes.c_void_p),
-            inv.ctypes.data_as(ctypes.c_void_p), 0, None))
+        _check(call(perm.ctypes.data_as(ctypes.c_void_p), inv.ctypes.data_as(ctypes.c_void_p), 0,
+                    None))
         return perm, inv
     perm = torch.empty(n_tokens, dtype=torch.int32, device=device)
     inv = torch.empty(n_tokens, dtype=torch.int32, device=device)
-    _check(lib().osp_skiparse_index(
-        m, int(sparse_k), int(n_tokens), ctypes.c_void_p(perm.data_ptr()),
-        ctypes.c_void_p(inv.data_ptr()), 1, _stream(perm)))
+    _check(call(ctypes.c_void_p(perm.data_ptr()), ctypes.c_void_p(inv.data_ptr()), 1,
+                _stream(perm)))
     return perm, inv

@@ -186,7 +186,7 @@ struct TileDma {
     }
   }
   // offsets of tile t (rows 64t ..) of subsequence j; returns its first token
-  __device__ __forceinline__ uint32_t at(int t, int mode, uint32_t j, const FastDiv& divk, int L,
+  __device__ __forceinline__ uint32_t at(int t, int mode, uint32_t j, const SkipDiv& divk, int L,
                                          int64_t sn) {
     const int r0 = t * kBwdRows;
     const uint32_t i0 = skiparse_token(mode, uint32_t(r0), j, divk, uint32_t(L));
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   const BwdBlock wb = bwd_block<PACKED, true>(a);
   if (!wb.live) return;              // padding of a packed launch, before any barrier
   const int mode = a.mode;
-  const FastDiv divk = a.divk;
+  const SkipDiv divk = a.divk;
   const int L = wb.L;
   const int64_t sn = a.sn;
   const int64_t in_off = int64_t(wb.b) * a.sb + int64_t(wb.h) * a.sh + wb.tok0 * sn;
@@ -553,7 +553,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
   const BwdBlock wb = bwd_block<PACKED, false>(a);
   if (!wb.live) return;              // padding of a packed launch, before any barrier
   const int mode = a.mode;
-  const FastDiv divk = a.divk;
+  const SkipDiv divk = a.divk;
   const int L = wb.L;
   const int64_t sn = a.sn;
   const int64_t in_off = int64_t(wb.b) * a.sb + int64_t(wb.h) * a.sh + wb.tok0 * sn;

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   const uint32_t b = u / uint32_t(a.heads);
 
   const int mode = a.mode;
-  const FastDiv divk = a.divk;
+  const SkipDiv divk = a.divk;
   const int64_t a_sn = a.sn;
 
   const int L = seq_len;
@@ -741,7 +741,7 @@ template <int D, bool RQ, bool RK, bool PK>
 static hipError_t launch_drk(const AttnArgs& a, hipStream_t s) {
   using T = TileCfg<D, RK>;
   dim3 grid(a.total_tiles), block(T::NW * 64);
-  const bool fixed = a.mode != MODE_GROUP || T::BN % int(a.divk.d) == 0;
+  const bool fixed = a.mode <= MODE_BLOCK && (a.mode != MODE_GROUP || T::BN % int(a.divk.d) == 0);
   if (fixed)
     hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, RQ, RK, true, PK>),
                        grid, block, 0, s, a);

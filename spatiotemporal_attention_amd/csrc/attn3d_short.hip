@@ -77,7 +77,7 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
   const uint32_t b = bj / uint32_t(a.groups);
 
   const int mode = a.mode;
-  const FastDiv divk = a.divk;
+  const SkipDiv divk = a.divk;
   const int L = live ? a.seq_len : 0;
   const int64_t sn = a.sn;
   const int64_t in_off = int64_t(b) * a.sb + int64_t(h) * a.sh;

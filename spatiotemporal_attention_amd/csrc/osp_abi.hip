@@ -118,14 +118,43 @@ void fill_rope(const osp_attn3d_desc* d, osp::RopeGeom* g) {
   g->div_w = osp::make_fastdiv(uint32_t(d->grid_w));
 }
 
+// Per-axis factor s of the Skiparse-2D modes (k = s*s), 0 if k is not a square.
+int32_t skip2d_axis(int32_t k) {
+  int32_t s = int32_t(sqrt(double(k)) + 0.5);
+  return (s >= 1 && s * s == k) ? s : 0;
+}
+
+bool is_skip2d(int32_t mode) {
+  return mode == OSP_MODE_SKIPARSE2D_SINGLE || mode == OSP_MODE_SKIPARSE2D_GROUP;
+}
+
+// Remap divisors of a checked (mode, k) on the grid of d.
+osp::SkipDiv skip_div(const osp_attn3d_desc* d, int32_t mode, int32_t groups) {
+  if (!is_skip2d(mode)) return osp::make_skipdiv(uint32_t(groups), 1, 1, 1);
+  return osp::make_skipdiv(uint32_t(groups), uint32_t(skip2d_axis(groups)), uint32_t(d->grid_h),
+                           uint32_t(d->grid_w));
+}
+
 osp_status check_mode(const osp_attn3d_desc* d, int64_t n, int32_t mode, int32_t k) {
-  if (mode < OSP_MODE_FULL || mode > OSP_MODE_BLOCK)
+  if (mode < OSP_MODE_FULL || mode > OSP_MODE_SKIPARSE2D_GROUP)
     return fail(OSP_ERR_PARAM, "unknown mode %d", mode);
   if (mode == OSP_MODE_FULL) return OSP_OK;
   if (k < 1) return fail(OSP_ERR_PARAM, "sparse_k (%d) must be >= 1", k);
   if (d && d->n_text != 0)
     return fail(OSP_ERR_UNSUPPORTED, "Skiparse and block attention take no text tokens (n_text = %d)",
                 d->n_text);
+  if (is_skip2d(mode)) {
+    if (!d)
+      return fail(OSP_ERR_PARAM, "Skiparse-2D index maps need the latent grid: use osp_skiparse_index3d");
+    const int32_t s = skip2d_axis(k);
+    if (!s) return fail(OSP_ERR_PARAM, "Skiparse-2D needs sparse_k = s*s (got %d)", k);
+    const int32_t step = (mode == OSP_MODE_SKIPARSE2D_SINGLE) ? s : s * s;
+    if (d->grid_h % step || d->grid_w % step)
+      return fail(OSP_ERR_SHAPE, "Skiparse-2D %s with k=%d needs grid_h (%d) and grid_w (%d) divisible by %d",
+                  mode == OSP_MODE_SKIPARSE2D_SINGLE ? "single" : "group", k, d->grid_h, d->grid_w,
+                  step);
+    return OSP_OK;
+  }
   const int64_t div = (mode == OSP_MODE_SKIPARSE_GROUP) ? int64_t(k) * k : int64_t(k);
   if (n % div)
     return fail(OSP_ERR_SHAPE, "%s needs N (%lld) divisible by %lld",
@@ -133,6 +162,13 @@ osp_status check_mode(const osp_attn3d_desc* d, int64_t n, int32_t mode, int32_t
                 : mode == OSP_MODE_SKIPARSE_GROUP ? "group skip" : "block attention",
                 (long long)n, (long long)div);
   return OSP_OK;
+}
+
+// Tokens spanned by bn consecutive rows of a Skiparse-2D subsequence: at
+// most bn/(W/s) + 2 lattice rows, each within s*s rows of the grid.
+int64_t skip2d_span(const osp_attn3d_desc* d, int64_t k, int64_t bn) {
+  const int64_t s = skip2d_axis(int32_t(k));
+  return (bn / std::max<int64_t>(1, d->grid_w / s) + 2) * k * d->grid_w;
 }
 
 osp_status check_attn(const osp_attn3d_desc* d, int32_t mode, int32_t k, int32_t flags,
@@ -162,7 +198,8 @@ osp_status check_attn(const osp_attn3d_desc* d, int32_t mode, int32_t k, int32_t
   // rows of one key tile span bn tokens (full, block), bn*k (single skip)
   // or up to (bn + k)*k (group skip)
   const int64_t rows = (mode == OSP_MODE_SKIPARSE_SINGLE) ? bn * groups
-                     : (mode == OSP_MODE_SKIPARSE_GROUP) ? (bn + groups) * groups : bn;
+                     : (mode == OSP_MODE_SKIPARSE_GROUP) ? (bn + groups) * groups
+                     : is_skip2d(mode) ? skip2d_span(d, groups, bn) : bn;
   const int64_t span = rows * s->sn * 2 + int64_t(d->head_dim) * 2;
   if (span >= (int64_t(1) << 30))
     return fail(OSP_ERR_UNSUPPORTED, "token stride %lld with k=%lld spans more than 1 GiB per key tile",
@@ -190,7 +227,8 @@ osp_status check_bwd(const osp_attn3d_desc* d, int32_t mode, int32_t k, Shape* s
   // from their first token
   const int64_t bn = osp::bwd_tile_rows(d->head_dim);
   const int64_t rows = (mode == OSP_MODE_SKIPARSE_SINGLE) ? bn * groups
-                     : (mode == OSP_MODE_SKIPARSE_GROUP) ? (bn + groups) * groups : bn;
+                     : (mode == OSP_MODE_SKIPARSE_GROUP) ? (bn + groups) * groups
+                     : is_skip2d(mode) ? skip2d_span(d, groups, bn) : bn;
   const int64_t span = rows * s->sn * 2 + int64_t(d->head_dim) * 2;
   if (span >= (int64_t(1) << 30))
     return fail(OSP_ERR_UNSUPPORTED, "token stride %lld with k=%lld spans more than 1 GiB per tile",
@@ -231,7 +269,7 @@ void fill_fwd_args(const osp_attn3d_desc* desc, const Shape& s, int32_t mode, in
   a.groups = groups;
   a.seq_len = int32_t(s.n_tokens / groups);
   a.mode = mode;
-  a.divk = osp::make_fastdiv(uint32_t(groups));
+  a.divk = skip_div(desc, mode, groups);
   a.scale_log2 = float(scale * 1.4426950408889634);
   const int bm = osp::attn_rows_per_block(D);
   a.q_tiles = (a.seq_len + bm - 1) / bm;
@@ -247,6 +285,10 @@ osp_status check_packed_bwd(const osp_attn3d_desc* desc, const osp_segment* segm
   if (!desc) return fail(OSP_ERR_NULL, "desc is NULL");
   if (!segments) return fail(OSP_ERR_NULL, "segments is NULL");
   if (n_segments < 1) return fail(OSP_ERR_PARAM, "n_segments (%d) must be >= 1", n_segments);
+  if (is_skip2d(mode))
+    return fail(OSP_ERR_UNSUPPORTED,
+                "packed sequences take full, Skiparse or block attention (the Skiparse-2D lattice "
+                "depends on each segment's grid)");
   int64_t n = 0, grid = 0;
   for (int32_t i = 0; i < n_segments; ++i) {
     osp_attn3d_desc d = *desc;
@@ -329,7 +371,7 @@ osp_status enqueue_bwd(const osp_attn3d_desc* desc, const Shape& s, int32_t mode
   a.groups = groups;
   a.seq_len = int32_t(s.n_tokens / groups);
   a.mode = mode;
-  a.divk = osp::make_fastdiv(uint32_t(groups));
+  a.divk = skip_div(desc, mode, groups);
   a.scale = float(scale);
   a.scale_log2 = float(scale * 1.4426950408889634);
   const int kvr = osp::bwd_kv_rows_per_block(D), qr = osp::bwd_q_rows_per_block(D);
@@ -523,6 +565,10 @@ osp_status osp_attn3d_packed_fwd(const osp_attn3d_desc* desc, const osp_segment*
   if (!desc) return fail(OSP_ERR_NULL, "desc is NULL");
   if (!segments) return fail(OSP_ERR_NULL, "segments is NULL");
   if (n_segments < 1) return fail(OSP_ERR_PARAM, "n_segments (%d) must be >= 1", n_segments);
+  if (is_skip2d(mode))
+    return fail(OSP_ERR_UNSUPPORTED,
+                "packed sequences take full, Skiparse or block attention (the Skiparse-2D lattice "
+                "depends on each segment's grid)");
   // every segment is checked before anything is enqueued
   int64_t total = 0, tiles = 0;
   for (int32_t i = 0; i < n_segments; ++i) {
@@ -708,7 +754,7 @@ osp_status osp_attn3d_packed_bwd(const osp_attn3d_desc* desc, const osp_segment*
   const int32_t groups = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
   base.mode = mode;
   base.groups = groups;
-  base.divk = osp::make_fastdiv(uint32_t(groups));
+  base.divk = skip_div(desc, mode, groups);
   const int kvr = osp::bwd_kv_rows_per_block(desc->head_dim);
   const int qr = osp::bwd_q_rows_per_block(desc->head_dim);
   std::vector<osp::BwdPackSeg> segs;
@@ -749,22 +795,23 @@ osp_status osp_attn3d_packed_bwd(const osp_attn3d_desc* desc, const osp_segment*
   return ok();
 }
 
-osp_status osp_skiparse_index(int32_t mode, int32_t sparse_k, int64_t n_tokens, int32_t* perm,
-                              int32_t* inv, int32_t on_device, void* stream) {
+static osp_status skiparse_index_impl(const osp_attn3d_desc* d, int32_t mode, int32_t sparse_k,
+                                      int64_t n_tokens, int32_t* perm, int32_t* inv,
+                                      int32_t on_device, void* stream) {
   if (!perm && !inv) return fail(OSP_ERR_NULL, "perm and inv are both NULL");
   if (n_tokens < 0 || n_tokens > 0x7fffffffLL)
     return fail(OSP_ERR_SHAPE, "n_tokens %lld out of range", (long long)n_tokens);
-  osp_status st = check_mode(nullptr, n_tokens, mode, sparse_k);
+  osp_status st = check_mode(d, n_tokens, mode, sparse_k);
   if (st) return st;
   const int32_t n = int32_t(n_tokens);
   const int32_t k = (mode == OSP_MODE_FULL) ? 1 : sparse_k;
+  const osp::SkipDiv divk = skip_div(d, mode, k);
   if (on_device) {
-    hipError_t e = osp::launch_skiparse_index(mode, k, n, perm, inv,
+    hipError_t e = osp::launch_skiparse_index(mode, divk, n, perm, inv,
                                               static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_error(e, "skiparse_index launch");
     return ok();
   }
-  const osp::FastDiv divk = osp::make_fastdiv(uint32_t(k));
   const uint32_t len = uint32_t(n / k);
   for (uint32_t j = 0; j < uint32_t(k); ++j)
     for (uint32_t r = 0; r < len; ++r) {
@@ -774,6 +821,24 @@ osp_status osp_skiparse_index(int32_t mode, int32_t sparse_k, int64_t n_tokens, 
       if (inv) inv[i] = int32_t(pos);
     }
   return ok();
+}
+
+osp_status osp_skiparse_index(int32_t mode, int32_t sparse_k, int64_t n_tokens, int32_t* perm,
+                              int32_t* inv, int32_t on_device, void* stream) {
+  return skiparse_index_impl(nullptr, mode, sparse_k, n_tokens, perm, inv, on_device, stream);
+}
+
+osp_status osp_skiparse_index3d(int32_t mode, int32_t sparse_k, int32_t grid_t, int32_t grid_h,
+                                int32_t grid_w, int32_t* perm, int32_t* inv, int32_t on_device,
+                                void* stream) {
+  if (grid_t < 1 || grid_h < 1 || grid_w < 1)
+    return fail(OSP_ERR_SHAPE, "grid %d x %d x %d must be positive", grid_t, grid_h, grid_w);
+  osp_attn3d_desc d{};
+  d.grid_t = grid_t;
+  d.grid_h = grid_h;
+  d.grid_w = grid_w;
+  return skiparse_index_impl(&d, mode, sparse_k, int64_t(grid_t) * grid_h * grid_w, perm, inv,
+                             on_device, stream);
 }
 
 }  // extern "C"

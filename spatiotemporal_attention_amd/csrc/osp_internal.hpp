@@ -34,7 +34,7 @@ struct AttnArgs {
   int32_t batch, heads, n_tokens, seq_len, groups, mode;
   int32_t q_tiles;              // ceil(seq_len / rows per workgroup)
   int32_t total_tiles;          // batch * heads * groups * q_tiles
-  FastDiv divk;                 // division by the Skiparse ratio
+  SkipDiv divk;                 // division by the Skiparse ratio (and the 2D lattice)
   float scale_log2;             // sm_scale * log2(e)
   RopeGeom rope;
   // packed launches only: n_pack segments (workgroups from pack[s].tile0
@@ -100,7 +100,7 @@ struct BwdArgs {
   int32_t batch, heads, n_tokens, seq_len, groups, mode;
   int32_t kv_blocks;            // per (b, h, subsequence): key rows / rows per dK-dV workgroup
   int32_t q_blocks;             // per (b, h, subsequence): query rows / rows per dQ workgroup
-  FastDiv divk;
+  SkipDiv divk;
   float scale;                  // sm_scale
   float scale_log2;             // sm_scale * log2(e)
   int64_t ws_ld;                // token stride of a (b, h) row of the workspace arrays
@@ -122,7 +122,7 @@ hipError_t launch_attn3d_bwd_prep(const BwdArgs& a, int head_dim, hipStream_t s)
 hipError_t launch_attn3d_bwd_packed(const BwdArgs& pa, int kv_grid, int q_grid, int head_dim,
                                     hipStream_t s);
 
-hipError_t launch_skiparse_index(int32_t mode, int32_t k, int32_t n, int32_t* perm,
+hipError_t launch_skiparse_index(int32_t mode, const SkipDiv& divk, int32_t n, int32_t* perm,
                                  int32_t* inv, hipStream_t s);
 
 }  // namespace osp

@@ -7,7 +7,7 @@
 namespace osp {
 
 __global__ __launch_bounds__(256) void skiparse_index_kernel(int32_t mode, uint32_t n,
-                                                             FastDiv div_len, FastDiv divk,
+                                                             FastDiv div_len, SkipDiv divk,
                                                              int32_t* perm, int32_t* inv) {
   for (uint32_t pos = blockIdx.x * 256 + threadIdx.x; pos < n; pos += gridDim.x * 256) {
     const uint32_t j = fdiv(pos, div_len);
@@ -18,16 +18,14 @@ __global__ __launch_bounds__(256) void skiparse_index_kernel(int32_t mode, uint3
   }
 }
 
-hipError_t launch_skiparse_index(int32_t mode, int32_t k, int32_t n, int32_t* perm,
+hipError_t launch_skiparse_index(int32_t mode, const SkipDiv& divk, int32_t n, int32_t* perm,
                                  int32_t* inv, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  const int32_t groups = (mode == MODE_FULL) ? 1 : k;
-  const uint32_t len = uint32_t(n / groups);
+  const uint32_t len = uint32_t(n) / divk.d;
   uint32_t blocks = (uint32_t(n) + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(skiparse_index_kernel, dim3(blocks), dim3(256), 0, s, mode, uint32_t(n),
-                     make_fastdiv(len), make_fastdiv(uint32_t(mode == MODE_FULL ? 1 : k)), perm,
-                     inv);
+                     make_fastdiv(len), divk, perm, inv);
   return hipGetLastError();
 }
 

@@ -113,7 +113,20 @@ def _code(desc, mode="full", k=1, flags=1):
     # window attention over 28,800 tokens in windows of 64: 450 blocks
     ({"grid": (24, 30, 40), "heads": 24, "head_dim": 96, "rope_split": (32, 32, 32)},
      "block", 450, 1, OK),
-    ({}, 4, 1, 1, PARAM),
+    ({}, 6, 1, 1, PARAM),
+    # Skiparse-2D: k = s*s, grid_h and grid_w divisible by s (single) or s*s (group)
+    ({}, "skiparse2d_single", 4, 1, OK),
+    ({}, "skiparse2d_group", 4, 1, OK),
+    ({}, "skiparse2d_single", 16, 1, OK),
+    ({}, "skiparse2d_group", 16, 1, SHAPE),
+    ({}, "skiparse2d_single", 9, 1, SHAPE),
+    ({}, "skiparse2d_single", 2, 1, PARAM),
+    ({}, "skiparse2d_group", 0, 1, PARAM),
+    ({"n_text": 2, "grid": (2, 4, 4)}, "skiparse2d_single", 4, 1, UNSUP),
+    ({"grid": (24, 30, 40), "heads": 24, "head_dim": 96, "rope_split": (32, 32, 32)},
+     "skiparse2d_single", 4, 1, OK),
+    ({"grid": (24, 30, 40), "heads": 24, "head_dim": 96, "rope_split": (32, 32, 32)},
+     "skiparse2d_group", 4, 1, SHAPE),
 ])
 def test_attn_check_codes(kw, mode, k, flags, want):
     assert _code(_desc(**kw), mode, k, flags) == want

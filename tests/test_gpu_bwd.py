@@ -109,6 +109,17 @@ def test_bwd_modes(mode, k):
              tag=f"{mode}-{k}")
 
 
+@pytest.mark.parametrize("mode,k,grid,d", [
+    ("skiparse2d_single", 4, (5, 8, 12), 64),     # L = 120: two tiles, the second ragged
+    ("skiparse2d_group", 4, (3, 12, 16), 96),     # L = 144
+    ("skiparse2d_single", 9, (4, 12, 9), 128),    # L = 48
+    ("skiparse2d_group", 9, (2, 18, 9), 64),      # L = 36
+])
+def test_bwd_skiparse2d(mode, k, grid, d):
+    bwd_case(81, grid=grid, heads=2, head_dim=d, mode=mode, sparse_k=k, batch=2 if d == 64 else 1,
+             tag=f"{mode} k={k}")
+
+
 def test_bwd_text_tokens_batch_and_scale():
     bwd_case(2, grid=(3, 10, 12), n_text=37, heads=3, head_dim=96, batch=2, sm_scale=0.2,
              tag="text-batch-scale")
@@ -155,7 +166,7 @@ def test_bwd_strided_layout_and_determinism():
 
 
 # ---------------------------------------------------------- full-size checks
-@pytest.mark.parametrize("mode,k", [("full", 1), ("skiparse_single", 4)])
+@pytest.mark.parametrize("mode,k", [("full", 1), ("skiparse_single", 4), ("skiparse2d_single", 4)])
 def test_bwd_osp480_sampled_rows_and_identities(mode, k):
     """28,800 tokens (93x480x640 clip: 24x30x40 latent grid), 2 heads of 96.
     dQ rows are exact per row in the oracle (a row's gradient needs only its
@@ -177,7 +188,7 @@ def test_bwd_osp480_sampled_rows_and_identities(mode, k):
     dow = workloads.to_f64(do_cpu)
     got_q, got_k, got_v = to_np(dq), to_np(dk), to_np(dv)
     rows = workloads.sample_rows(9, n, 48)
-    for g in oracle.skiparse_groups(mode, k, n):
+    for g in oracle.skiparse_groups(mode, k, n, grid):
         sel = np.intersect1d(rows, g)
         for h in range(heads):
             if len(sel):

@@ -79,3 +79,14 @@ def test_osp480_separated_spatial_temporal(half):
 def test_osp15_8x8x8_d128(mode, k):
     # 121x576x1024 through the 8x8x8 VAE: 16x36x64 = 36,864 tokens, D=128
     run_sampled("osp15", mode, k)
+
+
+def test_osp480_skiparse2d_single_k4():
+    # 2 x 2 lattice over h and w in each of the 24 frames: 4 subsequences of 7,200
+    run_sampled("osp480_skiparse", "skiparse2d_single", 4)
+
+
+@pytest.mark.parametrize("mode", ["skiparse2d_single", "skiparse2d_group"])
+def test_osp15_skiparse2d_k4(mode):
+    # 16x36x64: H and W divisible by 4, so the 2 x 2 patch rule applies too
+    run_sampled("osp15", mode, 4)

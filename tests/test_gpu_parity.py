@@ -136,6 +136,37 @@ def test_multitile_d96(variant, mode, k):
              tol=4.0 if variant == "sharp" else 1.0)
 
 
+@pytest.mark.parametrize("mode,k,grid,d,split,batch,fuse", [
+    ("skiparse2d_single", 4, (6, 12, 16), 96, (32, 32, 32), 1, "qk"),   # L = 288: 3 tiles, ragged
+    ("skiparse2d_single", 4, (6, 12, 16), 96, (32, 32, 32), 1, True),   # K by osp_rope3d, DMA path
+    ("skiparse2d_group", 4, (5, 8, 12), 64, (16, 24, 24), 2, "qk"),     # L = 120
+    ("skiparse2d_group", 4, (5, 8, 12), 64, (16, 24, 24), 2, False),
+    ("skiparse2d_single", 9, (4, 12, 9), 128, (32, 48, 48), 1, "qk"),   # L = 48: short kernel
+    ("skiparse2d_group", 9, (3, 18, 18), 96, (32, 32, 32), 1, "qk"),    # L = 108
+    ("skiparse2d_single", 16, (24, 8, 8), 64, (16, 24, 24), 1, "qk"),   # L = 96
+    ("skiparse2d_single", 1, (2, 6, 10), 64, (16, 24, 24), 1, "qk"),    # k = 1: full attention
+])
+def test_skiparse2d(mode, k, grid, d, split, batch, fuse):
+    run_case(71, grid=grid, n_text=0, heads=2, head_dim=d, rope_split=split, mode=mode,
+             sparse_k=k, batch=batch, fuse_rope=fuse, tag=f"{mode} k={k}")
+
+
+@pytest.mark.parametrize("grid", [(2, 4, 4), (24, 30, 40), (16, 36, 64), (3, 18, 27)])
+def test_device_index_maps_2d_bitexact(grid):
+    n = int(np.prod(grid))
+    for mode in ("skiparse2d_single", "skiparse2d_group"):
+        for k in (4, 9):
+            step = int(round(k ** 0.5)) * (1 if mode == "skiparse2d_single" else int(round(k ** 0.5)))
+            if grid[1] % step or grid[2] % step:
+                continue
+            note(f"index3d {mode} k={k} grid={grid}")
+            perm, inv = osp.osp_skiparse_index3d(mode, k, grid, device="cuda")
+            torch.cuda.synchronize()
+            want_perm, want_inv = oracle.skiparse_index(mode, k, n, grid)
+            assert np.array_equal(perm.cpu().numpy(), want_perm), (mode, k, grid)
+            assert np.array_equal(inv.cpu().numpy(), want_inv), (mode, k, grid)
+
+
 def test_suv_schedule_layers():
     # every layer of the U-shaped schedule on one 768-token grid (a multiple
     # of 8^2, so that group skip at k = 8 divides it), each against the oracle
