@@ -264,7 +264,8 @@ def main():
     sep = None
     suv = None
     if not args.no_skiparse:
-        for mode in ("skiparse_single", "skiparse_group"):
+        # Skiparse-2D group needs H and W divisible by 4 at k = 4, which 30 x 40 is not
+        for mode in ("skiparse_single", "skiparse_group", "skiparse2d_single"):
             s_step, s_launch, s_med, s_min, _ = timed(mode, 4, max(args.steps, 5), args.warmup)
             tf = flops(4) / (s_launch * 1e-3) / 1e12
             extra[mode] = {"k": 4, "ms_per_launch": round(s_launch, 4), "ms_min": round(s_min, 4),

@@ -252,7 +252,9 @@ __device__ __forceinline__ void load_row_operand(const uint16_t* row, bool valid
 // spills some loop-invariant values, which still runs 10% faster than
 // KB = 1 (forming them again in every phase instead costs more); head_dim
 // 128 takes KB = 1.
-template <int D, bool PACKED>
+// S2D: the Skiparse-2D remap is compiled in; without it the mode is known
+// to be one of the four 1D ones, so their kernels carry none of its code.
+template <int D, bool PACKED, bool S2D>
 __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int KCH = C::KCH, KB = C::KB;
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
 
   const BwdBlock wb = bwd_block<PACKED, true>(a);
   if (!wb.live) return;              // padding of a packed launch, before any barrier
-  const int mode = a.mode;
+  const int mode = S2D ? a.mode : (a.mode & 3);
   const SkipDiv divk = a.divk;
   const int L = wb.L;
   const int64_t sn = a.sn;
@@ -528,7 +530,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
 // 32-key block (C operand layout: keys are rows, the lane's query the
 // column), P = exp2 of one fma, dS^T = P o (dP^T - delta) packed to bf16,
 // and dQ^T += K^T dS^T with K^T read transposed.
-template <int D, bool PACKED>
+template <int D, bool PACKED, bool S2D>
 __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int NW = C::NW_Q;
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
 
   const BwdBlock wb = bwd_block<PACKED, false>(a);
   if (!wb.live) return;              // padding of a packed launch, before any barrier
-  const int mode = a.mode;
+  const int mode = S2D ? a.mode : (a.mode & 3);
   const SkipDiv divk = a.divk;
   const int L = wb.L;
   const int64_t sn = a.sn;
@@ -709,22 +711,28 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   hipError_t e = launch_prep_d<D>(a, s);
   if (e != hipSuccess) return e;
   const uint32_t seqs = uint32_t(a.batch) * uint32_t(a.heads) * uint32_t(a.groups);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(seqs * uint32_t(a.kv_blocks)), dim3(512), 0,
-                     s, a);
+  const dim3 kv_grid(seqs * uint32_t(a.kv_blocks)), q_grid(seqs * uint32_t(a.q_blocks));
+  if (a.mode >= MODE_SINGLE2D)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), kv_grid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), kv_grid, dim3(512), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(seqs * uint32_t(a.q_blocks)),
-                     dim3(C::NW_Q * 64), 0, s, a);
+  if (a.mode >= MODE_SINGLE2D)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), q_grid, dim3(C::NW_Q * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), q_grid, dim3(C::NW_Q * 64), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_packed_d(const BwdArgs& pa, int kv_grid, int q_grid, hipStream_t s) {
   using C = BwdCfg<D>;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(kv_grid), dim3(512), 0, s, pa);
+  // packed calls take the 1D modes only
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), dim3(kv_grid), dim3(512), 0, s, pa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(q_grid), dim3(C::NW_Q * 64), 0, s, pa);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), dim3(q_grid), dim3(C::NW_Q * 64), 0, s, pa);
   return hipGetLastError();
 }
 

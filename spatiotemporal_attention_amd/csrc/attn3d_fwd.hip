@@ -193,7 +193,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   const uint32_t h = u % uint32_t(a.heads);
   const uint32_t b = u / uint32_t(a.heads);
 
-  const int mode = a.mode;
+  // the fixed-row path serves only 1D modes, which the compiler then knows
+  const int mode = FIXED_ROWS ? (a.mode & 3) : a.mode;
   const SkipDiv divk = a.divk;
   const int64_t a_sn = a.sn;
 
