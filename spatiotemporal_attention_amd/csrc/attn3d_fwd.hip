@@ -243,18 +243,55 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     if constexpr (FIXED_ROWS) return uint32_t(int64_t(kt) * BN * kmul + tile_c0);
     else return skiparse_token(mode, uint32_t(kt * BN), j, divk, uint32_t(L));
   };
+  // Skiparse-2D rows: a tile's row dm_row[t] split once into (frames,
+  // lattice rows, columns) of the (H/s) x (W/s) lattice, packed 10 bits
+  // each (rows < 64), so that each tile's rows follow from its first row
+  // by two carries instead of three divisions.
+  const bool s2d = !FIXED_ROWS && mode >= MODE_SINGLE2D;
+  const uint32_t lat_h = divk.gh / divk.axis.d;
+  const uint32_t sn2 = uint32_t(a_sn) * 2u;
+  uint32_t dm_lat[C::DPW];
+#pragma unroll
+  for (int t = 0; t < C::DPW; ++t) {
+    const uint32_t d = uint32_t(dm_row[t]);
+    const uint32_t dt = fdiv(d, divk.plane);
+    const uint32_t rem = d - dt * divk.plane.d;
+    const uint32_t dh = fdiv(rem, divk.row);
+    dm_lat[t] = dt | (dh << 10) | ((rem - dh * divk.row.d) << 20);
+  }
   // tile kt of the tensor at src into LDS tile dst (rows past the end read
   // as zeros: their offsets are out of the buffer's range)
   auto dma_tile = [&](const uint16_t* src, int kt, uint16_t* dst) __attribute__((always_inline)) {
     const uint32_t i0 = tile_first(kt);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(src + int64_t(i0) * a_sn), (short)0, kRecords, 0x00020000);
+    // lattice position of the tile's first row, and the subsequence's (jh, jw)
+    const uint32_t r0 = uint32_t(kt * BN);
+    const uint32_t t0 = fdiv(r0, divk.plane);
+    const uint32_t h0 = fdiv(r0 - t0 * divk.plane.d, divk.row);
+    const uint32_t w0 = r0 - t0 * divk.plane.d - h0 * divk.row.d;
+    const uint32_t jh = fdiv(j, divk.axis), jw = j - jh * divk.axis.d;
 #pragma unroll
     for (int t = 0; t < C::DPW; ++t) {
       int32_t off = dm_off[t];
       if constexpr (!FIXED_ROWS) {
-        const uint32_t r = uint32_t(min(kt * BN + dm_row[t], L - 1));
-        off = int32_t((int64_t(skiparse_token(mode, r, j, divk, uint32_t(L)) - i0) * a_sn + 8 * dm_col[t]) * 2);
+        if (s2d) {
+          // rows past the end give some token here; their offset is replaced below
+          uint32_t w = w0 + (dm_lat[t] >> 20);
+          const uint32_t cw = w >= divk.row.d ? 1u : 0u;
+          w -= cw * divk.row.d;
+          uint32_t h = h0 + ((dm_lat[t] >> 10) & 1023u) + cw;
+          const uint32_t ch = h >= lat_h ? 1u : 0u;
+          h -= ch * lat_h;
+          const uint32_t tt = t0 + (dm_lat[t] & 1023u) + ch;
+          const bool grp = mode == MODE_GROUP2D;
+          const uint32_t i = (tt * divk.gh + skip_axis(grp, h, jh, divk.axis)) * divk.gw +
+                             skip_axis(grp, w, jw, divk.axis);
+          off = int32_t((i - i0) * sn2 + 16u * uint32_t(dm_col[t]));
+        } else {
+          const uint32_t r = uint32_t(min(kt * BN + dm_row[t], L - 1));
+          off = int32_t((int64_t(skiparse_token(mode, r, j, divk, uint32_t(L)) - i0) * a_sn + 8 * dm_col[t]) * 2);
+        }
       }
       off = (dm_row[t] < L - kt * BN) ? off : kRecords;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(dst + 512 * (lw + C::LW * t)), 16,
