@@ -218,6 +218,10 @@ def test_packed_checks_every_segment_before_launch():
     assert call([]) == PARAM
     assert call(good + [(0, (0, 4, 4))]) == PARAM
     assert b"segment 2" in lib.osp_last_error()
+    # Skiparse-2D depends on each segment's grid: packed calls refuse it
+    for mode in (4, 5):
+        assert call([(0, (2, 4, 4)), (0, (1, 4, 8))], mode=mode, k=4) == UNSUP
+        assert b"Skiparse-2D" in lib.osp_last_error()
     assert call(good, mode=1, k=2) == UNSUP                  # Skiparse with text tokens
     assert call([(0, (2, 4, 4)), (0, (1, 3, 5))], mode=1, k=2) == SHAPE   # 15 % 2
     assert b"segment 1" in lib.osp_last_error()
