@@ -51,9 +51,10 @@ design notes):
 
 Parity status: grid arithmetic, rotation and attention are pinned by closed
 forms, invariants, a library routine and brute force (tests/test_oracle_*.py).
-The two readings that no page value can fix -- the RoPE channel order/pairing
-(readings 2-3) and the Group Skip group size (reading 9) -- are "parity
-unpinned" against any outside implementation: the pages print no example.
+The readings that no page value can fix -- the RoPE channel order/pairing
+(readings 2-3), the Group Skip group size (reading 9) and the Skiparse-2D
+rule (reading 14) -- are "parity unpinned" against any outside
+implementation: the pages print no example.
 """
 from __future__ import annotations
 
