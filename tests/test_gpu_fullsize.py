@@ -2,7 +2,8 @@
 benchmark times (K rotated by osp_rope3d, then one osp_attn3d_fwd call
 that rotates Q in its loader, over the whole tensor; and once with K
 rotated in the loader too), checked against the fp64 oracle on seeded
-sampled query rows.  Needs an MI355X."""
+sampled query rows.  O and LSE start filled with NaN, so every element of
+both is checked to have been written.  Needs an MI355X."""
 import math
 
 import numpy as np
@@ -28,10 +29,15 @@ def run_sampled(name, mode, sparse_k, variant="as-specified", fuse_rope=True):
     note(f"full-size {name} grid={grid} shape={shape} mode={mode} k={sparse_k} variant={variant} "
          f"fuse={fuse_rope}")
     cpu, (q, k, v) = qkv_for(seed, shape, scale)
-    o, lse = osp.osp_attn3d_fwd(q, k, v, grid=grid, n_text=wl.n_text, mode=mode,
-                                sparse_k=sparse_k, rope_split=wl.rope_split, theta=wl.theta,
-                                fuse_rope=fuse_rope, return_lse=True)
+    # outputs start as NaN: every element must be written by the call
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((wl.batch, wl.heads, n), float("nan"), dtype=torch.float32, device=q.device)
+    osp.osp_attn3d_fwd(q, k, v, grid=grid, n_text=wl.n_text, mode=mode, sparse_k=sparse_k,
+                       rope_split=wl.rope_split, theta=wl.theta, fuse_rope=fuse_rope, out=o,
+                       lse=lse)
     torch.cuda.synchronize()
+    assert not torch.isnan(o).any(), "O has unwritten elements"
+    assert not torch.isnan(lse).any(), "LSE has unwritten elements"
     rows = workloads.sample_rows(wl.seed, n, SAMPLE)
     want_o, want_l = oracle_attn(cpu, grid=grid, n_text=wl.n_text, mode=mode, sparse_k=sparse_k,
                                  rope_split=wl.rope_split, theta=wl.theta, rows=rows)
@@ -40,7 +46,6 @@ def run_sampled(name, mode, sparse_k, variant="as-specified", fuse_rope=True):
     got_l = to_np(lse.index_select(2, idx))
     assert_parity(got_o, want_o, f"{name} {mode} k={sparse_k} {variant} ({len(rows)} rows)")
     assert np.abs(got_l - want_l).max() <= LSE_ABS
-    assert not torch.isnan(o).any()
 
 
 def test_osp480_full_k_rotated_in_loader():

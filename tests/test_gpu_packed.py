@@ -5,8 +5,9 @@ the short-subsequence and the flash kernel, Skiparse inside the segments,
 fused and unfused K rotation), each segment against a plain forward call on
 its slice (bit for bit: a packed launch runs the same arithmetic per
 segment), more segments than one launch's table holds, the CogVideoX
-frame pack on sampled rows, and the packed backward through the RoPE
-chain (against plain backward calls per segment and the oracle).  Needs an
+frame pack on sampled rows with NaN-filled outputs, and the packed
+backward through the RoPE chain (against plain backward calls per segment
+and the oracle; at full size element by element on one head).  Needs an
 MI355X."""
 import numpy as np
 import pytest
@@ -110,9 +111,12 @@ def test_cogvideox_frame_pack_sampled_rows():
     shape = (1, n, wl.heads, wl.head_dim)
     note(f"cogvideox frame pack segments={segs} n={n}")
     cpu, (q, k, v) = qkv_for(pk["seed"], shape)
-    o, lse = osp.osp_attn3d_packed_fwd(q, k, v, segments=segs, rope_split=wl.rope_split,
-                                       return_lse=True)
+    # outputs start as NaN: every element must be written by the call
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((1, wl.heads, n), float("nan"), dtype=torch.float32, device=q.device)
+    osp.osp_attn3d_packed_fwd(q, k, v, segments=segs, rope_split=wl.rope_split, out=o, lse=lse)
     torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
     rows = workloads.sample_rows(pk["seed"], n, pk["sample_rows"])
     hs = slice(0, 8)
     want_o, want_l = oracle.attn3d_packed(*(workloads.to_f64(t[:, :, hs]) for t in cpu),
@@ -120,7 +124,6 @@ def test_cogvideox_frame_pack_sampled_rows():
     assert_parity(to_np(o[:, rows][:, :, hs]), want_o, "O frame pack rows")
     got_l = to_np(lse[:, hs][:, :, rows])
     assert np.abs(got_l - want_l).max() <= LSE_ABS
-    assert not torch.isnan(o).any()
 
 
 # ------------------------------------------------------------------ backward
@@ -176,12 +179,17 @@ def test_packed_bwd_equals_plain_calls_and_oracle(mode, k, segs):
         start = end
 
 
-def test_packed_bwd_frame_pack_sampled_rows():
+def test_packed_bwd_frame_pack_full_size():
     """The CogVideoX frame pack's backward at full size (the launches the
-    benchmark times): sampled dQ rows of every segment, each exact in the
-    oracle from the same bf16 rotated inputs (a row's dQ needs only its own
-    scores), and per segment the column identities of dK (sum 0) and dV
-    (sum of dO), for two of the 48 heads."""
+    benchmark times), through the RoPE chain: rope3d_packed of q and k,
+    the packed forward, the packed backward into NaN-filled gradients
+    (every element must be written), then rope3d_packed_inv of dq and dk.
+    For head 0, every segment's dq, dk and dv are compared element by
+    element with the oracle's gradients with respect to the unrotated
+    inputs (the 17,776-token segment is one 17,776 x 17,776 fp64 problem).
+    For head 1, per segment, the column identities of the gradients with
+    respect to the rotated k and v: dK sums to 0 over a segment's keys and
+    dV to the sum of dO over its queries."""
     pk = workloads.COGVIDEOX_PACK
     wl = workloads.WORKLOADS[pk["base"]]
     segs = [(pk["n_text"], osp.osp_latent_grid(*clip, wl.c_t, wl.c_s, wl.p_t, wl.p_s))
@@ -195,25 +203,28 @@ def test_packed_bwd_frame_pack_sampled_rows():
     kr = osp.osp_rope3d_packed(k, segments=segs, rope_split=wl.rope_split)
     o, lse = osp.osp_attn3d_packed_fwd(qr, kr, v, segments=segs, rope_split=wl.rope_split,
                                        fuse_rope=False, return_lse=True)
-    dq, dk, dv = osp.osp_attn3d_packed_bwd(qr, kr, v, o, lse, do_cpu.cuda(), segments=segs)
+    grads = [torch.full_like(q, float("nan")) for _ in range(3)]
+    osp.osp_attn3d_packed_bwd(qr, kr, v, o, lse, do_cpu.cuda(), segments=segs, dq=grads[0],
+                              dk=grads[1], dv=grads[2])
+    gq = osp.osp_rope3d_packed_inv(grads[0], segments=segs, rope_split=wl.rope_split)
+    gk = osp.osp_rope3d_packed_inv(grads[1], segments=segs, rope_split=wl.rope_split)
     torch.cuda.synchronize()
-    hs = slice(0, 2)
-    qw, kw = to_np(qr[:, :, hs]), to_np(kr[:, :, hs])
-    vw, dow = workloads.to_f64(cpu[2][:, :, hs]), workloads.to_f64(do_cpu[:, :, hs])
-    got_q, got_k, got_v = to_np(dq[:, :, hs]), to_np(dk[:, :, hs]), to_np(dv[:, :, hs])
+    for name, g in zip(("dq", "dk", "dv"), grads):
+        assert not torch.isnan(g).any(), f"{name} has unwritten elements"
+    got0 = [to_np(t[:, :, 0:1]) for t in (gq, gk, grads[2])]
+    got_k1, got_v1 = to_np(grads[1][:, :, 1]), to_np(grads[2][:, :, 1])
+    dow1 = workloads.to_f64(do_cpu[:, :, 1])
     start = 0
     for s_i, (nt, g) in enumerate(segs):
         end = start + nt + int(np.prod(g))
-        rows = start + workloads.sample_rows(pk["seed"] + s_i, end - start, 16)
-        for h in range(2):
-            want_q, _, _ = oracle.softmax_attention_bwd(qw[0, rows, h], kw[0, start:end, h],
-                                                        vw[0, start:end, h], dow[0, rows, h],
-                                                        1.0 / np.sqrt(wl.head_dim))
-            assert_parity(got_q[0, rows, h], want_q, f"dq segment {s_i} h={h}",
-                          BWD_MAX_REL * float(np.abs(want_q).max()), BWD_REL_L2)
-            gk, gv = got_k[0, start:end, h], got_v[0, start:end, h]
-            assert (np.abs(gk.sum(axis=0)) <= 1e-2 * np.abs(gk).sum(axis=0)).all()
-            want_dv = dow[0, start:end, h].sum(axis=0)
-            assert (np.abs(gv.sum(axis=0) - want_dv) <= 1e-2 * np.abs(gv).sum(axis=0)).all()
+        want = oracle.attn3d_bwd(*(workloads.to_f64(t[:, start:end, 0:1]) for t in (*cpu, do_cpu)),
+                                 grid=g, n_text=nt, rope_split=wl.rope_split)
+        for name, got, w in zip(("dq", "dk", "dv"), got0, want):
+            assert_parity(got[:, start:end], w, f"{name} segment {s_i} h=0",
+                          BWD_MAX_REL * float(np.abs(w).max()),
+                          BWD_REL_L2 if name == "dv" else BWD_REL_L2_ROPE)
+        gk1, gv1 = got_k1[0, start:end], got_v1[0, start:end]
+        assert (np.abs(gk1.sum(axis=0)) <= 1e-2 * np.abs(gk1).sum(axis=0)).all()
+        want_dv = dow1[0, start:end].sum(axis=0)
+        assert (np.abs(gv1.sum(axis=0) - want_dv) <= 1e-2 * np.abs(gv1).sum(axis=0)).all()
         start = end
-    assert not torch.isnan(dq).any() and not torch.isnan(dk).any() and not torch.isnan(dv).any()

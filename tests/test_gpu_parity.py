@@ -122,7 +122,7 @@ def test_separated_spatial_temporal(half):
 
 @pytest.mark.parametrize("variant", ["unscaled", "literal", "sharp"])
 @pytest.mark.parametrize("mode,k", [("full", 1), ("skiparse_single", 4), ("skiparse_group", 4),
-                                    ("skiparse_group", 2), ("block", 3)])
+                                    ("skiparse_group", 2), ("skiparse_group", 3), ("block", 3)])
 def test_multitile_d96(variant, mode, k):
     # 720 tokens: several 256-row query tiles and 64-key tiles, ragged tails.
     # "sharp" multiplies Q by 4 (logit std ~4 instead of ~1).  The kernel
@@ -134,6 +134,19 @@ def test_multitile_d96(variant, mode, k):
     run_case(10, grid=(4, 12, 15), n_text=0, heads=3, head_dim=96, rope_split=(32, 32, 32),
              mode=mode, sparse_k=k, scale=scale, q_mult=q_mult, tag=f"mt96-{variant}-{mode}{k}",
              tol=4.0 if variant == "sharp" else 1.0)
+
+
+@pytest.mark.parametrize("fuse", ["qk", True])
+def test_group_skip_k_not_dividing_the_key_tile(fuse):
+    # Group Skip with k = 3 against 32-key tiles (D=64): a tile's rows do not
+    # sit at fixed offsets from its first token, so the loader remaps every
+    # row (the path Group Skip takes whenever k does not divide the tile).
+    # 288 tokens, L = 96: three key tiles per subsequence; batch 2.
+    run_case(24, grid=(3, 8, 12), n_text=0, heads=2, head_dim=64, rope_split=(16, 24, 24),
+             mode="skiparse_group", sparse_k=3, batch=2, fuse_rope=fuse, tag="group3-d64")
+    # k = 5 at D=128 (64-key tiles), 1,200 tokens: L = 240, ragged last tile
+    run_case(24, grid=(3, 20, 20), n_text=0, heads=2, head_dim=128, rope_split=(32, 48, 48),
+             mode="skiparse_group", sparse_k=5, fuse_rope=fuse, tag="group5-d128")
 
 
 @pytest.mark.parametrize("mode,k,grid,d,split,batch,fuse", [
