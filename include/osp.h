@@ -275,6 +275,26 @@ osp_status osp_attn3d_bwd(const osp_attn3d_desc* desc, int32_t mode,
                           void* dk, void* dv, void* workspace,
                           int64_t workspace_bytes, void* stream);
 
+/* osp_attn3d_bwd without a workspace argument, for callers that cannot
+   allocate device memory (code under stream capture, serving loops,
+   harnesses that forbid allocation).  It calls no allocator: the two fp32
+   row arrays live in a 32 MiB device array inside the library, one per
+   GPU, held until the process ends; its address is looked up once per
+   device.  The call runs on the CURRENT HIP device (stream must belong to
+   it).  Limit: 2 * roundup256(4 * B * H * N) <= 32 MiB, i.e. B*H*N up to
+   4,194,304 rows (OSP_ERR_SHAPE beyond it, before anything is enqueued).
+   Every call on one GPU shares that array, and nothing in it needs to start
+   at zero (each call writes the rows it reads before reading them), so
+   calls that overlap in time on one GPU (other streams, other threads)
+   RACE: serialise them.  Arguments, results and other errors as
+   osp_attn3d_bwd; the results are bit-identical to it. */
+osp_status osp_attn3d_bwd_noalloc(const osp_attn3d_desc* desc, int32_t mode,
+                                  int32_t sparse_k, float sm_scale,
+                                  const void* q, const void* k, const void* v,
+                                  const void* o, const float* lse,
+                                  const void* dout, void* dq, void* dk, void* dv,
+                                  void* stream);
+
 /* Bytes of device workspace osp_attn3d_packed_bwd needs: two fp32
    [B, H, N] arrays over the packed N, each rounded up to 256 bytes.
    Checks every segment as osp_attn3d_packed_bwd does.  Host only. */

@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
                                             P, P, P, P, P, P, P, P, P, P, I64, P]),
             "osp_attn3d_bwd_workspace": (I32, [D, I32, I32, ctypes.POINTER(I64)]),
             "osp_attn3d_bwd": (I32, [D, I32, I32, F32, P, P, P, P, P, P, P, P, P, P, I64, P]),
+            "osp_attn3d_bwd_noalloc": (I32, [D, I32, I32, F32, P, P, P, P, P, P, P, P, P, P]),
             "osp_skiparse_index": (I32, [I32, I32, I64, P, P, I32, P]),
             "osp_skiparse_index3d": (I32, [I32, I32, I32, I32, I32, P, P, I32, P]),
         }
@@ -101,7 +102,8 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("osp_abi_version", "osp_status_string", "osp_last_error", "osp_latent_grid",
             "osp_attn3d_check", "osp_rope3d", "osp_rope3d_inv", "osp_attn3d_fwd",
             "osp_attn3d_packed_fwd", "osp_rope3d_packed", "osp_rope3d_packed_inv",
-            "osp_attn3d_bwd_workspace", "osp_attn3d_bwd", "osp_attn3d_packed_bwd_workspace",
+            "osp_attn3d_bwd_workspace", "osp_attn3d_bwd", "osp_attn3d_bwd_noalloc",
+            "osp_attn3d_packed_bwd_workspace",
             "osp_attn3d_packed_bwd", "osp_skiparse_index", "osp_skiparse_index3d")
 
 
@@ -370,6 +372,35 @@ def osp_attn3d_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
         *(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o, lse, dout, *outs, workspace)),
         int(workspace.numel() * workspace.element_size()), _stream(q)))
     return tuple(outs)
+
+
+def osp_attn3d_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                           lse: torch.Tensor, dout: torch.Tensor, *, grid, n_text: int = 0,
+                           mode="full", sparse_k: int = 1, sm_scale: float | None = None,
+                           dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor):
+    """osp_attn3d_bwd without a workspace: the library's own per-GPU scratch
+    array holds the row terms, and the call allocates nothing (dq, dk and
+    dv are required).  Runs on q's device; calls that overlap on one GPU
+    race on the scratch.  Returns (dq, dk, dv)."""
+    b, n, h, d = q.shape
+    st = _bnhd(q, "q")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if _bnhd(t, name) != st or t.shape != q.shape:
+            raise ValueError("q, k, v, o and dout must share shape and strides")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (b, h, n) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    ost = _bnhd(dq, "dq")
+    if any(_bnhd(t, "dk/dv") != ost or tuple(t.shape) != (b, n, h, d) for t in (dq, dk, dv)):
+        raise ValueError("dq, dk and dv must share the shape of q and one set of strides")
+    desc = make_desc(batch=b, n_text=n_text, grid=grid, heads=h, head_dim=d,
+                     rope_split=(d, 0, 0), strides=st, ostrides=ost)
+    with torch.cuda.device(q.device):
+        _check(lib().osp_attn3d_bwd_noalloc(
+            ctypes.byref(desc), _mode(mode), int(sparse_k),
+            float(sm_scale) if sm_scale is not None else 0.0,
+            *(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o, lse, dout, dq, dk, dv)),
+            _stream(q)))
+    return dq, dk, dv
 
 
 def osp_attn3d_packed_bwd_workspace(desc: OspAttn3dDesc, segments, mode="full",

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -390,6 +391,42 @@ osp_status enqueue_bwd(const osp_attn3d_desc* desc, const Shape& s, int32_t mode
 
 }  // namespace
 
+// Device scratch of osp_attn3d_bwd_noalloc: the backward's two fp32 row
+// arrays (-delta and -lse/scale, bwd_ws_half bytes each) for callers that
+// cannot allocate.  Every GPU the library runs on holds one copy, at its own
+// address, until the process ends.  In host code the name is only a handle:
+// kernels get the device address that hipGetSymbolAddress returns for the
+// current device (noalloc_scratch below).
+constexpr int64_t kNoAllocScratchBytes = int64_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's scratch, looked up once per
+// device (with that device current) and kept.
+osp_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_error(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(OSP_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return device_error(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return OSP_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t osp_abi_version(void) { return OSP_ABI_VERSION; }
@@ -700,6 +737,34 @@ osp_status osp_attn3d_bwd(const osp_attn3d_desc* desc, int32_t mode, int32_t spa
   float* ws = static_cast<float*>(workspace);
   return enqueue_bwd(desc, s, mode, sparse_k, sm_scale, q, k, v, o, lse, s.n_tokens, dout, dq, dk,
                      dv, ws, reinterpret_cast<float*>(static_cast<char*>(workspace) + half),
+                     static_cast<hipStream_t>(stream));
+}
+
+osp_status osp_attn3d_bwd_noalloc(const osp_attn3d_desc* desc, int32_t mode, int32_t sparse_k,
+                                  float sm_scale, const void* q, const void* k, const void* v,
+                                  const void* o, const float* lse, const void* dout, void* dq,
+                                  void* dk, void* dv, void* stream) {
+  Shape s;
+  osp_status st = check_bwd(desc, mode, sparse_k, &s);
+  if (st) return st;
+  // the pointer check wants a workspace: pass a stand-in aligned address
+  // (the scratch itself is looked up below)
+  st = check_bwd_pointers(q, k, v, o, lse, dout, dq, dk, dv,
+                          reinterpret_cast<void*>(uintptr_t(256)), sm_scale);
+  if (st) return st;
+  const int64_t half = bwd_ws_half(desc->batch, desc->heads, s.n_tokens);
+  if (2 * half > kNoAllocScratchBytes)
+    return fail(OSP_ERR_SHAPE,
+                "osp_attn3d_bwd_noalloc: batch*heads*N = %lld rows need %lld bytes of scratch, "
+                "more than its %lld; use osp_attn3d_bwd with a workspace",
+                (long long)(int64_t(desc->batch) * desc->heads * s.n_tokens),
+                (long long)(2 * half), (long long)kNoAllocScratchBytes);
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st) return st;
+  return enqueue_bwd(desc, s, mode, sparse_k, sm_scale, q, k, v, o, lse, s.n_tokens, dout, dq, dk,
+                     dv, static_cast<float*>(ws),
+                     reinterpret_cast<float*>(static_cast<char*>(ws) + half),
                      static_cast<hipStream_t>(stream));
 }
 

@@ -321,3 +321,20 @@ def test_last_error_is_per_thread():
     for t in threads:
         t.join()
     assert not failures, failures[:3]
+
+
+def test_bwd_noalloc_rejects_beyond_its_scratch_on_the_host():
+    """osp_attn3d_bwd_noalloc refuses, before touching any device, a call
+    whose two row arrays exceed its 32 MiB scratch (B*H*N > 4,194,304), and
+    accepts the argument checks of osp_attn3d_bwd otherwise (here it stops
+    at a NULL pointer first).  The pointers are never dereferenced."""
+    lib = osp.lib()
+    fake = ctypes.c_void_p(1 << 20)                       # aligned, never read
+    big = _desc(batch=2, grid=(24, 45, 80), heads=24, head_dim=64)     # 4,147,200 rows: fits
+    bigger = _desc(batch=3, grid=(24, 45, 80), heads=24, head_dim=64)  # 6,220,800 rows
+    args = [fake] * 9 + [None]
+    assert lib.osp_attn3d_bwd_noalloc(ctypes.byref(bigger), 0, 1, 0.0, *args) == SHAPE
+    assert b"scratch" in lib.osp_last_error()
+    nulls = [fake] * 8 + [None, None]
+    assert lib.osp_attn3d_bwd_noalloc(ctypes.byref(big), 0, 1, 0.0, *nulls) == NULL
+    assert lib.osp_attn3d_bwd_noalloc(ctypes.byref(bigger), 1, 3, 0.0, *args) == SHAPE
