@@ -11,11 +11,17 @@ tokens and the output written back in token order (osp_attn3d_fwd).
 Inputs are resident in HBM before timing.
 
 Prints ONE JSON line.  value = algorithmic attention TFLOP/s
-(4*B*H*N^2*D / k per call).  Also reported: the same kernel on Skiparse k=4
-(single and group skip), the roofline of the attention kernel (MFMA bound,
-dense bf16 peak 2516.6 TFLOP/s), HBM traffic from rocprofv3 counters (when
-taken on the current kernel source) and the fp64 CPU oracle's rate on a
-bounded sample.
+(4*B*H*N^2*D / k per call).  Also reported, each timed the same way
+(``configs``): Skiparse k=4 (single and group skip) on the same tensors,
+CogVideoX's joint attention (17,776 tokens, 48 heads of 64) and the 720p
+workload (86,400 tokens, full and Skiparse k=4); the roofline of the
+attention kernel (MFMA bound, dense bf16 peak 2516.6 TFLOP/s); MFMA
+utilisation, clock and HBM traffic from committed rocprofv3 counters (when
+taken on the current kernel source); and the fp64 CPU oracle's rate on a
+bounded sample, with the GPU output's error against it on that sample.
+
+``--summarize DIR ...`` instead reads rocprofv3 counter directories and
+prints the per-line counter summary that ``profiles/counters.json`` holds.
 """
 from __future__ import annotations
 
@@ -32,29 +38,47 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 KERNEL_SRC = os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", "attn3d_fwd.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn3d_fwd_osp480_traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+
+# Timed lines besides the headline: name -> (workload, mode, k).  Each is
+# one osp_rope3d of K plus one osp_attn3d_fwd launch, as the headline step.
+LINES = {
+    "osp480_full": ("osp480", "full", 1),
+    "osp480_skiparse_single_k4": ("osp480", "skiparse_single", 4),
+    "osp480_skiparse_group_k4": ("osp480", "skiparse_group", 4),
+    "osp480_skiparse2d_single_k4": ("osp480", "skiparse2d_single", 4),
+    "cogvideox_joint_full": ("cogvideox", "full", 1),
+    "osp720_full": ("osp720", "full", 1),
+    "osp720_skiparse_single_k4": ("osp720", "skiparse_single", 4),
+    "osp720_skiparse_group_k4": ("osp720", "skiparse_group", 4),
+}
 
 
-def kernel_source_hash() -> str:
+FWD_SOURCES = ("attn3d_fwd.hip", "osp_mfma.hpp", "osp_rope.hpp", "osp_common.hpp",
+               "osp_internal.hpp")
+BWD_SOURCES = ("attn3d_bwd.hip", "osp_mfma.hpp", "osp_common.hpp", "osp_internal.hpp")
+
+
+def kernel_source_hash(sources=FWD_SOURCES) -> str:
+    """Hash of the kernel sources a counter summary was taken on."""
     h = hashlib.sha256()
-    for name in ("attn3d_fwd.hip", "osp_mfma.hpp", "osp_rope.hpp", "osp_common.hpp",
-                 "osp_internal.hpp"):
+    for name in sources:
         with open(os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per launch from committed rocprofv3 counters, if they were
-    taken on the current kernel source; else None."""
+def load_counters():
+    """Per-line counter summaries (profiles/counters.json) taken on the
+    current kernel source; lines taken on another source are dropped."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTERS_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return t.get("hbm_bytes_per_launch")
+        return {}
+    hashes = {"fwd": kernel_source_hash(FWD_SOURCES), "bwd": kernel_source_hash(BWD_SOURCES)}
+    return {name: c for name, c in t.get("lines", {}).items()
+            if c.get("kernel_source_hash") == hashes.get(c.get("sources", "fwd"))}
 
 
 def parse():
@@ -62,27 +86,96 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--no-skiparse", action="store_true", help="skip the Skiparse k=4 lines")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the lines besides the headline (Skiparse, CogVideoX, 720p)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the separated 2D+1D, SUV-schedule, frame-pack and backward lines")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=6,
                    help="heads of the workload the oracle times (all query rows each)")
     p.add_argument("--profile", action="store_true",
-                   help="few steps of one attention mode only (for rocprofv3)")
+                   help="few steps of one line only (for rocprofv3)")
     p.add_argument("--no-backward", action="store_true", help="skip the backward line")
-    p.add_argument("--no-packed", action="store_true", help="skip the frame-pack line")
-    p.add_argument("--profile-mode", default="full",
-                   choices=("full", "skiparse_single", "skiparse_group", "bwd", "temporal",
-                            "packed"),
-                   help="what --profile runs: attention over the 28,800-token workload (Skiparse "
-                        "with k=4; temporal: Single Skip with k = H*W), its backward (bwd), or the "
-                        "CogVideoX frame pack (packed)")
+    p.add_argument("--no-packed", action="store_true", help="skip the frame-pack lines")
+    p.add_argument("--profile-mode", default="osp480_full",
+                   choices=tuple(LINES) + ("bwd", "temporal", "spatial", "packed", "packed_bwd"),
+                   help="what --profile runs: one of the timed lines, the backward on the "
+                        "28,800-token workload (bwd), its temporal (Single Skip, k = H*W) or "
+                        "spatial (block, k = T) attention, or the CogVideoX frame pack "
+                        "(packed, packed_bwd)")
     p.add_argument("--copy", type=int, default=0,
                    help="instead: time a plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--summarize", nargs="+", metavar="DIR",
+                   help="instead: summarise rocprofv3 --pmc output directories (see summarize())")
+    p.add_argument("--line", help="with --summarize: the line name the counters were taken on")
+    p.add_argument("--kernel", default="attn3d_fwd",
+                   help="with --summarize: substring of the kernel name to keep")
     return p.parse_args()
+
+
+# ----------------------------------------------------------- counter summary
+def _read_counter_csv(path):
+    """{(dispatch, kernel): {counter: value, "_ns": duration}} from a
+    rocprofv3 counter CSV."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            key = (row.get("Dispatch_Id"), row.get("Kernel_Name"))
+            d = out.setdefault(key, {})
+            d[row["Counter_Name"]] = float(row["Counter_Value"])
+            if row.get("End_Timestamp"):
+                d["_ns"] = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+    return out
+
+
+def summarize(dirs, line, kernel_sub):
+    """Mean per dispatch of every counter found under the rocprofv3 output
+    directories ``dirs`` (one ``--pmc`` pass each), for dispatches of
+    kernels whose name contains ``kernel_sub``; plus the figures derived
+    from them.  FETCH_SIZE and WRITE_SIZE are in KiB; the factors that turn
+    them into bytes come from a plain device copy (``--copy``): FETCH_SIZE
+    reads half the bytes a copy moves (factor 2), WRITE_SIZE all of them
+    (factor 1)."""
+    import glob
+    means, durations, kernels = {}, [], set()
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            per = [(name, v) for (disp, name), v in _read_counter_csv(path).items()
+                   if kernel_sub in name]
+            kernels.update(name for name, _ in per)
+            durations += [v["_ns"] for _, v in per if "_ns" in v]
+            for cname in sorted({c for _, v in per for c in v} - {"_ns"}):
+                vals = [v[cname] for _, v in per if cname in v]
+                # GRBM_GUI_ACTIVE is read in every pass: keep each pass's mean
+                means.setdefault(cname, []).append(sum(vals) / len(vals))
+    means = {c: sum(v) / len(v) for c, v in means.items()}
+    bwd = kernel_sub.startswith("bwd")
+    rec = {"line": line, "kernel_filter": kernel_sub, "kernels": sorted(kernels),
+           "sources": "bwd" if bwd else "fwd",
+           "kernel_source_hash": kernel_source_hash(BWD_SOURCES if bwd else FWD_SOURCES),
+           "counters": means}
+    if durations:
+        rec["ms_per_dispatch"] = round(sum(durations) / len(durations) * 1e-6, 4)
+    if "GRBM_GUI_ACTIVE" in means:
+        # GRBM_GUI_ACTIVE sums the GPU-busy cycles of the 8 XCDs
+        busy = means["GRBM_GUI_ACTIVE"] / 8.0
+        rec["gpu_busy_cycles"] = busy
+        if durations:
+            rec["sclk_mhz"] = round(busy / (rec["ms_per_dispatch"] * 1e3))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in means:
+            # MFMA busy cycles sum over the 1024 SIMDs
+            rec["mfma_util"] = round(means["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0 / busy, 4)
+    if "FETCH_SIZE" in means and "WRITE_SIZE" in means:
+        rec["hbm_bytes_per_launch"] = int((means["FETCH_SIZE"] * 2.0 + means["WRITE_SIZE"]) * 1024)
+    return rec
 
 
 def main():
     args = parse()
+    if args.summarize:
+        print(json.dumps(summarize(args.summarize, args.line, args.kernel), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(each attention unit (batch, head, subsequence) is independent; "
@@ -97,6 +190,7 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
 
     if args.copy:
         n = args.copy * (1 << 20) // 4
@@ -108,28 +202,69 @@ def main():
         print(json.dumps({"copy_mib": args.copy, "bytes_read": n * 4, "bytes_written": n * 4}))
         return
 
-    wl = workloads.WORKLOADS["osp480"]
-    grid = osp.osp_latent_grid(*wl.clip, wl.c_t, wl.c_s, wl.p_t, wl.p_s)      # row a1 on the host
-    n_tok = wl.n_text + grid[0] * grid[1] * grid[2]
-    B, H, D = wl.batch, wl.heads, wl.head_dim
-    shape = (B, n_tok, H, D)
-    q, k, v = (t.to(dev) for t in workloads.make_qkv(wl.seed, shape, wl.input_scale))
-    o = torch.empty_like(q)
-    k_rot = torch.empty_like(k)
-    stream = torch.cuda.current_stream(dev)
+    class Work:
+        """One workload's tensors, resident on the device: q, k, v, the
+        rotated K the step writes, and o."""
 
-    def step(mode="full", sk=1, marks=None):
-        osp.osp_rope3d(k, grid=grid, n_text=wl.n_text, rope_split=wl.rope_split,
-                       theta=wl.theta, out=k_rot)
-        if marks:
-            marks[0].record(stream)
-        osp.osp_attn3d_fwd(q, k_rot, v, grid=grid, n_text=wl.n_text, mode=mode, sparse_k=sk,
-                           rope_split=wl.rope_split, theta=wl.theta, fuse_rope="q", out=o)
-        if marks:
-            marks[1].record(stream)
+        def __init__(self, name):
+            wl = workloads.WORKLOADS[name]
+            self.wl = wl
+            self.grid = osp.osp_latent_grid(*wl.clip, wl.c_t, wl.c_s, wl.p_t, wl.p_s)   # a1
+            self.n = wl.n_text + self.grid[0] * self.grid[1] * self.grid[2]
+            self.shape = (wl.batch, self.n, wl.heads, wl.head_dim)
+            self.q, self.k, self.v = (t.to(dev) for t in
+                                      workloads.make_qkv(wl.seed, self.shape, wl.input_scale))
+            self.o = torch.empty_like(self.q)
+            self.k_rot = torch.empty_like(self.k)
 
-    def flops(sk=1):
-        return 4.0 * B * H * float(n_tok) ** 2 * D / sk
+        def step(self, mode="full", sk=1, marks=None):
+            wl = self.wl
+            osp.osp_rope3d(self.k, grid=self.grid, n_text=wl.n_text, rope_split=wl.rope_split,
+                           theta=wl.theta, out=self.k_rot)
+            if marks:
+                marks[0].record(stream)
+            osp.osp_attn3d_fwd(self.q, self.k_rot, self.v, grid=self.grid, n_text=wl.n_text,
+                               mode=mode, sparse_k=sk, rope_split=wl.rope_split, theta=wl.theta,
+                               fuse_rope="q", out=self.o)
+            if marks:
+                marks[1].record(stream)
+
+        def flops(self, sk=1):
+            wl = self.wl
+            return 4.0 * wl.batch * wl.heads * float(self.n) ** 2 * wl.head_dim / sk
+
+        def timed(self, mode, sk, steps, warmup):
+            """(ms per step, mean / median / min ms per attention launch)."""
+            for _ in range(warmup):
+                self.step(mode, sk)
+            torch.cuda.synchronize()
+            # per-launch events on the launch stream (the kernel's own duration)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps)]
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0.record(stream)
+            for marks in evs:
+                self.step(mode, sk, marks)     # events bracket the attention launch
+            t1.record(stream)
+            torch.cuda.synchronize()
+            per = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+            return t0.elapsed_time(t1) / steps, sum(per) / len(per), per[len(per) // 2], per[0]
+
+    works = {}
+
+    def work(name):
+        if name not in works:
+            works.clear()          # one workload resident at a time
+            torch.cuda.empty_cache()
+            works[name] = Work(name)
+        return works[name]
+
+    main_w = work("osp480")
+    grid, B, H, D, n_tok = main_w.grid, main_w.wl.batch, main_w.wl.heads, main_w.wl.head_dim, main_w.n
+    wl = main_w.wl
+    q, k, v, k_rot = main_w.q, main_w.k, main_w.v, main_w.k_rot
 
     # backward: gradients with respect to the rotated q and k (then through
     # the RoPE transpose), from the forward's o and lse
@@ -138,6 +273,7 @@ def main():
     def bwd_setup():
         if bwd_state:
             return bwd_state
+        shape = main_w.shape
         q_rot = osp.osp_rope3d(q, grid=grid, n_text=wl.n_text, rope_split=wl.rope_split,
                                theta=wl.theta)
         osp.osp_rope3d(k, grid=grid, n_text=wl.n_text, rope_split=wl.rope_split,
@@ -217,67 +353,82 @@ def main():
         if pm == "bwd":
             bwd_setup()
             run = bwd_step
-        elif pm == "packed":
+        elif pm in ("packed", "packed_bwd"):
             run = packed_setup()[0]
+            if pm == "packed_bwd":
+                run = run.bwd_setup()
         elif pm == "temporal":
-            run = lambda: step("skiparse_single", grid[1] * grid[2])   # noqa: E731
+            run = lambda: main_w.step("skiparse_single", grid[1] * grid[2])   # noqa: E731
+        elif pm == "spatial":
+            run = lambda: main_w.step("block", grid[0])   # noqa: E731
         else:
-            pk = 1 if pm == "full" else 4
-            run = lambda: step(pm, pk)   # noqa: E731
+            wname, mode, sk = LINES[pm]
+            w = work(wname)
+            run = lambda: w.step(mode, sk)   # noqa: E731
         for _ in range(max(args.warmup, 1)):
             run()
         torch.cuda.synchronize()
         for _ in range(max(args.steps, 1)):
             run()
         torch.cuda.synchronize()
-        print(json.dumps({"profile_launches": args.steps, "workload": f"osp480 {pm}"}))
+        print(json.dumps({"profile_launches": args.steps, "line": pm}))
         return
 
-    def timed(mode, sk, steps, warmup):
-        for _ in range(warmup):
-            step(mode, sk)
-        torch.cuda.synchronize()
-        # per-launch events on the launch stream (the kernel's own duration)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t_wall = time.perf_counter()
-        t0.record(stream)
-        for marks in evs:
-            step(mode, sk, marks)     # events bracket the attention launch
-        t1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t_wall
-        total_ms = t0.elapsed_time(t1)
-        per = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
-        return total_ms / steps, sum(per) / len(per), per[len(per) // 2], per[0], wall
+    counters = load_counters()
 
-    ms_step, ms_launch, ms_med, ms_min, wall = timed("full", 1, args.steps, args.warmup)
-    f_full = flops(1)
+    def line_record(name, ms_step, ms_launch, ms_med, ms_min):
+        wname, mode, sk = LINES[name]
+        w = work(wname)
+        f = w.flops(sk)
+        tf = f / (ms_launch * 1e-3) / 1e12
+        rec = {"workload": wname, "mode": mode, "k": sk, "N": w.n, "B": w.wl.batch,
+               "H": w.wl.heads, "D": w.wl.head_dim, "n_text": w.wl.n_text,
+               "ms_per_launch": round(ms_launch, 4), "ms_median": round(ms_med, 4),
+               "ms_min": round(ms_min, 4), "ms_per_step_with_k_rope": round(ms_step, 4),
+               "flop_per_launch": f, "tflops_alg": round(tf, 2),
+               "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+               "tflops_dense_equiv": round(w.flops(1) / (ms_launch * 1e-3) / 1e12, 2)}
+        c = counters.get(name)
+        if c:
+            if "mfma_util" in c:
+                rec["mfma_util"] = c["mfma_util"]
+                # the clock the chip held: GPU-busy cycles per XCD over the
+                # counted run's own mean kernel duration
+                if c.get("sclk_mhz"):
+                    rec["sclk_mhz"] = c["sclk_mhz"]
+            if "hbm_bytes_per_launch" in c:
+                rec["hbm_bytes_per_launch"] = c["hbm_bytes_per_launch"]
+                rec["hbm_gbps"] = round(c["hbm_bytes_per_launch"] / (ms_launch * 1e-3) / 1e9, 1)
+        return rec
+
+    ms_step, ms_launch, ms_med, ms_min = main_w.timed("full", 1, args.steps, args.warmup)
+    f_full = main_w.flops(1)
     value = f_full / (ms_step * 1e-3) / 1e12
     achieved = f_full / (ms_launch * 1e-3) / 1e12
-    traffic = load_traffic()
+    head_rec = line_record("osp480_full", ms_step, ms_launch, ms_med, ms_min)
+    traffic = head_rec.get("hbm_bytes_per_launch")
 
-    extra = {}
+    configs = {"osp480_full": head_rec}
     sep = None
     suv = None
-    if not args.no_skiparse:
-        # Skiparse-2D group needs H and W divisible by 4 at k = 4, which 30 x 40 is not
-        for mode in ("skiparse_single", "skiparse_group", "skiparse2d_single"):
-            s_step, s_launch, s_med, s_min, _ = timed(mode, 4, max(args.steps, 5), args.warmup)
-            tf = flops(4) / (s_launch * 1e-3) / 1e12
-            extra[mode] = {"k": 4, "ms_per_launch": round(s_launch, 4), "ms_min": round(s_min, 4),
-                           "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                           "dense_equiv_tflops": round(f_full / (s_launch * 1e-3) / 1e12, 2)}
+    if not args.no_configs:
+        nl = max(args.steps // 2, 5)
+        for name, (wname, mode, sk) in LINES.items():
+            if name == "osp480_full":
+                continue
+            w = work(wname)
+            t = w.timed(mode, sk, nl if wname == "osp720" else max(args.steps, 5), args.warmup)
+            configs[name] = line_record(name, *t)
+        main_w = work("osp480")
+        q, k, v, k_rot = main_w.q, main_w.k, main_w.v, main_w.k_rot
+    if not args.no_extras:
         # separated spatial / temporal attention on the same tensors: block
         # attention over each frame, then single skip over each (h, w) position
         sep = {}
         for name, mode, kk in (("spatial", "block", grid[0]),
                                ("temporal", "skiparse_single", grid[1] * grid[2])):
-            _, s_launch, _, s_min, _ = timed(mode, kk, max(args.steps, 5), args.warmup)
-            tf = flops(kk) / (s_launch * 1e-3) / 1e12
+            _, s_launch, _, s_min = main_w.timed(mode, kk, max(args.steps, 5), args.warmup)
+            tf = main_w.flops(kk) / (s_launch * 1e-3) / 1e12
             sep[name] = {"mode": mode, "k": kk, "ms_per_launch": round(s_launch, 4),
                          "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
         sep["ms_spatial_plus_temporal"] = round(sep["spatial"]["ms_per_launch"] +
@@ -289,9 +440,9 @@ def main():
         per = {}
         for mode, kk in workloads.SUV_SCHEDULE:
             if (mode, kk) not in per:
-                per[(mode, kk)] = timed(mode, kk, max(args.steps // 2, 5), args.warmup)[1]
+                per[(mode, kk)] = main_w.timed(mode, kk, max(args.steps // 2, 5), args.warmup)[1]
         ms_pass = sum(per[mk] for mk in workloads.SUV_SCHEDULE)
-        f_pass = sum(flops(kk) for _, kk in workloads.SUV_SCHEDULE)
+        f_pass = sum(main_w.flops(kk) for _, kk in workloads.SUV_SCHEDULE)
         suv = {"schedule": [[m, kk] for m, kk in workloads.SUV_SCHEDULE],
                "ms_per_pass": round(ms_pass, 4),
                "ms_all_full": round(len(workloads.SUV_SCHEDULE) * ms_launch, 4),
@@ -299,7 +450,7 @@ def main():
                "tflops": round(f_pass / (ms_pass * 1e-3) / 1e12, 2)}
 
     packed = None
-    if not args.no_packed:
+    if not args.no_packed and not args.no_extras:
         runp, segs, lens, wlc = packed_setup()
         for _ in range(args.warmup):
             runp()
@@ -339,7 +490,7 @@ def main():
                                           "of dq and dk"}
 
     bwd = None
-    if not args.no_backward:
+    if not args.no_backward and not args.no_extras:
         bwd_setup()
         nb = max(args.steps // 2, 5)
         for _ in range(args.warmup):
@@ -365,19 +516,31 @@ def main():
                "ms_per_step_with_rope_transpose": round(b_step, 4),
                "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                "flop_per_call": f_bwd, "executed_mfma_tflops": round(tf * 7 / 5, 2),
-               "kernels": "bwd_prep + bwd_dkdv_kernel (8 waves in pairs, 64 keys per pair) + bwd_dq_kernel (8 waves), D=96",
+               "kernels": "bwd_prep + bwd_dkdv_kernel + bwd_dq_kernel, D=96",
                "fwd_plus_bwd_ms": round(ms_launch + b_launch, 4)}
+        for name in ("bwd_dkdv", "bwd_dq"):
+            c = counters.get(f"osp480_backward_{name}")
+            if c and "mfma_util" in c:
+                bwd[f"{name}_mfma_util"] = c["mfma_util"]
+                bwd[f"{name}_sclk_mhz"] = c.get("sclk_mhz")
 
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
+        # the oracle on a bounded sample of the headline workload: all query
+        # rows of the first heads; the GPU output of the timed step on the
+        # same heads is compared with it
+        main_w.step("full", 1)
+        torch.cuda.synchronize()
         nh = max(1, min(args.cpu_heads, H))
         hs = slice(0, nh)
         cpu_in = [workloads.to_f64(t[:, :, hs].cpu()) for t in (q, k, v)]
         t_c = time.perf_counter()
-        oracle.attn3d(*cpu_in, grid=grid, n_text=wl.n_text, rope_split=wl.rope_split,
-                      theta=wl.theta)
+        want, _ = oracle.attn3d(*cpu_in, grid=grid, n_text=wl.n_text, rope_split=wl.rope_split,
+                                theta=wl.theta)
         dt = time.perf_counter() - t_c
+        got = main_w.o[:, :, hs].to(torch.float64).cpu().numpy()
+        diff = got - want
         cores = torch.get_num_threads()
         try:
             import threadpoolctl
@@ -388,7 +551,12 @@ def main():
         cpu = {"value": round(4.0 * B * nh * float(n_tok) ** 2 * D / dt / 1e12, 5),
                "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
                "sample": f"fp64 numpy oracle, full attention with 3D RoPE over all {n_tok} query "
-                         f"rows of {nh} of {H} heads ({dt:.1f} s)"}
+                         f"rows of {nh} of {H} heads ({dt:.1f} s)",
+               "oracle_s": round(dt, 2),
+               "gpu_vs_oracle_on_sample": {
+                   "max_abs": float(np.abs(diff).max()),
+                   "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(want)),
+                   "bar": {"max_abs": 2e-2, "rel_l2": 5e-3}}}
 
     line = {
         "metric": "attention TFLOP/s and % of bf16 MFMA peak at 28,800 tokens, full vs Skiparse k=4",
@@ -414,7 +582,8 @@ def main():
                      "kernel": "attn3d_fwd_kernel<D=96, QB=1, BN=64, NW=8, OCC=2, rope_q, fixed_rows>",
                      "flop_per_launch": f_full, "ms_per_launch": round(ms_launch, 4),
                      "ms_median": round(ms_med, 4), "ms_min": round(ms_min, 4)},
-        "skiparse": extra,
+        "kernel_source_hash": kernel_source_hash(),
+        "configs": configs,
         "separated_2d1d": sep,
         "suv_schedule": suv,
         "backward": bwd,
