@@ -43,7 +43,9 @@
 // exceed it by more than kTau (= 8, a factor 256), so the O rescale is
 // skipped for most tiles; probabilities stay <= 2^8 and O / l is unchanged
 // in exact arithmetic.  Row sums add the fp32 probabilities.
+#include <atomic>
 #include <type_traits>
+#include <utility>
 
 #include "osp_internal.hpp"
 #include "osp_mfma.hpp"
@@ -117,30 +119,65 @@ __device__ __forceinline__ void m_phase_order() {
 #define OSP_LEAD_RANK (wave % (NW / 2))
 #endif
 
-template <int D, int QB, int BN, int NW, int OCC, bool ROPE_Q, bool ROPE_K, bool FIXED_ROWS,
-          bool PACKED>
+// Calls f(int_c<0>), ..., f(int_c<N-1>) in order.
+template <typename F, int... I>
+__device__ __forceinline__ void for_slots(F&& f, std::integer_sequence<int, I...>) {
+  (f(int_c<I>{}), ...);
+}
+
+// NS: LDS slots per K and V tile (3 to 6): tile x lives in slot x % NS and
+// is requested NS - 1 tiles ahead of its use.
+// TAB (per-row remap only): the remap of a subsequence differs from that of
+// subsequence 0 by a constant, token(r, j) = token(r, 0) + token(0, j)
+// (Group Skip: j*k; Skiparse-2D: jh*W + jw, times s for group), so the
+// workgroup tabulates token(r, 0) for its L rows once, in dynamic LDS, and
+// the loader looks rows up instead of dividing.
+template <int D, int QB, int BN, int NW, int OCC, int NS, bool ROPE_Q, bool ROPE_K,
+          bool FIXED_ROWS, bool PACKED, bool TAB>
 __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs a) {
+  static_assert(!TAB || !FIXED_ROWS, "the row table serves the per-row remap");
+  extern __shared__ __attribute__((aligned(16))) uint32_t row_tab[];   // TAB: L entries
   using C = AttnCfg<D, QB, BN, NW>;
   constexpr int NKB = BN / 32;        // 32-key blocks per tile
-  // K and V tiles, three slots each (tile x in slot x % 3); separate arrays
-  // so that the compiler can see that an LDS DMA into one slot does not
-  // touch the slot being read
+  static_assert(NS >= 3 && NS <= 6, "three to six tile slots");
+  // K and V tiles, NS slots each; separate arrays so that the compiler can
+  // see that an LDS DMA into one slot does not touch the slot being read.
+  // The last slot of K and of V share one array, which also holds the RoPE
+  // cos/sin table while Q is rotated in the prologue (when K is not
+  // rotated in the loader, the table is used nowhere else); it is at least
+  // a RopeLds long.
+  constexpr int kSL = (ROPE_Q && !ROPE_K && 2 * C::TILE * 2 < int(sizeof(RopeLds)))
+                          ? int((sizeof(RopeLds) + 1) / 2) : 2 * C::TILE;
+  // (slots 2 .. 4 that are not used, or are the last, take 8 elements)
+  constexpr int kT2 = NS > 3 ? C::TILE : 8, kT3 = NS > 4 ? C::TILE : 8, kT4 = NS > 5 ? C::TILE : 8;
   __shared__ __attribute__((aligned(1024))) uint16_t k_s0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t k_s1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t k_s2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_s2[kT2];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_s3[kT3];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_s4[kT4];
   __shared__ __attribute__((aligned(1024))) uint16_t v_s0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_s1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_s2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_s2[kT2];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_s3[kT3];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_s4[kT4];
+  __shared__ __attribute__((aligned(1024))) uint16_t kv_sl[kSL];
   auto kslot = [&](auto sl) __attribute__((always_inline)) -> uint16_t* {
     constexpr int S = decltype(sl)::value;
-    if constexpr (S == 0) return k_s0; else if constexpr (S == 1) return k_s1; else return k_s2;
+    if constexpr (S == NS - 1) return kv_sl;
+    else if constexpr (S == 0) return k_s0; else if constexpr (S == 1) return k_s1;
+    else if constexpr (S == 2) return k_s2; else if constexpr (S == 3) return k_s3;
+    else return k_s4;
   };
   auto vslot = [&](auto sl) __attribute__((always_inline)) -> uint16_t* {
     constexpr int S = decltype(sl)::value;
-    if constexpr (S == 0) return v_s0; else if constexpr (S == 1) return v_s1; else return v_s2;
+    if constexpr (S == NS - 1) return kv_sl + C::TILE;
+    else if constexpr (S == 0) return v_s0; else if constexpr (S == 1) return v_s1;
+    else if constexpr (S == 2) return v_s2; else if constexpr (S == 3) return v_s3;
+    else return v_s4;
   };
-  __shared__ __attribute__((aligned(16))) RopeSmem<ROPE_Q || ROPE_K> rsm;
-  RopeLds* const rl = rsm.get();
+  // K rotated in the loader reads the table in every tile: its own array
+  __shared__ __attribute__((aligned(16))) RopeSmem<ROPE_K> rsm;
+  RopeLds* const rl = ROPE_K ? rsm.get() : ROPE_Q ? reinterpret_cast<RopeLds*>(kv_sl) : nullptr;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -247,7 +284,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   // lattice rows, columns) of the (H/s) x (W/s) lattice, packed 10 bits
   // each (rows < 64), so that each tile's rows follow from its first row
   // by two carries instead of three divisions.
-  const bool s2d = !FIXED_ROWS && mode >= MODE_SINGLE2D;
+  const bool s2d = !FIXED_ROWS && !TAB && mode >= MODE_SINGLE2D;
   const uint32_t lat_h = divk.gh / divk.axis.d;
   const uint32_t sn2 = uint32_t(a_sn) * 2u;
   uint32_t dm_lat[C::DPW];
@@ -259,8 +296,37 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     const uint32_t dh = fdiv(rem, divk.row);
     dm_lat[t] = dt | (dh << 10) | ((rem - dh * divk.row.d) << 20);
   }
+  // TAB: token(0, j), the subsequence's offset from the table's tokens
+  const uint32_t tab_cj = TAB ? skiparse_token(mode, 0u, j, divk, uint32_t(L)) : 0u;
   // tile kt of the tensor at src into LDS tile dst (rows past the end read
-  // as zeros: their offsets are out of the buffer's range)
+  // as zeros: their offsets are out of the buffer's range).  USE_TAB: rows
+  // from the row table (built in the prologue, after the first tiles are
+  // requested)
+  // The table entries of a tile (its first row, then this lane's rows) are
+  // read one tile ahead: each half requests consecutive tiles, one per
+  // iteration, so the entries of the next are read right after a tile is
+  // requested and have arrived when it is its turn.
+  uint32_t tab_nx[C::DPW + 1];
+  auto tab_fetch = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t r0 = uint32_t(kt * BN);
+    tab_nx[0] = row_tab[min(r0, uint32_t(L - 1))];
+#pragma unroll
+    for (int t = 0; t < C::DPW; ++t)
+      tab_nx[t + 1] = row_tab[min(r0 + uint32_t(dm_row[t]), uint32_t(L - 1))];
+  };
+  auto dma_tile_tab = [&](const uint16_t* src, int kt, uint16_t* dst) __attribute__((always_inline)) {
+    const uint32_t base = tab_nx[0];
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(src + int64_t(base + tab_cj) * a_sn), (short)0, kRecords, 0x00020000);
+#pragma unroll
+    for (int t = 0; t < C::DPW; ++t) {
+      int32_t off = int32_t((tab_nx[t + 1] - base) * sn2 + 16u * uint32_t(dm_col[t]));
+      off = (dm_row[t] < L - kt * BN) ? off : kRecords;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(dst + 512 * (lw + C::LW * t)), 16,
+                                               off, 0, 0, 0);
+    }
+    tab_fetch(kt + 1);
+  };
   auto dma_tile = [&](const uint16_t* src, int kt, uint16_t* dst) __attribute__((always_inline)) {
     const uint32_t i0 = tile_first(kt);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -512,6 +578,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   auto issue_tile = [&](int kt, auto slot) __attribute__((always_inline)) {
     if (lead) {
       if constexpr (ROPE_K) staged_issue(kt);
+      else if constexpr (TAB) dma_tile_tab(kg, kt, kslot(slot));
+      else dma_tile(kg, kt, kslot(slot));
+    } else {
+      if constexpr (TAB) dma_tile_tab(vg, kt, vslot(slot));
+      else dma_tile(vg, kt, vslot(slot));
+    }
+  };
+  // the prologue's tiles, requested before the row table exists
+  auto issue_tile_first = [&](int kt, auto slot) __attribute__((always_inline)) {
+    if (lead) {
+      if constexpr (ROPE_K) staged_issue(kt);
       else dma_tile(kg, kt, kslot(slot));
     } else {
       dma_tile(vg, kt, vslot(slot));
@@ -542,8 +619,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (!ROPE_K) {
-    issue_tile(0, int_c<0>{});
-    issue_tile(1, int_c<1>{});
+    for_slots([&](auto sl) __attribute__((always_inline)) {
+      if constexpr (decltype(sl)::value < NS - 1) issue_tile_first(decltype(sl)::value, sl);
+    }, std::make_integer_sequence<int, NS>{});
   }
   // Q rows: every chunk is requested before any is used (a row past the end
   // reads the last row and is zeroed afterwards, so the loads need no
@@ -556,6 +634,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     const uint16_t* p = qg + int64_t(i) * a_sn;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) qraw[qb][c] = ld16(p + 16 * c + 8 * g);
+  }
+  // the row table, while the loads above are in flight (the barriers below
+  // or the prologue's last one publish it)
+  if constexpr (TAB) {
+    for (int r = tid; r < L; r += C::NT)
+      row_tab[r] = skiparse_token(mode, uint32_t(r), 0u, divk, uint32_t(L));
   }
   if constexpr (ROPE_Q || ROPE_K) {
     if (tid < kMaxPairs) rl->omega[tid] = omega;
@@ -596,19 +680,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   // phase behind: on each SIMD one wave's MFMAs overlap the other wave's
   // softmax.
   //
-  // Loads: tile x of K and V lives in slot x % 3.  In its softmax phase
-  // for tile t each wave of the leading half issues its share of K(t+2),
-  // each wave of the trailing half its share of V(t+2); the tiles they
-  // replace, K(t-1) and V(t-1), were last read in earlier phases.  At the
-  // end of that phase a wave waits for its loads of the previous iteration
-  // only (K(t+1) or V(t+1)), at least one phase before their first
-  // reader, so each load has two phases or more to arrive.  The tile count
-  // is padded to a multiple of 3 with tiles past the end of the
-  // subsequence (keys masked to -inf, loads out of range of the buffer,
-  // which read as zeros), so that every slot index is a compile-time
-  // constant.
+  // Loads: tile x of K and V lives in slot x % NS.  In its softmax phase
+  // for tile t each wave of the leading half issues its share of
+  // K(t+NS-1), each wave of the trailing half its share of V(t+NS-1); the
+  // tiles they replace, K(t-1) and V(t-1), were last read in earlier
+  // phases.  At the end of that phase a wave waits for its loads of
+  // K(t+1) or V(t+1) only (issued NS-2 iterations before), at least one
+  // phase before their first reader, so each load has 2(NS-2) phases or
+  // more to arrive.  The tile count is padded to a multiple of NS with
+  // tiles past the end of the subsequence (keys masked to -inf, loads out
+  // of range of the buffer, which read as zeros), so that every slot index
+  // is a compile-time constant.
   const bool ragged = (L % BN) != 0;
-  const int nkt3 = (nkt + 2) / 3 * 3;
+  const int nkt3 = (nkt + NS - 1) / NS * NS;
   f32x16_t s[NKB][QB];
   bf16x8_t pb[QB][NKB][2];
 
@@ -617,17 +701,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Wait for all but this iteration's DPW loads (vmcnt(DPW)); the leading
-  // half on the staged path has just stored its tile and waits for all
-  // (vmcnt(0) lgkmcnt(0)).  The compiler tracks these waits, so it knows
-  // which slots are complete.
+  // Wait for all but the last NS-2 iterations' loads (vmcnt((NS-2)*DPW));
+  // the leading half on the staged path has just stored its tile and waits
+  // for all (vmcnt(0) lgkmcnt(0)).  The compiler tracks these waits, so it
+  // knows which slots are complete.
+  constexpr int kInFlight = (NS - 2) * C::DPW;
+  static_assert(kInFlight < 64, "vmcnt field");
   auto loads_done = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     if (ROPE_K && lead) __builtin_amdgcn_s_waitcnt(0x0070);
-    else __builtin_amdgcn_s_waitcnt((C::DPW & 15) | ((C::DPW >> 4) << 14) | 0x0F70);
+    else __builtin_amdgcn_s_waitcnt((kInFlight & 15) | ((kInFlight >> 4) << 14) | 0x0F70);
   };
   // matrix phase of tile t: QK(t) from K slot P (QK) and PV(t-1) from V
-  // slot (P + 2) % 3 (PV).  Instruction order inside it (one query block
+  // slot (P + NS - 1) % NS (PV).  Instruction order inside it (one query block
   // per wave): the LDS reads run OSP_M_LEAD MFMAs ahead of the MFMAs that
   // use them.  With two blocks the compiler's own order was as fast.
   auto m_phase = [&](int t, auto slot, auto do_qk, auto do_pv, auto masked) __attribute__((always_inline)) {
@@ -635,7 +721,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
     __builtin_amdgcn_s_setprio(1);
     if constexpr (QK) qk(int_c<P>{}, s, t, masked);
-    if constexpr (PV) pv(int_c<(P + 2) % 3>{}, pb);
+    if constexpr (PV) pv(int_c<(P + NS - 1) % NS>{}, pb);
     if constexpr (QB == 1) {
       constexpr int NMV = PV ? NKB * 2 * (D / 32) : 0, NMK = QK ? NKB * (D / 16) : 0;
       __builtin_amdgcn_sched_group_barrier(0x100, m_first_reads<NMK, NMV, OSP_M_LEAD>(), 0);
@@ -646,24 +732,47 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   // tiles from tu on hold keys past the end (the last real tile when
   // ragged, and the padding); whole groups before tu run unmasked
   const int tu = nkt - (ragged ? 1 : 0);
-  // one iteration (two phases) for tile t in slot P = t % 3; MASKED: mask
+  // one iteration (two phases) for tile t in slot P = t % NS; MASKED: mask
   // keys past the end (correct for any tile; used for the last groups)
   auto iter = [&](int t, auto slot, auto masked) __attribute__((always_inline)) {
     constexpr int P = decltype(slot)::value;
     m_phase(t, slot, bool_c<true>{}, bool_c<true>{}, masked);
     barrier();
-    issue_tile(t + 2, int_c<(P + 2) % 3>{});
+    issue_tile(t + NS - 1, int_c<(P + NS - 1) % NS>{});
     softmax_phase(s, pb, t == 0);
-    finish_tile(t + 2, int_c<(P + 2) % 3>{});
+    finish_tile(t + NS - 1, int_c<(P + NS - 1) % NS>{});
     loads_done();
     barrier();
   };
 
-  // prologue, part 2: K(0), K(1), V(0), V(1) into slots 0 and 1 (with K
-  // rotation in the loader: here); V slot 2 (read as "V(-1)" by the first
-  // matrix phase, with P = 0) cleared
+  // an iteration of the last group for a tile t that may lie past the end:
+  // as iter when t < nkt; for t == nkt only the PV product of tile t - 1;
+  // beyond, no work.  The loads and barriers are those of iter.
+  // (with K rotated in the loader, or two query blocks per wave and a
+  // per-row remap, the padding runs as masked tiles: the branches would
+  // push those variants' registers past the budget)
+  constexpr bool kSkipPad = !ROPE_K && (FIXED_ROWS || QB == 1);
+  auto iter_pad = [&](int t, auto slot) __attribute__((always_inline)) {
+    constexpr int P = decltype(slot)::value;
+    if (!kSkipPad || t < nkt) {
+      iter(t, slot, bool_c<true>{});
+    } else {
+      if (t == nkt) m_phase(t, slot, bool_c<false>{}, bool_c<true>{}, bool_c<false>{});
+      barrier();
+      issue_tile(t + NS - 1, int_c<(P + NS - 1) % NS>{});
+      finish_tile(t + NS - 1, int_c<(P + NS - 1) % NS>{});
+      loads_done();
+      barrier();
+    }
+  };
+
+  // prologue, part 2: K and V of tiles 0 .. NS-2 into their slots (with K
+  // rotation in the loader: here); V slot NS-1 (read as "V(-1)" by the
+  // first matrix phase, with P = 0) cleared, once every wave has finished
+  // reading the table it shares with that slot
+  if constexpr (ROPE_Q && !ROPE_K) lds_barrier();
   for (int e = tid; e < C::TILE / 8; e += C::NT)
-    reinterpret_cast<uint4*>(v_s2)[e] = make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4*>(vslot(int_c<NS - 1>{}))[e] = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -672,26 +781,34 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       pb[qb][kb][1] = bf16x8_t{};
     }
   if constexpr (ROPE_K) {
-    issue_tile(0, int_c<0>{});
-    finish_tile(0, int_c<0>{});
-    issue_tile(1, int_c<1>{});
-    finish_tile(1, int_c<1>{});
+    for_slots([&](auto sl) __attribute__((always_inline)) {
+      if constexpr (decltype(sl)::value < NS - 1) {
+        issue_tile_first(decltype(sl)::value, sl);
+        finish_tile(decltype(sl)::value, sl);
+      }
+    }, std::make_integer_sequence<int, NS>{});
   }
   __syncthreads();
+  if constexpr (TAB) tab_fetch(NS - 1);    // the first tile the loop requests
   if (!lead) barrier();
   int t = 0;
-  for (; t + 3 <= tu; t += 3) {
-    iter(t, int_c<0>{}, bool_c<false>{});
-    iter(t + 1, int_c<1>{}, bool_c<false>{});
-    iter(t + 2, int_c<2>{}, bool_c<false>{});
+  for (; t + NS <= tu; t += NS) {
+    for_slots([&](auto sl) __attribute__((always_inline)) {
+      iter(t + decltype(sl)::value, sl, bool_c<false>{});
+    }, std::make_integer_sequence<int, NS>{});
   }
-  for (; t < nkt3; t += 3) {
-    iter(t, int_c<0>{}, bool_c<true>{});
-    iter(t + 1, int_c<1>{}, bool_c<true>{});
-    iter(t + 2, int_c<2>{}, bool_c<true>{});
+  // the last group: tiles past nkt - 1 only pad the group to NS slots;
+  // their matrix and softmax work is skipped (uniform branches), except the
+  // PV product of the last real tile
+  for (; t < nkt3; t += NS) {
+    for_slots([&](auto sl) __attribute__((always_inline)) {
+      if constexpr (decltype(sl)::value == 0) iter(t, sl, bool_c<true>{});
+      else iter_pad(t + decltype(sl)::value, sl);
+    }, std::make_integer_sequence<int, NS>{});
   }
-  // the last matrix phase: PV of tile nkt3 - 1 (V slot 2)
-  m_phase(nkt3, int_c<0>{}, bool_c<false>{}, bool_c<true>{}, bool_c<false>{});
+  // the last matrix phase: PV of tile nkt3 - 1 (V slot NS-1), when it is real
+  if (!kSkipPad || nkt3 == nkt)
+    m_phase(nkt3, int_c<0>{}, bool_c<false>{}, bool_c<true>{}, bool_c<false>{});
   if (lead) barrier();   // the trailing half's last barrier
   // loads of the padding tiles past nkt3 may still be writing LDS: finish
   // them before the workgroup's LDS is released
@@ -729,27 +846,39 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
 // fragment read from LDS then feeds two MFMAs, and the matrix phase is as
 // long as at D=128 with half the registers per block (7% faster on
 // CogVideoX's 17,776 tokens than one block over 64-key tiles)
+// NS: tile slots of the fixed-row instances (see the kernel).  D=96 takes
+// four (loads issued three tiles ahead): 0.5-1.5% faster than three on the
+// 28,800-token workload, full and Skiparse k=4; five or six gain nothing
+// more.  At D=64 and D=128 a fourth slot spills.  The per-row-remap
+// instances keep three (a fourth spills at D=96 and ran 2.5% slower on
+// Skiparse-2D), and so does K rotated in the loader, whose K tile goes
+// through registers and is waited for at once.
 #ifndef OSP_D64_TILE
-#define OSP_D64_TILE 2, 32, 8, 2
+#define OSP_D64_TILE 2, 32, 8, 2, 3
 #endif
 #ifndef OSP_D96_TILE
-#define OSP_D96_TILE 1, 64, 8, 2
+#define OSP_D96_TILE 1, 64, 8, 2, 4
 #endif
 #ifndef OSP_D128_TILE
-#define OSP_D128_TILE 1, 64, 8, 2
+#define OSP_D128_TILE 1, 64, 8, 2, 3
 #endif
 // D=128 with K rotated in the loader: 64-key tiles spill, 32 do not
 #ifndef OSP_D128_ROPE_K_TILE
-#define OSP_D128_ROPE_K_TILE 1, 32, 8, 2
+#define OSP_D128_ROPE_K_TILE 1, 32, 8, 2, 3
 #endif
-template <int QB_, int BN_, int NW_, int OCC_> struct TileShape {
-  static constexpr int QB = QB_, BN = BN_, NW = NW_, OCC = OCC_;
+template <int QB_, int BN_, int NW_, int OCC_, int NS_> struct TileShape {
+  static constexpr int QB = QB_, BN = BN_, NW = NW_, OCC = OCC_, NS = NS_;
+};
+template <typename T> struct RopeKShape : T {
+  static constexpr int NS = 3;
 };
 template <int D, bool RK> struct TileCfg;
-template <bool RK> struct TileCfg<64, RK> : TileShape<OSP_D64_TILE> {};
-template <bool RK> struct TileCfg<96, RK> : TileShape<OSP_D96_TILE> {};
+template <> struct TileCfg<64, false> : TileShape<OSP_D64_TILE> {};
+template <> struct TileCfg<64, true> : RopeKShape<TileShape<OSP_D64_TILE>> {};
+template <> struct TileCfg<96, false> : TileShape<OSP_D96_TILE> {};
+template <> struct TileCfg<96, true> : RopeKShape<TileShape<OSP_D96_TILE>> {};
 template <> struct TileCfg<128, false> : TileShape<OSP_D128_TILE> {};
-template <> struct TileCfg<128, true> : TileShape<OSP_D128_ROPE_K_TILE> {};
+template <> struct TileCfg<128, true> : RopeKShape<TileShape<OSP_D128_ROPE_K_TILE>> {};
 
 template <int D> constexpr int max_keys_per_tile() {
   return TileCfg<D, false>::BN > TileCfg<D, true>::BN ? TileCfg<D, false>::BN : TileCfg<D, true>::BN;
@@ -775,17 +904,43 @@ int attn_rows_per_block(int head_dim) {
 static_assert(TileCfg<128, false>::NW * TileCfg<128, false>::QB ==
               TileCfg<128, true>::NW * TileCfg<128, true>::QB, "rows per workgroup");
 
+#ifndef OSP_TAB_NS
+#define OSP_TAB_NS 3
+#endif
+// LDS of a workgroup, static plus dynamic, in bytes
+constexpr int kLdsBytes = 160 * 1024;
+
 template <int D, bool RQ, bool RK, bool PK>
 static hipError_t launch_drk(const AttnArgs& a, hipStream_t s) {
   using T = TileCfg<D, RK>;
   dim3 grid(a.total_tiles), block(T::NW * 64);
   const bool fixed = a.mode <= MODE_BLOCK && (a.mode != MODE_GROUP || T::BN % int(a.divk.d) == 0);
-  if (fixed)
-    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, RQ, RK, true, PK>),
-                       grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, RQ, RK, false, PK>),
-                       grid, block, 0, s, a);
+  if (fixed) {
+    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, T::NS, RQ, RK, true, PK,
+                                          false>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
+  // per-row remap: with Q rotated in the loader and K already rotated (the
+  // fast path), rows come from an LDS row table when it fits beside the
+  // kernel's static LDS
+  if constexpr (RQ && !RK && !PK) {
+    auto kern = attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, (D == 96 ? OSP_TAB_NS : 3), RQ, RK,
+                                  false, PK, true>;
+    static std::atomic<int> static_lds{-1};
+    if (static_lds.load() < 0) {
+      hipFuncAttributes attr;
+      if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kern)) != hipSuccess)
+        return hipErrorInvalidDeviceFunction;
+      static_lds.store(int(attr.sharedSizeBytes));
+    }
+    const int64_t tab = int64_t(a.seq_len) * 4;
+    if (static_lds.load() + tab <= kLdsBytes) {
+      hipLaunchKernelGGL(kern, grid, block, size_t(tab), s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, 3, RQ, RK, false, PK, false>),
+                     grid, block, 0, s, a);
   return hipGetLastError();
 }
 
