@@ -26,11 +26,12 @@
 //     row order, and dV^T += dO^T P (P wave), dK^T += Q^T dS (dS wave)
 //     take their A operands transposed from the same LDS tiles
 //     (ds_read_b64_tr_b16) in that row order.
-//  3. bwd_dq: a workgroup owns NW*32 queries, 32 per wave, Q and dO in
-//     registers, and streams the keys (K and V tiles): S^T - lse/scale =
-//     K Q^T - lse/scale, dP^T - delta = V dO^T - delta (a lane holds ONE
-//     query, so both row terms are one value per lane), P^T and dS^T
-//     as above, dQ^T += K^T dS^T with K^T read transposed.
+//  3. bwd_dq: a workgroup owns NW*32 queries, 32 per wave, Q (times scale
+//     log2(e), rounded to bf16 once, as the forward rounds its scaled Q)
+//     and dO in registers, and streams the keys (K and V tiles): X^T =
+//     K Q'^T - lse log2(e), dP^T - delta = V dO^T - delta (a lane holds ONE
+//     query, so both row terms are one value per lane), P^T = exp2(X^T),
+//     dS^T as above, dQ^T += K^T dS^T with K^T read transposed.
 // dQ gets a pass of its own instead of atomic fp32 adds from the dK/dV
 // pass: the score products are formed twice (7 MFMA products per 32x32
 // block instead of 5), but no workspace for dQ and no atomics are needed.
@@ -217,6 +218,20 @@ __device__ __forceinline__ void store_rows_t(uint16_t* p, const f32x16_t (&acc)[
       const uint32_t w1 = pack_bf16(acc[db][4 * r4 + 2] * mul, acc[db][4 * r4 + 3] * mul);
       *reinterpret_cast<uint2*>(p + 32 * db + 8 * r4 + 4 * g) = make_uint2(w0, w1);
     }
+}
+
+// Multiply an operand row by m in fp32 and round it to bf16 again (RNE).
+template <int D>
+__device__ __forceinline__ void scale_operand(bf16x8_t (&x)[D / 16], float m) {
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    uint4 u = __builtin_bit_cast(uint4, x[c]);
+    u.x = pack_bf16(bf16lo(u.x) * m, bf16hi(u.x) * m);
+    u.y = pack_bf16(bf16lo(u.y) * m, bf16hi(u.y) * m);
+    u.z = pack_bf16(bf16lo(u.z) * m, bf16hi(u.z) * m);
+    u.w = pack_bf16(bf16lo(u.w) * m, bf16hi(u.w) * m);
+    x[c] = __builtin_bit_cast(bf16x8_t, u);
+  }
 }
 
 // Rows 16c + 8g .. +7 (channels) of this lane's token row, as B operands.
@@ -524,8 +539,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ.  Each wave owns 32 queries: Q and dO rows in registers, the
-// row's -lse/scale and -delta from the workspace.  Per streamed tile of 64
+// 3. dQ.  Each wave owns 32 queries: Q (times scale log2(e)) and dO rows in
+// registers, the row's -lse log2(e) and -delta from the workspace.  Per streamed tile of 64
 // keys (K and V through LDS, double-buffered): S^T and dP^T - delta per
 // 32-key block (C operand layout: keys are rows, the lane's query the
 // column), P = exp2 of one fma, dS^T = P o (dP^T - delta) packed to bf16,
@@ -562,14 +577,18 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
   const int64_t bhn = (int64_t(wb.b) * a.heads + wb.h) * a.ws_ld + wb.tok0;
   const float c2 = a.scale_log2;
 
-  // ---- this lane's query: Q and dO rows as B operands, its two workspace values
+  // ---- this lane's query: Q and dO rows as B operands, its two workspace
+  // values.  Q is multiplied by scale * log2(e) and rounded to bf16 once,
+  // so that the score product started from -lse log2(e) is the exponent of
+  // P in base 2 (Q enters no other product of this kernel).
   const int qr = int(wb.blk) * NW * 32 + wave * 32 + l32;
   const bool qvalid = qr < L;
   const uint32_t qi = skiparse_token(mode, uint32_t(qvalid ? qr : 0), wb.j, divk, uint32_t(L));
   bf16x8_t qreg[D / 16], oreg[D / 16];
   load_row_operand<D>(a.q + in_off + int64_t(qi) * sn, qvalid, g, qreg);
+  scale_operand<D>(qreg, c2);
   load_row_operand<D>(a.dout + in_off + int64_t(qi) * sn, qvalid, g, oreg);
-  const float nlc2 = (qvalid ? a.neg_lse_s[bhn + qi] : 0.f) * c2;
+  const float nl2 = (qvalid ? a.neg_lse_s[bhn + qi] : 0.f) * c2;     // -lse log2(e)
   const float ne = qvalid ? a.neg_delta[bhn + qi] : 0.f;
 
   f32x16_t dq[D / 32];
@@ -610,12 +629,14 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
     }
   };
 
-  auto compute = [&](int t, auto sl) __attribute__((always_inline)) {
+  // CLAMP (the last tile, when it holds keys past the end of the
+  // subsequence): those keys have zero K and V rows, so they add dS * 0 to
+  // dQ; P is clamped to [0, 1] (its true range), which keeps their
+  // exp2(-lse log2(e)) finite without a branch per element.
+  auto compute = [&](int t, auto sl, auto clamp) __attribute__((always_inline)) {
+    constexpr bool CLAMP = decltype(clamp)::value;
     const char* ks = reinterpret_cast<const char*>(kslot(sl));
     const char* vs = reinterpret_cast<const char*>(vslot(sl));
-    // Keys past the end of the subsequence have zero K and V rows, so they
-    // add dS * 0 to dQ; P is clamped to [0, 1] (its true range), which
-    // keeps their exp2(-lse) finite without a branch per element.
 #pragma unroll
     for (int kb = 0; kb < kBwdRows / 32; ++kb) {
       const char* kblk = ks + 32 * kb * KCH * 16;
@@ -623,7 +644,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
       f32x16_t s, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        s[e] = 0.f;
+        s[e] = nl2;
         dp[e] = ne;
       }
       // At head_dim 128 (one wave per SIMD) nothing else hides the LDS
@@ -654,10 +675,12 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const int e0 = 8 * hh + 2 * tt, e1 = e0 + 1;
-          const float p0 = __builtin_amdgcn_fmed3f(
-              __builtin_amdgcn_exp2f(__builtin_fmaf(s[e0], c2, nlc2)), 0.f, 1.f);
-          const float p1 = __builtin_amdgcn_fmed3f(
-              __builtin_amdgcn_exp2f(__builtin_fmaf(s[e1], c2, nlc2)), 0.f, 1.f);
+          float p0 = __builtin_amdgcn_exp2f(s[e0]);
+          float p1 = __builtin_amdgcn_exp2f(s[e1]);
+          if constexpr (CLAMP) {
+            p0 = __builtin_amdgcn_fmed3f(p0, 0.f, 1.f);
+            p1 = __builtin_amdgcn_fmed3f(p1, 0.f, 1.f);
+          }
           sw[tt] = pack_bf16(p0 * dp[e0], p1 * dp[e1]);
         }
         sb[hh] = __builtin_bit_cast(bf16x8_t, make_uint4(sw[0], sw[1], sw[2], sw[3]));
@@ -672,20 +695,36 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
     }
   };
 
+  // Tiles alternate between the two slots; the loop runs the tiles that
+  // hold no key past the end (tc of them), then the ragged last tile, if
+  // any, runs once with the clamp.
   const int nkt = (L + kBwdRows - 1) / kBwdRows;
+  const int tc = (L % kBwdRows) ? nkt - 1 : nkt;
   issue(0, int_c<0>{});
   __builtin_amdgcn_s_waitcnt(0x0070);
   __syncthreads();
-  for (int t = 0; t < nkt; t += 2) {
+  int t = 0;
+  for (; t + 2 <= tc; t += 2) {
     if (t + 1 < nkt) issue(t + 1, int_c<1>{});
-    compute(t, int_c<0>{});
+    compute(t, int_c<0>{}, bool_c<false>{});
     __builtin_amdgcn_s_waitcnt(0x0070);
     __syncthreads();
-    if (t + 1 >= nkt) break;
     if (t + 2 < nkt) issue(t + 2, int_c<0>{});
-    compute(t + 1, int_c<1>{});
+    compute(t + 1, int_c<1>{}, bool_c<false>{});
     __builtin_amdgcn_s_waitcnt(0x0070);
     __syncthreads();
+  }
+  // one or two tiles left: an odd tile count leaves one unclamped tile in
+  // slot 0, and a ragged sequence one clamped tile after it
+  if (t < tc) {
+    if (t + 1 < nkt) issue(t + 1, int_c<1>{});
+    compute(t, int_c<0>{}, bool_c<false>{});
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __syncthreads();
+    ++t;
+    if (t < nkt) compute(t, int_c<1>{}, bool_c<true>{});
+  } else if (t < nkt) {
+    compute(t, int_c<0>{}, bool_c<true>{});
   }
 
   if (qvalid) {

@@ -18,7 +18,9 @@ Forward (the flash kernel and the short-subsequence kernel alike):
   * O = bf16(sum bf16(p) v / l), LSE = (m + log2 l) ln 2 in fp32.
 Backward (q and k the rotated bf16 tensors, o and lse from the forward):
   * -delta = -sum O dO in fp32, -lse / s in fp32;
-  * p = exp2(s log2(e) (q k^T - lse / s)) in fp32, rounded to bf16 for
+  * the dK/dV pass forms p = exp2(s log2(e) (q k^T - lse / s)), the dQ pass
+    p = exp2(bf16(s log2(e) q) k^T - (lse / s) s log2(e)) (Q scaled in
+    registers and rounded to bf16 once), in fp32; p is rounded to bf16 for
     dV = p^T dO;
   * dS = p (dO v^T - delta) in fp32, rounded to bf16 for dQ = s dS k and
     dK = s dS^T q;
@@ -132,14 +134,15 @@ def attn_bwd(q, k, v, do, *, grid, n_text=0, mode="full", sparse_k=1, rope_split
         for b in range(b_sz):
             for h in range(h_sz):
                 qq, kk, vv, dd = q[b, g, h], k[b, g, h], v[b, g, h], do[b, g, h]
-                x = qq @ kk.T + neg_lse_s[b, h, g][:, None]
-                p = np.exp2(c2 * x).astype(pr.dt)
+                nls = neg_lse_s[b, h, g][:, None]
                 dpd = dd @ vv.T + neg_delta[b, g, h][:, None]
-                ds = p * dpd
-                dv[b, g, h] = pr.rnd(pr.rnd(p).T.astype(pr.dt) @ dd)
-                dsr = pr.rnd(ds).astype(pr.dt)
-                dq[b, g, h] = pr.rnd(s * (dsr @ kk))
-                dk[b, g, h] = pr.rnd(s * (dsr.T @ qq))
+                # the dK/dV pass
+                p_kv = np.exp2(c2 * (qq @ kk.T + nls)).astype(pr.dt)
+                dv[b, g, h] = pr.rnd(pr.rnd(p_kv).T.astype(pr.dt) @ dd)
+                dk[b, g, h] = pr.rnd(s * (pr.rnd(p_kv * dpd).astype(pr.dt).T @ qq))
+                # the dQ pass: Q scaled in registers
+                p_q = np.exp2(pr.rnd(c2 * qq).astype(pr.dt) @ kk.T + pr.f(nls * c2)).astype(pr.dt)
+                dq[b, g, h] = pr.rnd(s * (pr.rnd(p_q * dpd).astype(pr.dt) @ kk))
     if rope_chain:
         dq = pr.rnd(_rotate(dq, grid, n_text, rope_split, theta, pos_offset, pr, inverse=True))
         dk = pr.rnd(_rotate(dk, grid, n_text, rope_split, theta, pos_offset, pr, inverse=True))

@@ -181,6 +181,15 @@ def test_packed_bwd_rope_chain_bar(mode, k, segs):
         start = sl.stop
 
 
+def test_bwd_text_tokens_batch_and_scale_bar():
+    """test_bwd_text_tokens_batch_and_scale: seed 2, 37 text tokens and a
+    3x10x12 grid, batch 2, 3 heads of 96, sm_scale 0.2 (about twice the
+    default logit scale) under the unit bar."""
+    errs = bwd_errors(2, (2, 397, 3, 96), rope_chain=False, grid=(3, 10, 12), n_text=37,
+                      sm_scale=0.2)
+    check_bwd(errs, False, "bwd text+batch+scale")
+
+
 @pytest.mark.parametrize("d", [64, 96, 128])
 def test_bwd_unit_bar(d):
     """test_bwd_full_ragged: seed 0, grid 5x7x9, 2 heads; q and k taken as
