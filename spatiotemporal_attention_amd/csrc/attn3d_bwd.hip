@@ -175,16 +175,19 @@ __device__ __forceinline__ BwdBlock bwd_block(const BwdArgs& a) {
 template <int D>
 struct TileDma {
   using C = BwdCfg<D>;
-  int row[C::DPW], col[C::DPW];
+  int w, lane;
   int32_t off[C::DPW];   // byte offsets of the current tile, relative to its first token
 
-  __device__ __forceinline__ void init(int w, int lane) {
-#pragma unroll
-    for (int u = 0; u < C::DPW; ++u) {
-      const int p = 64 * (w + C::LW * u) + lane;
-      row[u] = p / C::KCH;
-      col[u] = (p % C::KCH) ^ chunk_swz<D>(row[u]);
-    }
+  __device__ __forceinline__ void init(int w_, int lane_) {
+    w = w_;
+    lane = lane_;
+  }
+  // row and stored chunk of load u (formed again for each tile rather than
+  // held: the dK/dV kernel is short of registers)
+  __device__ __forceinline__ int row(int u) const { return (64 * (w + C::LW * u) + lane) / C::KCH; }
+  __device__ __forceinline__ int col(int u) const {
+    const int p = 64 * (w + C::LW * u) + lane;
+    return (p % C::KCH) ^ chunk_swz<D>(p / C::KCH);
   }
   // offsets of tile t (rows 64t ..) of subsequence j; returns its first token
   __device__ __forceinline__ uint32_t at(int t, int mode, uint32_t j, const SkipDiv& divk, int L,
@@ -193,9 +196,9 @@ struct TileDma {
     const uint32_t i0 = skiparse_token(mode, uint32_t(r0), j, divk, uint32_t(L));
 #pragma unroll
     for (int u = 0; u < C::DPW; ++u) {
-      const int r = r0 + row[u];
+      const int r = r0 + row(u);
       const uint32_t i = skiparse_token(mode, uint32_t(min(r, L - 1)), j, divk, uint32_t(L));
-      off[u] = (r < L) ? int32_t((int64_t(i - i0) * sn + 8 * col[u]) * 2) : kRecords;
+      off[u] = (r < L) ? int32_t((int64_t(i - i0) * sn + 8 * col(u)) * 2) : kRecords;
     }
     return i0;
   }
@@ -322,17 +325,19 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
 
   // ---- this lane's keys (one per key block): K rows (P wave) or V rows
   // (dS wave) as B operands
+  // (the key rows and tokens are formed again for the store at the end
+  // rather than held through the query loop)
+  auto key_row = [&](int kb) __attribute__((always_inline)) {
+    return int(wb.blk) * C::KV_ROWS + (pr * KB + kb) * 32 + l32;
+  };
   bf16x8_t xreg[KB][D / 16];
-  uint32_t ktok[KB];
-  bool kval[KB];
   {
     const uint16_t* src = (pw ? a.k : a.v) + in_off;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const int r = int(wb.blk) * C::KV_ROWS + (pr * KB + kb) * 32 + l32;
-      kval[kb] = r < L;
-      ktok[kb] = skiparse_token(mode, uint32_t(kval[kb] ? r : 0), wb.j, divk, uint32_t(L));
-      load_row_operand<D>(src + int64_t(ktok[kb]) * sn, kval[kb], g, xreg[kb]);
+      const int r = key_row(kb);
+      const uint32_t tok = skiparse_token(mode, uint32_t(r < L ? r : 0), wb.j, divk, uint32_t(L));
+      load_row_operand<D>(src + int64_t(tok) * sn, r < L, g, xreg[kb]);
     }
   }
 
@@ -343,10 +348,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[kb][db][e] = 0.f;
-  int r_off[D / 16];
-  row_read_offsets<D>(lane, r_off);
-  int t_off[2][D / 32];
-  tr_read_offsets<D>(lane, t_off);
+  const RowOff<D> r_off(lane);
+  const TrOff<D> t_off(lane);
 
   // ---- loads: the P waves load the Q tile and the -lse/scale row, the dS
   // waves the dO tile and the -delta row
@@ -408,7 +411,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      const bf16x8_t ra = *reinterpret_cast<const bf16x8_t*>(rows + r_off[c]);
+      const bf16x8_t ra = *reinterpret_cast<const bf16x8_t*>(rows + r_off(c));
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
         x[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra, xreg[kb][c], x[kb], 0, 0, 0);
@@ -530,9 +533,10 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
 
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
-    if (kval[kb]) {
+    if (key_row(kb) < L) {
+      const uint32_t tok = skiparse_token(mode, uint32_t(key_row(kb)), wb.j, divk, uint32_t(L));
       const int64_t out = int64_t(wb.b) * a.osb + int64_t(wb.h) * a.osh +
-                          (wb.tok0 + int64_t(ktok[kb])) * a.osn;
+                          (wb.tok0 + int64_t(tok)) * a.osn;
       if (pw) store_rows_t<D>(a.dv + out, acc[kb], 1.0f, g);
       else store_rows_t<D>(a.dk + out, acc[kb], a.scale, g);
     }
@@ -596,10 +600,8 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) dq[db][e] = 0.f;
-  int r_off[D / 16];
-  row_read_offsets<D>(lane, r_off);
-  int t_off[2][D / 32];
-  tr_read_offsets<D>(lane, t_off);
+  const RowOff<D> r_off(lane);
+  const TrOff<D> t_off(lane);
 
   static_assert(NW == C::LW || NW == 2 * C::LW, "one or two loading wave groups");
   const int lw = wave % C::LW;       // rank among the waves loading a tensor
@@ -653,9 +655,9 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
       if constexpr (NW == C::LW) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kblk + r_off[c]);
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kblk + r_off(c));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[c], s, 0, 0, 0);
-        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vblk + r_off[c]);
+        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vblk + r_off(c));
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, oreg[c], dp, 0, 0, 0);
       }
       if constexpr (NW == C::LW) {

@@ -415,25 +415,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   }
 
   // per-lane LDS byte offsets of the operand reads (swizzle folded in)
-  int k_off[D / 16];
-  {
-    const int hsw = g ^ chunk_swz<D>(l32);
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) k_off[c] = (l32 * C::KCH + ((2 * c) ^ hsw)) * 16;
-  }
-  int v_off[2][D / 32];
-  {
-    const int G = lane >> 4, s16 = lane & 15;
-    const int ta = s16 & 3, te = s16 >> 2;
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int key = 4 * (G >> 1) + te + 8 * s;
-        const int chunk = 4 * db + 2 * (G & 1) + (ta >> 1);
-        v_off[s][db] = (key * C::KCH + (chunk ^ chunk_swz<D>(key))) * 16 + 8 * (ta & 1);
-      }
-  }
+  const RowOff<D> k_off(lane);
+  const TrOff<D> v_off(lane);
 
   // S^T - m of the K tile in slot SK into s; MASKED: keys of tile kt past
   // the end of the subsequence start from -inf instead
@@ -458,7 +441,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(ks + 32 * kb * C::KCH * 16 + k_off[c]);
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(ks + 32 * kb * C::KCH * 16 + k_off(c));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], s[kb][qb], 0, 0, 0);

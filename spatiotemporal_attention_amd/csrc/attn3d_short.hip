@@ -196,8 +196,7 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
         qc[e] = raw;
       }
     }
-    int r_off[D / 16];
-    row_read_offsets<D>(lane, r_off);
+    const RowOff<D> r_off(lane);
     const char* vsb = reinterpret_cast<const char*>(vs);
     auto get_rows = [&](bf16x8_t (&y)[NB][D / 16]) __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's stores landed
@@ -206,7 +205,7 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
       for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
         for (int c = 0; c < D / 16; ++c)
-          y[rb][c] = *reinterpret_cast<const bf16x8_t*>(vsb + 32 * rb * KCH * 16 + r_off[c]);
+          y[rb][c] = *reinterpret_cast<const bf16x8_t*>(vsb + 32 * rb * KCH * 16 + r_off(c));
     };
     put_rows(kc);
     get_rows(kreg);
@@ -247,8 +246,7 @@ __global__ __launch_bounds__(ShortCfg<NB>::W * 64) void attn3d_short_kernel(cons
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
   __builtin_amdgcn_wave_barrier();
 
-  int v_off[2][D / 32];
-  tr_read_offsets<D>(lane, v_off);
+  const TrOff<D> v_off(lane);
   const char* vb_ = reinterpret_cast<const char*>(vs);
 
   uint16_t* og = a.o + int64_t(b) * a.osb + int64_t(h) * a.osh;

@@ -84,11 +84,49 @@ __device__ __forceinline__ void tr_read_offsets(int lane, int (&off)[2][D / 32])
     }
 }
 
-// The transposed A operand at byte offsets off[.][db] from blk.
+// The offsets above, held per lane.  At head_dim 96 the swizzle flips only
+// the two low bits of a chunk index ((r >> 2) & 3), so the offsets of the
+// 16-channel blocks c (rows) or 32-channel blocks db (transposed) differ by
+// constants: row block c sits at one of two bases (c even or odd) plus
+// 64 (c / 2) bytes, transposed block db at its base for s plus 64 db bytes.
+// Two registers then hold what takes six, and the constants become the LDS
+// reads' immediate offsets.
+template <int D> struct RowOff {
+  int v[D / 16];
+  __device__ __forceinline__ explicit RowOff(int lane) { row_read_offsets<D>(lane, v); }
+  __device__ __forceinline__ int operator()(int c) const { return v[c]; }
+};
+template <> struct RowOff<96> {
+  int e[2];
+  __device__ __forceinline__ explicit RowOff(int lane) {
+    int v[6];
+    row_read_offsets<96>(lane, v);
+    e[0] = v[0];
+    e[1] = v[1];
+  }
+  __device__ __forceinline__ int operator()(int c) const { return e[c & 1] + 64 * (c >> 1); }
+};
+template <int D> struct TrOff {
+  int v[2][D / 32];
+  __device__ __forceinline__ explicit TrOff(int lane) { tr_read_offsets<D>(lane, v); }
+  __device__ __forceinline__ int operator()(int s, int db) const { return v[s][db]; }
+};
+template <> struct TrOff<96> {
+  int e[2];
+  __device__ __forceinline__ explicit TrOff(int lane) {
+    int v[2][3];
+    tr_read_offsets<96>(lane, v);
+    e[0] = v[0][0];
+    e[1] = v[1][0];
+  }
+  __device__ __forceinline__ int operator()(int s, int db) const { return e[s] + 64 * db; }
+};
+
+// The transposed A operand of block db, at offsets off(., db) from blk.
 template <int D>
-__device__ __forceinline__ bf16x8_t tr_read(const char* blk, const int (&off)[2][D / 32], int db) {
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(blk + off[0][db]));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(blk + off[1][db]));
+__device__ __forceinline__ bf16x8_t tr_read(const char* blk, const TrOff<D>& off, int db) {
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(blk + off(0, db)));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(blk + off(1, db)));
   const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
   return __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
 }
