@@ -40,6 +40,8 @@
 // the next tile loading while the current one is used; rows past the end of
 // the subsequence read as zeros (out of the buffer range), which makes
 // their contributions exactly zero.
+#include <atomic>
+
 #include "osp_internal.hpp"
 #include "osp_mfma.hpp"
 
@@ -202,7 +204,34 @@ struct TileDma {
     }
     return i0;
   }
+  // the same from a row table: tab[r] = token of row r of subsequence 0,
+  // cj = token(0, j) (the per-row remaps differ between subsequences by a
+  // constant)
+  __device__ __forceinline__ uint32_t at_tab(int t, const uint32_t* tab, uint32_t cj, int L,
+                                             int64_t sn) {
+    const int r0 = t * kBwdRows;
+    const uint32_t base = tab[min(r0, L - 1)];
+#pragma unroll
+    for (int u = 0; u < C::DPW; ++u) {
+      const int r = r0 + row(u);
+      const uint32_t tok = tab[min(r, L - 1)];
+      off[u] = (r < L) ? int32_t((int64_t(tok - base) * sn + 8 * col(u)) * 2) : kRecords;
+    }
+    return base + cj;
+  }
 };
+
+// TAB instances (per-row remaps): the workgroup tabulates token(r, 0) for
+// the L rows of a subsequence in dynamic LDS before its first load.
+extern __shared__ __attribute__((aligned(16))) uint32_t bwd_row_tab[];
+template <bool TAB>
+__device__ __forceinline__ uint32_t build_row_tab(int mode, uint32_t j, const SkipDiv& divk, int L) {
+  if constexpr (!TAB) return 0u;
+  for (int r = threadIdx.x; r < L; r += blockDim.x)
+    bwd_row_tab[r] = skiparse_token(mode, uint32_t(r), 0u, divk, uint32_t(L));
+  __syncthreads();
+  return skiparse_token(mode, 0u, j, divk, uint32_t(L));
+}
 // (The DMA instructions are issued from lambdas inside each kernel, with
 // the offset copied to a local first: this compiler's host pass drops a
 // kernel, without a diagnostic, whose buffer_load_lds builtin takes a
@@ -272,7 +301,8 @@ __device__ __forceinline__ void load_row_operand(const uint16_t* row, bool valid
 // 128 takes KB = 1.
 // S2D: the Skiparse-2D remap is compiled in; without it the mode is known
 // to be one of the four 1D ones, so their kernels carry none of its code.
-template <int D, bool PACKED, bool S2D>
+// TAB: tile rows from the LDS row table (build_row_tab).
+template <int D, bool PACKED, bool S2D, bool TAB>
 __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int KCH = C::KCH, KB = C::KB;
@@ -353,6 +383,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
 
   // ---- loads: the P waves load the Q tile and the -lse/scale row, the dS
   // waves the dO tile and the -delta row
+  const uint32_t tab_cj = build_row_tab<TAB>(mode, wb.j, divk, L);
   TileDma<D> dma;
   dma.init(pr, lane);
   const uint16_t* tsrc = (pw ? a.q : a.dout) + in_off;
@@ -369,14 +400,16 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   };
   auto load_floats = [&](uint32_t i0, int t, float* dst) __attribute__((always_inline)) {
     const int r = t * kBwdRows + lane;
-    const uint32_t i = skiparse_token(mode, uint32_t(min(r, L - 1)), wb.j, divk, uint32_t(L));
+    const uint32_t i = TAB ? bwd_row_tab[min(r, L - 1)] + tab_cj
+                           : skiparse_token(mode, uint32_t(min(r, L - 1)), wb.j, divk, uint32_t(L));
     const int32_t off = (r < L) ? int32_t((i - i0) * 4) : kRecords;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(fsrc + i0), (short)0, kRecords, 0x00020000);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 4, off, 0, 0, 0);
   };
   auto issue = [&](int t, auto sl) __attribute__((always_inline)) {
-    const uint32_t i0 = dma.at(t, mode, wb.j, divk, L, sn);
+    const uint32_t i0 = TAB ? dma.at_tab(t, bwd_row_tab, tab_cj, L, sn)
+                            : dma.at(t, mode, wb.j, divk, L, sn);
     if (pw) {
       load(i0, qslot(sl));
       if (pr == 0) load_floats(i0, t, lslot(sl));
@@ -549,7 +582,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(const BwdArgs a) {
 // 32-key block (C operand layout: keys are rows, the lane's query the
 // column), P = exp2 of one fma, dS^T = P o (dP^T - delta) packed to bf16,
 // and dQ^T += K^T dS^T with K^T read transposed.
-template <int D, bool PACKED, bool S2D>
+template <int D, bool PACKED, bool S2D, bool TAB>
 __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int NW = C::NW_Q;
@@ -605,6 +638,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
 
   static_assert(NW == C::LW || NW == 2 * C::LW, "one or two loading wave groups");
   const int lw = wave % C::LW;       // rank among the waves loading a tensor
+  const uint32_t tab_cj = build_row_tab<TAB>(mode, wb.j, divk, L);
   TileDma<D> dma;
   dma.init(lw, lane);
   const uint16_t* kg = a.k + in_off;
@@ -620,7 +654,8 @@ __global__ __launch_bounds__(BwdCfg<D>::NW_Q * 64, BwdCfg<D>::OCC_Q) void bwd_dq
     }
   };
   auto issue = [&](int t, auto sl) __attribute__((always_inline)) {
-    const uint32_t i0 = dma.at(t, mode, wb.j, divk, L, sn);
+    const uint32_t i0 = TAB ? dma.at_tab(t, bwd_row_tab, tab_cj, L, sn)
+                            : dma.at(t, mode, wb.j, divk, L, sn);
     if constexpr (NW == C::LW) {
       load(kg, i0, kslot(sl));
       load(vg, i0, vslot(sl));
@@ -746,6 +781,14 @@ static hipError_t launch_prep_d(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// LDS of a workgroup, static plus dynamic, in bytes; the static part of a
+// kernel (-1 if the runtime cannot say)
+constexpr int kBwdLdsBytes = 160 * 1024;
+static int static_lds_bytes(const void* kernel) {
+  hipFuncAttributes attr;
+  return hipFuncGetAttributes(&attr, kernel) == hipSuccess ? int(attr.sharedSizeBytes) : -1;
+}
+
 template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   using C = BwdCfg<D>;
@@ -753,16 +796,33 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint32_t seqs = uint32_t(a.batch) * uint32_t(a.heads) * uint32_t(a.groups);
   const dim3 kv_grid(seqs * uint32_t(a.kv_blocks)), q_grid(seqs * uint32_t(a.q_blocks));
-  if (a.mode >= MODE_SINGLE2D)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), kv_grid, dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), kv_grid, dim3(512), 0, s, a);
+  // Skiparse-2D: rows from an LDS row table when it fits beside the
+  // kernel's static LDS
+  const size_t tab = size_t(a.seq_len) * 4;
+  if (a.mode >= MODE_SINGLE2D) {
+    auto kv = bwd_dkdv_kernel<D, false, true, true>;
+    static std::atomic<int> kv_lds{-1};
+    if (kv_lds.load() < 0) kv_lds.store(static_lds_bytes(reinterpret_cast<const void*>(kv)));
+    if (kv_lds.load() >= 0 && kv_lds.load() + tab <= size_t(kBwdLdsBytes))
+      hipLaunchKernelGGL(kv, kv_grid, dim3(512), tab, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true, false>), kv_grid, dim3(512), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false, false>), kv_grid, dim3(512), 0, s, a);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.mode >= MODE_SINGLE2D)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), q_grid, dim3(C::NW_Q * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), q_grid, dim3(C::NW_Q * 64), 0, s, a);
+  if (a.mode >= MODE_SINGLE2D) {
+    auto qk = bwd_dq_kernel<D, false, true, true>;
+    static std::atomic<int> q_lds{-1};
+    if (q_lds.load() < 0) q_lds.store(static_lds_bytes(reinterpret_cast<const void*>(qk)));
+    if (q_lds.load() >= 0 && q_lds.load() + tab <= size_t(kBwdLdsBytes))
+      hipLaunchKernelGGL(qk, q_grid, dim3(C::NW_Q * 64), tab, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false, true, false>), q_grid, dim3(C::NW_Q * 64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false, false, false>), q_grid, dim3(C::NW_Q * 64), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -770,10 +830,10 @@ template <int D>
 static hipError_t launch_packed_d(const BwdArgs& pa, int kv_grid, int q_grid, hipStream_t s) {
   using C = BwdCfg<D>;
   // packed calls take the 1D modes only
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), dim3(kv_grid), dim3(512), 0, s, pa);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false, false>), dim3(kv_grid), dim3(512), 0, s, pa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), dim3(q_grid), dim3(C::NW_Q * 64), 0, s, pa);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, false>), dim3(q_grid), dim3(C::NW_Q * 64), 0, s, pa);
   return hipGetLastError();
 }
 
