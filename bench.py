@@ -51,6 +51,8 @@ LINES = {
     "osp720_full": ("osp720", "full", 1),
     "osp720_skiparse_single_k4": ("osp720", "skiparse_single", 4),
     "osp720_skiparse_group_k4": ("osp720", "skiparse_group", 4),
+    # 121x576x1024 through an 8x8x8 VAE: 16x36x64 = 36,864 tokens, head_dim 128
+    "osp15_full": ("osp15", "full", 1),
 }
 
 
@@ -105,6 +107,9 @@ def parse():
                         "(packed, packed_bwd)")
     p.add_argument("--copy", type=int, default=0,
                    help="instead: time a plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--gemm", type=int, default=0,
+                   help="instead: time a bf16 GEMM of this size cubed through torch.matmul "
+                        "(the vendor library's dense MFMA rate on this device, for context)")
     p.add_argument("--summarize", nargs="+", metavar="DIR",
                    help="instead: summarise rocprofv3 --pmc output directories (see summarize())")
     p.add_argument("--line", help="with --summarize: the line name the counters were taken on")
@@ -200,6 +205,29 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_mib": args.copy, "bytes_read": n * 4, "bytes_written": n * 4}))
+        return
+    if args.gemm:
+        # C = A B in bf16 (fp32 accumulation inside the library), square
+        # operands; the rate it holds under sustained load is the practical
+        # ceiling that the attention kernels' MFMA rates are read against
+        m = args.gemm
+        ga = torch.randn(m, m, device=dev).to(torch.bfloat16)
+        gb = torch.randn(m, m, device=dev).to(torch.bfloat16)
+        gc = torch.empty(m, m, device=dev, dtype=torch.bfloat16)
+        for _ in range(max(args.warmup, 3)):
+            torch.matmul(ga, gb, out=gc)
+        torch.cuda.synchronize()
+        reps = max(args.steps, 20)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(ga, gb, out=gc)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * m ** 3 / (ms * 1e-3) / 1e12
+        print(json.dumps({"gemm": m, "dtype": "bf16", "ms_per_call": round(ms, 4),
+                          "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}))
         return
 
     class Work:
