@@ -90,6 +90,22 @@ typedef enum {
 #define OSP_FUSE_ROPE_K 2  /* rotate K inside the attention loader; without it
                               K is taken as already rotated                  */
 #define OSP_FUSE_ROPE 3    /* both                                           */
+#define OSP_ONE_TILE_PER_WORKGROUP 4
+                           /* launch one workgroup per query tile.  Without
+                              it, a call at head_dim 96 whose rows map to
+                              tokens with a fixed stride (full, BLOCK,
+                              SKIPARSE_SINGLE, SKIPARSE_GROUP with 64 % k ==
+                              0) and with more query tiles than the GPU holds
+                              workgroups at once launches that many
+                              workgroups, each taking its XCD's tiles in
+                              turn (the RoPE table built once, the next
+                              tile's first loads overlapping the current
+                              tile's end).  Results are the same bits either
+                              way; the flag is for comparison and for
+                              callers sharing the GPU with concurrent
+                              kernels.  Other calls, packed calls and
+                              OSP_FUSE_ROPE_K always take one tile per
+                              workgroup. */
 
 /* Shape, layout and RoPE settings of one attention call. */
 typedef struct {
@@ -224,7 +240,8 @@ osp_status osp_rope3d_inv(const osp_attn3d_desc* desc, const void* x, void* y,
    (else OSP_ERR_UNSUPPORTED; rotate K with osp_rope3d instead).  It is
    slower than rotating K once with osp_rope3d and passing OSP_FUSE_ROPE_Q
    alone, since every query tile rotates the same K again: use it where a
-   rotated copy of K cannot be held.
+   rotated copy of K cannot be held.  OSP_ONE_TILE_PER_WORKGROUP: see its
+   definition above.
    q, k, v: [B, N, H, D] bf16 read with stride_*; o: written with ostride_*,
    must not overlap q, k or v.  lse: NULL, or [B, H, N] fp32 contiguous,
    receives ln(sum_j exp(sm_scale * q_i . k_j)) over the row's subsequence,

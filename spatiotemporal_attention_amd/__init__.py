@@ -22,6 +22,7 @@ MODES = {"full": 0, "skiparse_single": 1, "skiparse_group": 2, "block": 3, "skip
 OSP_FUSE_ROPE_Q = 1
 OSP_FUSE_ROPE_K = 2
 OSP_FUSE_ROPE = 3
+OSP_ONE_TILE_PER_WORKGROUP = 4
 ABI_VERSION = 1
 
 
@@ -197,7 +198,7 @@ def osp_attn3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid,
                    theta: float = 1e4, sm_scale: float | None = None,
                    fuse_rope=True, pos_offset=(0, 0, 0),
                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-                   return_lse: bool = False):
+                   return_lse: bool = False, one_tile_per_workgroup: bool = False):
     """Attention forward over [B, N, H, D] bf16 q, k, v on the GPU.
 
     fuse_rope: True (q and k unrotated: k is rotated by osp_rope3d into a
@@ -205,6 +206,8 @@ def osp_attn3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid,
     already rotated), "q" or "k" (only that one unrotated, rotated in its
     loader), "qk" (both rotated in the loaders, no temporary; slower, since
     every query tile rotates the same K again).  All give the same bits.
+    one_tile_per_workgroup: pass OSP_ONE_TILE_PER_WORKGROUP (no persistent
+    launch; the same bits).
     Returns o (and lse [B, H, N] fp32 when return_lse or lse is given)."""
     b, n, h, d = q.shape
     st = _bnhd(q, "q")
@@ -227,7 +230,8 @@ def osp_attn3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, grid,
                        pos_offset=pos_offset, out=_like_strided(k))
     _check(lib().osp_attn3d_fwd(
         ctypes.byref(desc), _mode(mode), int(sparse_k),
-        float(sm_scale) if sm_scale is not None else 0.0, _flags(fuse_rope),
+        float(sm_scale) if sm_scale is not None else 0.0,
+        _flags(fuse_rope) | (OSP_ONE_TILE_PER_WORKGROUP if one_tile_per_workgroup else 0),
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
         ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
         ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), _stream(q)))

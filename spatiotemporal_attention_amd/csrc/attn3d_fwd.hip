@@ -132,10 +132,16 @@ __device__ __forceinline__ void for_slots(F&& f, std::integer_sequence<int, I...
 // (Group Skip: j*k; Skiparse-2D: jh*W + jw, times s for group), so the
 // workgroup tabulates token(r, 0) for its L rows once, in dynamic LDS, and
 // the loader looks rows up instead of dividing.
+// PERSIST: the grid holds one workgroup per slot the chip can run at once,
+// and each workgroup walks its XCD's list of query tiles (see "which tiles"
+// below) instead of taking one: the RoPE and row tables are built once,
+// and the first K/V tiles and the Q rows of the next query tile are
+// requested while the current one finishes.
 template <int D, int QB, int BN, int NW, int OCC, int NS, bool ROPE_Q, bool ROPE_K,
-          bool FIXED_ROWS, bool PACKED, bool TAB>
+          bool FIXED_ROWS, bool PACKED, bool TAB, bool PERSIST>
 __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs a) {
   static_assert(!TAB || !FIXED_ROWS, "the row table serves the per-row remap");
+  static_assert(!PERSIST || (!PACKED && !ROPE_K), "persistent launches: plain calls, K rotated before");
   extern __shared__ __attribute__((aligned(16))) uint32_t row_tab[];   // TAB: L entries
   using C = AttnCfg<D, QB, BN, NW>;
   constexpr int NKB = BN / 32;        // 32-key blocks per tile
@@ -145,8 +151,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   // The last slot of K and of V share one array, which also holds the RoPE
   // cos/sin table while Q is rotated in the prologue (when K is not
   // rotated in the loader, the table is used nowhere else); it is at least
-  // a RopeLds long.
-  constexpr int kSL = (ROPE_Q && !ROPE_K && 2 * C::TILE * 2 < int(sizeof(RopeLds)))
+  // a RopeLds long.  A persistent workgroup rotates the Q rows of every
+  // tile it takes, so there the table has an array of its own.
+  constexpr bool kOwnTable = ROPE_K || (ROPE_Q && PERSIST);
+  constexpr int kSL = (ROPE_Q && !kOwnTable && 2 * C::TILE * 2 < int(sizeof(RopeLds)))
                           ? int((sizeof(RopeLds) + 1) / 2) : 2 * C::TILE;
   // (slots 2 .. 4 that are not used, or are the last, take 8 elements)
   constexpr int kT2 = NS > 3 ? C::TILE : 8, kT3 = NS > 4 ? C::TILE : 8, kT4 = NS > 5 ? C::TILE : 8;
@@ -176,8 +184,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     else return v_s4;
   };
   // K rotated in the loader reads the table in every tile: its own array
-  __shared__ __attribute__((aligned(16))) RopeSmem<ROPE_K> rsm;
-  RopeLds* const rl = ROPE_K ? rsm.get() : ROPE_Q ? reinterpret_cast<RopeLds*>(kv_sl) : nullptr;
+  __shared__ __attribute__((aligned(16))) RopeSmem<kOwnTable> rsm;
+  RopeLds* const rl = kOwnTable ? rsm.get() : ROPE_Q ? reinterpret_cast<RopeLds*>(kv_sl) : nullptr;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -187,12 +195,28 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   const int g = lane >> 5;      // half of the wave
   const int l32 = lane & 31;
 
-  // ---- which tile: consecutive tiles of one (b, h, j) stay on one XCD ----
-  // (workgroup x runs on XCD x mod 8; XCD c takes the c-th eighth of the tiles)
+  // ---- which tiles: consecutive tiles of one (b, h, j) stay on one XCD ----
+  // Workgroup x runs on XCD x mod 8.  XCD c takes the c-th eighth of the
+  // tiles (the last total mod 8 tiles go one to each of the first XCDs),
+  // and its workgroups take that list in order: workgroup x the entry
+  // x / 8, a persistent one every (grid / 8)-th entry from there.
   const uint32_t total = uint32_t(a.total_tiles);
-  const uint32_t t8 = total & ~7u;
+  const uint32_t t8 = total & ~7u, q8 = t8 >> 3;
   const uint32_t x = blockIdx.x;
-  uint32_t u = (x < t8) ? (x & 7u) * (t8 >> 3) + (x >> 3) : x;
+  const uint32_t xcd = x & 7u;
+  uint32_t wn = x >> 3;
+  if (PERSIST && wn >= q8 + (xcd < (total & 7u) ? 1u : 0u)) return;   // (not launched so)
+  uint32_t u = wn < q8 ? xcd * q8 + wn : t8 + xcd;
+
+  // The argument block, for values read once per tile.  A persistent
+  // workgroup reads it through a pointer the compiler cannot see through,
+  // so that such values are read again at each tile instead of being held
+  // in registers through the tile loop.
+  auto args = [&]() __attribute__((always_inline)) -> const AttnArgs* {
+    auto p = (const __attribute__((address_space(4))) AttnArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    if constexpr (PERSIST) asm volatile("" : "+s"(p));
+    return (const AttnArgs*)p;
+  };
 
   // kernel arguments used below, as locals (keeps the argument block out of
   // private memory)
@@ -223,12 +247,24 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     rg.div_hw = ps.div_hw;
     rg.div_w = ps.div_w;
   }
-  const uint32_t qt = u % uint32_t(q_tiles);
-  u /= uint32_t(q_tiles);
-  const uint32_t j = u % uint32_t(a.groups);
-  u /= uint32_t(a.groups);
-  const uint32_t h = u % uint32_t(a.heads);
-  const uint32_t b = u / uint32_t(a.heads);
+  // (query tile, subsequence, head, batch) of tile w
+  struct TileId {
+    uint32_t qt, j, h, b;
+  };
+  auto decode = [&](uint32_t w) __attribute__((always_inline)) {
+    const AttnArgs* A = args();
+    const uint32_t nq = PACKED ? uint32_t(q_tiles) : uint32_t(A->q_tiles);
+    TileId r;
+    r.qt = w % nq;
+    w /= nq;
+    r.j = w % uint32_t(A->groups);
+    w /= uint32_t(A->groups);
+    r.h = w % uint32_t(A->heads);
+    r.b = w / uint32_t(A->heads);
+    return r;
+  };
+  uint32_t ucur = u;                   // the current tile
+  const uint32_t jcur = decode(u).j;   // its subsequence (one-tile workgroups)
 
   // the fixed-row path serves only 1D modes, which the compiler then knows
   const int mode = FIXED_ROWS ? (a.mode & 3) : a.mode;
@@ -237,11 +273,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
 
   const int L = seq_len;
   const int nkt = (L + BN - 1) / BN;
-  const int64_t in_off = int64_t(b) * a.sb + int64_t(h) * a.sh + tok0 * a_sn;
-  const uint16_t* __restrict__ qg = a.q + in_off;
-  const uint16_t* __restrict__ kg = a.k + in_off;
-  const uint16_t* __restrict__ vg = a.v + in_off;
-  const float c2 = a.scale_log2;
+  // element offset of tile w's (batch, head) in q, k and v
+  auto in_off = [&](uint32_t w) __attribute__((always_inline)) {
+    const TileId t = decode(w);
+    const AttnArgs* A = args();
+    return int64_t(t.b) * A->sb + int64_t(t.h) * A->sh + tok0 * a_sn;
+  };
+  // K and V at the tile's (batch, head) (one-tile workgroups)
+  const uint16_t* kg = a.k + in_off(ucur);
+  const uint16_t* vg = a.v + in_off(ucur);
+  // tiles of one query tile, padded to a multiple of the slot count (see
+  // the schedule below)
+  const bool ragged = (L % BN) != 0;
+  const int nkt3 = (nkt + NS - 1) / NS * NS;
 
   const bool fast_rope = rg.aligned8 && rg.tab_entries;
 
@@ -254,7 +298,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   // to i0(kt) + drow(row), so per-lane byte offsets are fixed and only the
   // tile base moves.  K of tile kt goes to K slot kt&1, V to V slot kt&1.
   const int kmul = (mode == MODE_SINGLE || mode == MODE_GROUP) ? int(divk.d) : 1;
-  auto drow_of = [&](int rw) __attribute__((always_inline)) -> uint32_t {
+  auto drow_of = [mode, kmul](int rw) __attribute__((always_inline)) -> uint32_t {
     const uint32_t r = uint32_t(rw);
     return (mode == MODE_FULL || mode == MODE_BLOCK) ? r
          : (mode == MODE_SINGLE) ? r * uint32_t(kmul)
@@ -272,13 +316,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     dm_col[t] = (p % C::KCH) ^ chunk_swz<D>(dm_row[t]);    // logical chunk
     dm_off[t] = int32_t((int64_t(drow_of(dm_row[t])) * a_sn + 8 * dm_col[t]) * 2);
   }
-  // first token of tile kt: with FIXED_ROWS, i0(kt) = kt*BN*kmul + c_j
-  const int64_t tile_c0 = (mode == MODE_SINGLE) ? int64_t(j)
-                        : (mode == MODE_GROUP) ? int64_t(j) * kmul
-                        : (mode == MODE_BLOCK) ? int64_t(j) * L : 0;
-  auto tile_first = [&](int kt) __attribute__((always_inline)) -> uint32_t {
-    if constexpr (FIXED_ROWS) return uint32_t(int64_t(kt) * BN * kmul + tile_c0);
-    else return skiparse_token(mode, uint32_t(kt * BN), j, divk, uint32_t(L));
+  // first token of tile kt of subsequence jj: with FIXED_ROWS, i0(kt) =
+  // kt*BN*kmul + c_jj
+  auto tile_first = [mode, kmul, L, divk](int kt, uint32_t jj) __attribute__((always_inline))
+      -> uint32_t {
+    if constexpr (FIXED_ROWS) {
+      const int64_t c0 = (mode == MODE_SINGLE) ? int64_t(jj)
+                       : (mode == MODE_GROUP) ? int64_t(jj) * kmul
+                       : (mode == MODE_BLOCK) ? int64_t(jj) * L : 0;
+      return uint32_t(int64_t(kt) * BN * kmul + c0);
+    } else {
+      return skiparse_token(mode, uint32_t(kt * BN), jj, divk, uint32_t(L));
+    }
   };
   // Skiparse-2D rows: a tile's row dm_row[t] split once into (frames,
   // lattice rows, columns) of the (H/s) x (W/s) lattice, packed 10 bits
@@ -296,8 +345,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     const uint32_t dh = fdiv(rem, divk.row);
     dm_lat[t] = dt | (dh << 10) | ((rem - dh * divk.row.d) << 20);
   }
-  // TAB: token(0, j), the subsequence's offset from the table's tokens
-  const uint32_t tab_cj = TAB ? skiparse_token(mode, 0u, j, divk, uint32_t(L)) : 0u;
+  // TAB: token(0, jj), subsequence jj's offset from the table's tokens
+  auto tab_cj = [&](uint32_t jj) __attribute__((always_inline)) {
+    return TAB ? skiparse_token(mode, 0u, jj, divk, uint32_t(L)) : 0u;
+  };
   // tile kt of the tensor at src into LDS tile dst (rows past the end read
   // as zeros: their offsets are out of the buffer's range).  USE_TAB: rows
   // from the row table (built in the prologue, after the first tiles are
@@ -305,7 +356,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   // The table entries of a tile (its first row, then this lane's rows) are
   // read one tile ahead: each half requests consecutive tiles, one per
   // iteration, so the entries of the next are read right after a tile is
-  // requested and have arrived when it is its turn.
+  // requested and have arrived when it is its turn (fetch_kt: the next
+  // request's tile, in its own subsequence).
   uint32_t tab_nx[C::DPW + 1];
   auto tab_fetch = [&](int kt) __attribute__((always_inline)) {
     const uint32_t r0 = uint32_t(kt * BN);
@@ -314,10 +366,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     for (int t = 0; t < C::DPW; ++t)
       tab_nx[t + 1] = row_tab[min(r0 + uint32_t(dm_row[t]), uint32_t(L - 1))];
   };
-  auto dma_tile_tab = [&](const uint16_t* src, int kt, uint16_t* dst) __attribute__((always_inline)) {
+  auto dma_tile_tab = [&](const uint16_t* src, int kt, uint16_t* dst, uint32_t cj, int fetch_kt)
+      __attribute__((always_inline)) {
     const uint32_t base = tab_nx[0];
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(src + int64_t(base + tab_cj) * a_sn), (short)0, kRecords, 0x00020000);
+        const_cast<uint16_t*>(src + int64_t(base + cj) * a_sn), (short)0, kRecords, 0x00020000);
 #pragma unroll
     for (int t = 0; t < C::DPW; ++t) {
       int32_t off = int32_t((tab_nx[t + 1] - base) * sn2 + 16u * uint32_t(dm_col[t]));
@@ -325,10 +378,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(dst + 512 * (lw + C::LW * t)), 16,
                                                off, 0, 0, 0);
     }
-    tab_fetch(kt + 1);
+    tab_fetch(fetch_kt);
   };
-  auto dma_tile = [&](const uint16_t* src, int kt, uint16_t* dst) __attribute__((always_inline)) {
-    const uint32_t i0 = tile_first(kt);
+  auto dma_tile = [&](const uint16_t* src, int kt, uint16_t* dst, uint32_t jj)
+      __attribute__((always_inline)) {
+    const uint32_t i0 = tile_first(kt, jj);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(src + int64_t(i0) * a_sn), (short)0, kRecords, 0x00020000);
     // lattice position of the tile's first row, and the subsequence's (jh, jw)
@@ -336,7 +390,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     const uint32_t t0 = fdiv(r0, divk.plane);
     const uint32_t h0 = fdiv(r0 - t0 * divk.plane.d, divk.row);
     const uint32_t w0 = r0 - t0 * divk.plane.d - h0 * divk.row.d;
-    const uint32_t jh = fdiv(j, divk.axis), jw = j - jh * divk.axis.d;
+    const uint32_t jh = fdiv(jj, divk.axis), jw = jj - jh * divk.axis.d;
 #pragma unroll
     for (int t = 0; t < C::DPW; ++t) {
       int32_t off = dm_off[t];
@@ -356,7 +410,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
           off = int32_t((i - i0) * sn2 + 16u * uint32_t(dm_col[t]));
         } else {
           const uint32_t r = uint32_t(min(kt * BN + dm_row[t], L - 1));
-          off = int32_t((int64_t(skiparse_token(mode, r, j, divk, uint32_t(L)) - i0) * a_sn + 8 * dm_col[t]) * 2);
+          off = int32_t((int64_t(skiparse_token(mode, r, jj, divk, uint32_t(L)) - i0) * a_sn + 8 * dm_col[t]) * 2);
         }
       }
       off = (dm_row[t] < L - kt * BN) ? off : kRecords;
@@ -375,7 +429,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       const int row = idx / C::KCH, col = idx % C::KCH;
       const bool on = kt * BN + row < L;
       const uint32_t r = uint32_t(min(kt * BN + row, L - 1));
-      const uint32_t i = skiparse_token(mode, r, j, divk, uint32_t(L));
+      const uint32_t i = skiparse_token(mode, r, jcur, divk, uint32_t(L));
       st_reg[e] = on ? ld16(kg + int64_t(i) * a_sn + 8 * col) : make_uint4(0, 0, 0, 0);
     }
   };
@@ -386,7 +440,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       const int row = idx / C::KCH, col = idx % C::KCH;
       uint4 val = st_reg[e];
       const int r = kt * BN + row;
-      const uint32_t i = skiparse_token(mode, uint32_t(min(r, L - 1)), j, divk, uint32_t(L));
+      const uint32_t i = skiparse_token(mode, uint32_t(min(r, L - 1)), jcur, divk, uint32_t(L));
       if (r < L && is_video(rg, i)) {
         const Coord3 cc = video_coords(rg, i);
         val = fast_rope ? rotate_chunk_col(rl, chunk_col(rg, 4 * col), cc, val)
@@ -402,17 +456,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   f32x16_t o[QB][D / 32];
   f32x16_t negm[QB];
   float mref[QB], lsum[QB];
+  auto init_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    mref[qb] = 0.f;
-    lsum[qb] = 0.f;
+    for (int qb = 0; qb < QB; ++qb) {
+      mref[qb] = 0.f;
+      lsum[qb] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) negm[qb][e] = 0.f;
+      for (int e = 0; e < 16; ++e) negm[qb][e] = 0.f;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[qb][db][e] = 0.f;
-  }
+        for (int e = 0; e < 16; ++e) o[qb][db][e] = 0.f;
+    }
+  };
 
   // per-lane LDS byte offsets of the operand reads (swizzle folded in)
   const RowOff<D> k_off(lane);
@@ -557,24 +613,61 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
 
   // Loads of one tile: the leading half loads K tiles, the trailing half V
   // tiles.  issue_tile starts them; finish_tile completes the staged
-  // (rotating) K path.
+  // (rotating) K path.  Requests kt >= nkt3 are the padding of the last
+  // group; a persistent workgroup with a next tile requests that tile's
+  // tiles 0, 1, ... there instead (into the same slots, nkt3 being a
+  // multiple of NS).
+  //
+  // A persistent workgroup keeps, per wave, one base sb for the tensor the
+  // wave loads (K in the leading half, V in the trailing half) with the
+  // subsequence's offset folded in (c_j with fixed rows, token(0, j) with
+  // the row table; both instances take subsequence 0's offsets from
+  // there).  It moves to the next tile's at that tile's first request.
+  // (The base is formed there rather than chosen between two variables:
+  // a run-time choice between two variables these lambdas capture by
+  // reference becomes a load at a computed offset into the capture block,
+  // which the compiler then keeps in scratch memory, with everything it
+  // points to.)
+  const uint32_t cj_cur = tab_cj(jcur);
+  auto stream_base = [&](uint32_t w) __attribute__((always_inline)) -> const uint16_t* {
+    const AttnArgs* A = args();
+    const uint32_t jj = decode(w).j;
+    const int64_t c = FIXED_ROWS ? int64_t(tile_first(0, jj)) : int64_t(tab_cj(jj));
+    return (lead ? A->k : A->v) + in_off(w) + c * a_sn;
+  };
+  bool has_next = false;
+  uint32_t unxt = ucur;
+  const uint16_t* sb = nullptr;
+  if constexpr (PERSIST) sb = stream_base(ucur);
   auto issue_tile = [&](int kt, auto slot) __attribute__((always_inline)) {
-    if (lead) {
+    if constexpr (PERSIST) {
+      const bool nx = has_next && kt >= nkt3;
+      if (has_next && kt == nkt3) sb = stream_base(unxt);
+      const int kk = nx ? kt - nkt3 : kt;
+      const int fetch = (has_next && kt + 1 >= nkt3) ? kt + 1 - nkt3 : kt + 1;
+      if constexpr (TAB) {
+        if (lead) dma_tile_tab(sb, kk, kslot(slot), 0u, fetch);
+        else dma_tile_tab(sb, kk, vslot(slot), 0u, fetch);
+      } else {
+        if (lead) dma_tile(sb, kk, kslot(slot), 0u);
+        else dma_tile(sb, kk, vslot(slot), 0u);
+      }
+    } else if (lead) {
       if constexpr (ROPE_K) staged_issue(kt);
-      else if constexpr (TAB) dma_tile_tab(kg, kt, kslot(slot));
-      else dma_tile(kg, kt, kslot(slot));
+      else if constexpr (TAB) dma_tile_tab(kg, kt, kslot(slot), cj_cur, kt + 1);
+      else dma_tile(kg, kt, kslot(slot), jcur);
     } else {
-      if constexpr (TAB) dma_tile_tab(vg, kt, vslot(slot));
-      else dma_tile(vg, kt, vslot(slot));
+      if constexpr (TAB) dma_tile_tab(vg, kt, vslot(slot), cj_cur, kt + 1);
+      else dma_tile(vg, kt, vslot(slot), jcur);
     }
   };
-  // the prologue's tiles, requested before the row table exists
+  // the first tile's first tiles, requested before the row table exists
   auto issue_tile_first = [&](int kt, auto slot) __attribute__((always_inline)) {
     if (lead) {
       if constexpr (ROPE_K) staged_issue(kt);
-      else dma_tile(kg, kt, kslot(slot));
+      else dma_tile(kg, kt, kslot(slot), jcur);
     } else {
-      dma_tile(vg, kt, vslot(slot));
+      dma_tile(vg, kt, vslot(slot), jcur);
     }
   };
   auto finish_tile = [&](int kt, auto slot) __attribute__((always_inline)) {
@@ -608,16 +701,32 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   }
   // Q rows: every chunk is requested before any is used (a row past the end
   // reads the last row and is zeroed afterwards, so the loads need no
-  // branch); the table is built while they are in flight.
+  // branch); the tables are built while they are in flight.
   uint4 qraw[QB][D / 16];
+  // Lane coordinates formed again where a persistent workgroup uses them
+  // once per tile, so that the compiler does not hold what it derives from
+  // them through the tile loop.
+  auto lane_ids = [&](int& l, int& gg) __attribute__((always_inline)) {
+    int x = lane;
+    if constexpr (PERSIST) asm volatile("" : "+v"(x));
+    l = x & 31;
+    gg = x >> 5;
+  };
+  auto load_q = [&](uint32_t w) __attribute__((always_inline)) {
+    const TileId tl = decode(w);
+    const uint16_t* qsrc = args()->q + in_off(w);
+    int lq, gq;
+    lane_ids(lq, gq);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int r = int(qt) * C::BM + (wave * QB + qb) * 32 + l32;
-    const uint32_t i = skiparse_token(mode, uint32_t(min(r, L - 1)), j, divk, uint32_t(L));
-    const uint16_t* p = qg + int64_t(i) * a_sn;
+    for (int qb = 0; qb < QB; ++qb) {
+      const int r = int(tl.qt) * C::BM + (wave * QB + qb) * 32 + lq;
+      const uint32_t i = skiparse_token(mode, uint32_t(min(r, L - 1)), tl.j, divk, uint32_t(L));
+      const uint16_t* p = qsrc + int64_t(i) * a_sn;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) qraw[qb][c] = ld16(p + 16 * c + 8 * g);
-  }
+      for (int c = 0; c < D / 16; ++c) qraw[qb][c] = ld16(p + 16 * c + 8 * gq);
+    }
+  };
+  load_q(ucur);
   // the row table, while the loads above are in flight (the barriers below
   // or the prologue's last one publish it)
   if constexpr (TAB) {
@@ -630,30 +739,40 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     fill_rope_table(rg, rl, tid, C::NT);
     lds_barrier();
   }
+  // Q^T operand of the current tile from the rows in qraw
+  auto rotate_q = [&]() __attribute__((always_inline)) {
+    const TileId tc = decode(ucur);
+    // (a persistent workgroup reads the geometry and the scale again here)
+    const RopeGeom rq = PERSIST ? rope_scalars(args()->rope) : rg;
+    const bool fast_rq = rq.aligned8 && rq.tab_entries;
+    const float c2 = args()->scale_log2;
+    int lq, gq;
+    lane_ids(lq, gq);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int r = int(qt) * C::BM + (wave * QB + qb) * 32 + l32;
-    const bool valid = r < L;
-    const uint32_t i = skiparse_token(mode, uint32_t(valid ? r : 0), j, divk, uint32_t(L));
-    const bool video = ROPE_Q && is_video(rg, i);
-    const Coord3 cc = video_coords(rg, i);
+    for (int qb = 0; qb < QB; ++qb) {
+      const int r = int(tc.qt) * C::BM + (wave * QB + qb) * 32 + lq;
+      const bool valid = r < L;
+      const uint32_t i = skiparse_token(mode, uint32_t(valid ? r : 0), tc.j, divk, uint32_t(L));
+      const bool video = ROPE_Q && is_video(rq, i);
+      const Coord3 cc = video_coords(rq, i);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      uint4 raw = valid ? qraw[qb][c] : make_uint4(0, 0, 0, 0);
-      // times scale * log2(e) so that the score products come out in log2
-      // units; a rotated row is rotated and scaled in fp32, rounded once
-      if (ROPE_Q && video) {
-        raw = fast_rope ? rotate_chunk_col_scaled(rl, chunk_col(rg, 8 * c + 4 * g), cc, raw, c2)
-                        : rotate_chunk_scaled(rg, rl, 8 * c + 4 * g, cc, raw, c2);
-      } else {
-        raw.x = pack_bf16(bf16lo(raw.x) * c2, bf16hi(raw.x) * c2);
-        raw.y = pack_bf16(bf16lo(raw.y) * c2, bf16hi(raw.y) * c2);
-        raw.z = pack_bf16(bf16lo(raw.z) * c2, bf16hi(raw.z) * c2);
-        raw.w = pack_bf16(bf16lo(raw.w) * c2, bf16hi(raw.w) * c2);
+      for (int c = 0; c < D / 16; ++c) {
+        uint4 raw = valid ? qraw[qb][c] : make_uint4(0, 0, 0, 0);
+        // times scale * log2(e) so that the score products come out in log2
+        // units; a rotated row is rotated and scaled in fp32, rounded once
+        if (ROPE_Q && video) {
+          raw = fast_rq ? rotate_chunk_col_scaled(rl, chunk_col(rq, 8 * c + 4 * gq), cc, raw, c2)
+                        : rotate_chunk_scaled(rq, rl, 8 * c + 4 * gq, cc, raw, c2);
+        } else {
+          raw.x = pack_bf16(bf16lo(raw.x) * c2, bf16hi(raw.x) * c2);
+          raw.y = pack_bf16(bf16lo(raw.y) * c2, bf16hi(raw.y) * c2);
+          raw.z = pack_bf16(bf16lo(raw.z) * c2, bf16hi(raw.z) * c2);
+          raw.w = pack_bf16(bf16lo(raw.w) * c2, bf16hi(raw.w) * c2);
+        }
+        qreg[qb][c] = __builtin_bit_cast(bf16x8_t, raw);
       }
-      qreg[qb][c] = __builtin_bit_cast(bf16x8_t, raw);
     }
-  }
+  };
 
   // ---- ping-pong schedule.  The waves form two halves, one wave of each
   // on every SIMD.  Per key tile t a wave runs a matrix phase M(t) (S(t) =
@@ -674,8 +793,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   // tiles past the end of the subsequence (keys masked to -inf, loads out
   // of range of the buffer, which read as zeros), so that every slot index
   // is a compile-time constant.
-  const bool ragged = (L % BN) != 0;
-  const int nkt3 = (nkt + NS - 1) / NS * NS;
   f32x16_t s[NKB][QB];
   bf16x8_t pb[QB][NKB][2];
 
@@ -749,76 +866,102 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     }
   };
 
-  // prologue, part 2: K and V of tiles 0 .. NS-2 into their slots (with K
-  // rotation in the loader: here); V slot NS-1 (read as "V(-1)" by the
-  // first matrix phase, with P = 0) cleared, once every wave has finished
-  // reading the table it shares with that slot
-  if constexpr (ROPE_Q && !ROPE_K) lds_barrier();
-  for (int e = tid; e < C::TILE / 8; e += C::NT)
-    reinterpret_cast<uint4*>(vslot(int_c<NS - 1>{}))[e] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      pb[qb][kb][0] = bf16x8_t{};
-      pb[qb][kb][1] = bf16x8_t{};
+  // ---- the tiles of this workgroup: one, or (persistent) a list ----
+  for (;;) {
+    rotate_q();
+    init_acc();
+    if constexpr (PERSIST) {
+      const AttnArgs* A = args();
+      const uint32_t tot = uint32_t(A->total_tiles), tq8 = tot >> 3, xc = blockIdx.x & 7u;
+      const uint32_t wnx = wn + (gridDim.x >> 3);
+      has_next = wnx < tq8 + (xc < (tot & 7u) ? 1u : 0u);
+      if (has_next) unxt = wnx < tq8 ? xc * tq8 + wnx : (tot & ~7u) + xc;
     }
-  if constexpr (ROPE_K) {
-    for_slots([&](auto sl) __attribute__((always_inline)) {
-      if constexpr (decltype(sl)::value < NS - 1) {
-        issue_tile_first(decltype(sl)::value, sl);
-        finish_tile(decltype(sl)::value, sl);
+    // prologue, part 2: K and V of tiles 0 .. NS-2 into their slots (with K
+    // rotation in the loader: here); V slot NS-1 (read as "V(-1)" by the
+    // first matrix phase, with P = 0) cleared, once every wave has finished
+    // reading it: the RoPE table it holds in the prologue, or (persistent)
+    // the previous tile's last V tile
+    if constexpr ((ROPE_Q && !ROPE_K) || PERSIST) lds_barrier();
+    for (int e = tid; e < C::TILE / 8; e += C::NT)
+      reinterpret_cast<uint4*>(vslot(int_c<NS - 1>{}))[e] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        pb[qb][kb][0] = bf16x8_t{};
+        pb[qb][kb][1] = bf16x8_t{};
       }
-    }, std::make_integer_sequence<int, NS>{});
-  }
-  __syncthreads();
-  if constexpr (TAB) tab_fetch(NS - 1);    // the first tile the loop requests
-  if (!lead) barrier();
-  int t = 0;
-  for (; t + NS <= tu; t += NS) {
-    for_slots([&](auto sl) __attribute__((always_inline)) {
-      iter(t + decltype(sl)::value, sl, bool_c<false>{});
-    }, std::make_integer_sequence<int, NS>{});
-  }
-  // the last group: tiles past nkt - 1 only pad the group to NS slots;
-  // their matrix and softmax work is skipped (uniform branches), except the
-  // PV product of the last real tile
-  for (; t < nkt3; t += NS) {
-    for_slots([&](auto sl) __attribute__((always_inline)) {
-      if constexpr (decltype(sl)::value == 0) iter(t, sl, bool_c<true>{});
-      else iter_pad(t + decltype(sl)::value, sl);
-    }, std::make_integer_sequence<int, NS>{});
-  }
-  // the last matrix phase: PV of tile nkt3 - 1 (V slot NS-1), when it is real
-  if (!kSkipPad || nkt3 == nkt)
-    m_phase(nkt3, int_c<0>{}, bool_c<false>{}, bool_c<true>{}, bool_c<false>{});
-  if (lead) barrier();   // the trailing half's last barrier
-  // loads of the padding tiles past nkt3 may still be writing LDS: finish
-  // them before the workgroup's LDS is released
-  __builtin_amdgcn_s_waitcnt(0x0070);
-
-  // ---- epilogue: O = O^T / l, stored at the original token row ----
-  uint16_t* og = a.o + int64_t(b) * a.osb + int64_t(h) * a.osh + tok0 * a.osn;
-  float* const lse_out = a.lse ? a.lse + tok0 : nullptr;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = sum_pair32(lsum[qb]);
-    const float inv = 1.0f / lt;
-    const int r = int(qt) * C::BM + (wave * QB + qb) * 32 + l32;
-    if (r < L) {
-      const uint32_t i = skiparse_token(mode, uint32_t(r), j, divk, uint32_t(L));
-      uint16_t* p = og + int64_t(i) * a.osn;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const uint32_t w0 = pack_bf16(o[qb][db][4 * r4 + 0] * inv, o[qb][db][4 * r4 + 1] * inv);
-          const uint32_t w1 = pack_bf16(o[qb][db][4 * r4 + 2] * inv, o[qb][db][4 * r4 + 3] * inv);
-          *reinterpret_cast<uint2*>(p + 32 * db + 8 * r4 + 4 * g) = make_uint2(w0, w1);
+    if constexpr (ROPE_K) {
+      for_slots([&](auto sl) __attribute__((always_inline)) {
+        if constexpr (decltype(sl)::value < NS - 1) {
+          issue_tile_first(decltype(sl)::value, sl);
+          finish_tile(decltype(sl)::value, sl);
         }
-      if (lse_out && g == 0)
-        lse_out[(int64_t(b) * a.heads + h) * a.lse_ld + i] = (mref[qb] + __log2f(lt)) * kLn2;
+      }, std::make_integer_sequence<int, NS>{});
     }
+    __syncthreads();
+    if constexpr (TAB) tab_fetch(NS - 1);    // the first tile the loop requests
+    if (!lead) barrier();
+    int t = 0;
+    for (; t + NS <= tu; t += NS) {
+      for_slots([&](auto sl) __attribute__((always_inline)) {
+        iter(t + decltype(sl)::value, sl, bool_c<false>{});
+      }, std::make_integer_sequence<int, NS>{});
+    }
+    // the last group: tiles past nkt - 1 only pad the group to NS slots;
+    // their matrix and softmax work is skipped (uniform branches), except
+    // the PV product of the last real tile
+    for (; t < nkt3; t += NS) {
+      for_slots([&](auto sl) __attribute__((always_inline)) {
+        if constexpr (decltype(sl)::value == 0) iter(t, sl, bool_c<true>{});
+        else iter_pad(t + decltype(sl)::value, sl);
+      }, std::make_integer_sequence<int, NS>{});
+    }
+    // the last matrix phase: PV of tile nkt3 - 1 (V slot NS-1), when it is real
+    if (!kSkipPad || nkt3 == nkt)
+      m_phase(nkt3, int_c<0>{}, bool_c<false>{}, bool_c<true>{}, bool_c<false>{});
+    if (lead) barrier();   // the trailing half's last barrier
+    if (PERSIST && has_next) {
+      // the next tile's Q rows, in flight during this tile's stores (its
+      // first K/V tiles were requested in the last group)
+      load_q(unxt);
+    } else {
+      // loads of the padding tiles past nkt3 may still be writing LDS:
+      // finish them before the workgroup's LDS is released
+      __builtin_amdgcn_s_waitcnt(0x0070);
+    }
+
+    // ---- epilogue: O = O^T / l, stored at the original token row ----
+    const TileId cur = decode(ucur);
+    const AttnArgs* A = args();
+    uint16_t* og = A->o + int64_t(cur.b) * A->osb + int64_t(cur.h) * A->osh + tok0 * A->osn;
+    float* const lse_out = A->lse ? A->lse + tok0 : nullptr;
+    int le, ge;
+    lane_ids(le, ge);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float lt = sum_pair32(lsum[qb]);
+      const float inv = 1.0f / lt;
+      const int r = int(cur.qt) * C::BM + (wave * QB + qb) * 32 + le;
+      if (r < L) {
+        const uint32_t i = skiparse_token(mode, uint32_t(r), cur.j, divk, uint32_t(L));
+        uint16_t* p = og + int64_t(i) * A->osn;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const uint32_t w0 = pack_bf16(o[qb][db][4 * r4 + 0] * inv, o[qb][db][4 * r4 + 1] * inv);
+            const uint32_t w1 = pack_bf16(o[qb][db][4 * r4 + 2] * inv, o[qb][db][4 * r4 + 3] * inv);
+            *reinterpret_cast<uint2*>(p + 32 * db + 8 * r4 + 4 * ge) = make_uint2(w0, w1);
+          }
+        if (lse_out && ge == 0)
+          lse_out[(int64_t(cur.b) * A->heads + cur.h) * A->lse_ld + i] = (mref[qb] + __log2f(lt)) * kLn2;
+      }
+    }
+    if (!PERSIST || !has_next) break;
+    wn += gridDim.x >> 3;
+    ucur = unxt;
   }
 }
 
@@ -893,54 +1036,103 @@ static_assert(TileCfg<128, false>::NW * TileCfg<128, false>::QB ==
 // LDS of a workgroup, static plus dynamic, in bytes
 constexpr int kLdsBytes = 160 * 1024;
 
+// Workgroups of `kern` the current device runs at once: CUs times the
+// workgroups of `block` threads and `dyn` bytes of dynamic LDS that fit on
+// one CU, rounded down to a multiple of 8 (the XCDs), so that every XCD
+// holds as many; 0 when the runtime cannot tell.
+static int persist_grid(const void* kern, int block, size_t dyn) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, block, dyn) != hipSuccess) return 0;
+  return (cus * per_cu) & ~7;
+}
+
+// Static LDS of a kernel in bytes (-1 if the runtime cannot say), looked
+// up once per kernel
+template <typename K> static int static_lds_of(K kern) {
+  static std::atomic<int> bytes{-2};
+  if (bytes.load() == -2) {
+    hipFuncAttributes attr;
+    bytes.store(hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kern)) == hipSuccess
+                    ? int(attr.sharedSizeBytes) : -1);
+  }
+  return bytes.load();
+}
+
+// One launch of `kern` over the tiles of `a`: persistent (PERSIST
+// instances, when the tiles outnumber the workgroups the chip runs at once)
+// or one workgroup per tile.
+template <typename K>
+static hipError_t launch_tiles(K kern, bool persist, const AttnArgs& a, dim3 block, size_t dyn,
+                               hipStream_t s) {
+  int grid = a.total_tiles;
+  if (persist) {
+    const int g = persist_grid(reinterpret_cast<const void*>(kern), int(block.x), dyn);
+    if (g <= 0 || a.total_tiles <= g) return hipErrorNotSupported;   // caller takes the other
+    grid = g;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), block, dyn, s, a);
+  return hipGetLastError();
+}
+
+// Persistent launches are taken where they measured faster: head_dim 96
+// with fixed rows (full, block, Single and Group Skip with 64 % k == 0),
+// 2-4% on the 28,800-token workload's full and Skiparse k=4 attention and
+// 8% on its spatial (1,200-token) attention.  At head_dim 64 and 128 the
+// tile loop pushes the register budget (a few spills outside the key loop)
+// and the row-table instance runs more scalar work per key tile; there
+// they ran 3-8% slower, so those launches keep one workgroup per tile.
+template <int D> constexpr bool kPersistFixed = D == 96;
+
 template <int D, bool RQ, bool RK, bool PK>
-static hipError_t launch_drk(const AttnArgs& a, hipStream_t s) {
+static hipError_t launch_drk(const AttnArgs& a, bool persist, hipStream_t s) {
   using T = TileCfg<D, RK>;
-  dim3 grid(a.total_tiles), block(T::NW * 64);
+  const dim3 block(T::NW * 64);
   const bool fixed = a.mode <= MODE_BLOCK && (a.mode != MODE_GROUP || T::BN % int(a.divk.d) == 0);
   if (fixed) {
-    hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, T::NS, RQ, RK, true, PK,
-                                          false>), grid, block, 0, s, a);
-    return hipGetLastError();
+    if constexpr (!RK && !PK && kPersistFixed<D>) {
+      const hipError_t e = !persist ? hipErrorNotSupported : launch_tiles(
+          attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, T::NS, RQ, RK, true, PK, false, true>,
+          true, a, block, 0, s);
+      if (e != hipErrorNotSupported) return e;
+    }
+    return launch_tiles(
+        attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, T::NS, RQ, RK, true, PK, false, false>,
+        false, a, block, 0, s);
   }
   // per-row remap: with Q rotated in the loader and K already rotated (the
   // fast path), rows come from an LDS row table when it fits beside the
   // kernel's static LDS
   if constexpr (RQ && !RK && !PK) {
-    auto kern = attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, (D == 96 ? OSP_TAB_NS : 3), RQ, RK,
-                                  false, PK, true>;
-    static std::atomic<int> static_lds{-1};
-    if (static_lds.load() < 0) {
-      hipFuncAttributes attr;
-      if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kern)) != hipSuccess)
-        return hipErrorInvalidDeviceFunction;
-      static_lds.store(int(attr.sharedSizeBytes));
-    }
+    constexpr int NS = D == 96 ? OSP_TAB_NS : 3;
     const int64_t tab = int64_t(a.seq_len) * 4;
-    if (static_lds.load() + tab <= kLdsBytes) {
-      hipLaunchKernelGGL(kern, grid, block, size_t(tab), s, a);
-      return hipGetLastError();
-    }
+    auto kern = attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, NS, RQ, RK, false, PK, true, false>;
+    const int lds = static_lds_of(kern);
+    if (lds < 0) return hipErrorInvalidDeviceFunction;
+    if (lds + tab <= kLdsBytes) return launch_tiles(kern, false, a, block, size_t(tab), s);
   }
-  hipLaunchKernelGGL((attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, 3, RQ, RK, false, PK, false>),
-                     grid, block, 0, s, a);
-  return hipGetLastError();
+  return launch_tiles(
+      attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, 3, RQ, RK, false, PK, false, false>, false, a,
+      block, 0, s);
 }
 
 template <int D, bool PK>
-static hipError_t launch_d(const AttnArgs& a, int rope_q, int rope_k, hipStream_t s) {
-  if (rope_q && rope_k) return launch_drk<D, true, true, PK>(a, s);
-  if (rope_q) return launch_drk<D, true, false, PK>(a, s);
-  if (rope_k) return launch_drk<D, false, true, PK>(a, s);
-  return launch_drk<D, false, false, PK>(a, s);
+static hipError_t launch_d(const AttnArgs& a, int rope_q, int rope_k, bool persist,
+                           hipStream_t s) {
+  if (rope_q && rope_k) return launch_drk<D, true, true, PK>(a, persist, s);
+  if (rope_q) return launch_drk<D, true, false, PK>(a, persist, s);
+  if (rope_k) return launch_drk<D, false, true, PK>(a, persist, s);
+  return launch_drk<D, false, false, PK>(a, persist, s);
 }
 
-hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_q, int rope_k, hipStream_t s) {
+hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_q, int rope_k, int persist,
+                         hipStream_t s) {
   if (a.seq_len <= kShortRows) return launch_attn3d_short(a, head_dim, rope_q, rope_k, s);
   switch (head_dim) {
-    case 64: return launch_d<64, false>(a, rope_q, rope_k, s);
-    case 96: return launch_d<96, false>(a, rope_q, rope_k, s);
-    case 128: return launch_d<128, false>(a, rope_q, rope_k, s);
+    case 64: return launch_d<64, false>(a, rope_q, rope_k, persist != 0, s);
+    case 96: return launch_d<96, false>(a, rope_q, rope_k, persist != 0, s);
+    case 128: return launch_d<128, false>(a, rope_q, rope_k, persist != 0, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -948,9 +1140,9 @@ hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_q, int rope_k, hipS
 hipError_t launch_attn3d_packed(const AttnArgs& a, int head_dim, int rope_q, int rope_k,
                                 hipStream_t s) {
   switch (head_dim) {
-    case 64: return launch_d<64, true>(a, rope_q, rope_k, s);
-    case 96: return launch_d<96, true>(a, rope_q, rope_k, s);
-    case 128: return launch_d<128, true>(a, rope_q, rope_k, s);
+    case 64: return launch_d<64, true>(a, rope_q, rope_k, false, s);
+    case 96: return launch_d<96, true>(a, rope_q, rope_k, false, s);
+    case 128: return launch_d<128, true>(a, rope_q, rope_k, false, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -176,7 +176,7 @@ osp_status check_attn(const osp_attn3d_desc* d, int32_t mode, int32_t k, int32_t
                       Shape* s) {
   osp_status st = check_desc(d, true, s);
   if (st) return st;
-  if (flags & ~int32_t(OSP_FUSE_ROPE_Q | OSP_FUSE_ROPE_K))
+  if (flags & ~int32_t(OSP_FUSE_ROPE_Q | OSP_FUSE_ROPE_K | OSP_ONE_TILE_PER_WORKGROUP))
     return fail(OSP_ERR_PARAM, "unknown flags 0x%x", flags);
   st = check_mode(d, s->n_tokens, mode, k);
   if (st) return st;
@@ -590,6 +590,7 @@ osp_status osp_attn3d_fwd(const osp_attn3d_desc* desc, int32_t mode, int32_t spa
   if (a.total_tiles == 0) return ok();
   hipError_t e = osp::launch_attn3d(a, desc->head_dim, (flags & OSP_FUSE_ROPE_Q) ? 1 : 0,
                                     (flags & OSP_FUSE_ROPE_K) ? 1 : 0,
+                                    (flags & OSP_ONE_TILE_PER_WORKGROUP) ? 0 : 1,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(e, "attn3d_fwd launch");
   return ok();

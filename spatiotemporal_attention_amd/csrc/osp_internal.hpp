@@ -53,7 +53,11 @@ int attn_keys_per_tile(int head_dim);
 // Subsequences of at most kShortRows rows go to the one-wave-per-unit
 // kernel (launch_attn3d_short), longer ones to the flash kernel.
 constexpr int kShortRows = 64;
-hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_q, int rope_k, hipStream_t s);
+// persist: a call with more query tiles than the GPU holds workgroups at
+// once may take a persistent launch (one workgroup per slot, each walking a
+// list of tiles).
+hipError_t launch_attn3d(AttnArgs& a, int head_dim, int rope_q, int rope_k, int persist,
+                         hipStream_t s);
 hipError_t launch_attn3d_short(const AttnArgs& a, int head_dim, int rope_q, int rope_k,
                                hipStream_t s);
 // One flash-kernel launch over a.n_pack segments (each longer than kShortRows).

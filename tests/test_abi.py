@@ -78,7 +78,8 @@ def _code(desc, mode="full", k=1, flags=1):
     ({}, "skiparse_single", 3, 1, SHAPE),          # 320 % 3 != 0
     ({}, "skiparse_single", 0, 1, PARAM),
     ({}, 7, 1, 1, PARAM),
-    ({}, "full", 1, 4, PARAM),                     # unknown flag bit
+    ({}, "full", 1, 8, PARAM),                     # unknown flag bit
+    ({}, "full", 1, 5, OK),                        # one tile per workgroup
     ({"n_text": 2, "grid": (2, 3, 53)}, "skiparse_single", 2, 1, UNSUP),
     ({"n_text": 226, "grid": (13, 30, 45), "heads": 48}, "full", 1, 1, OK),
     ({"head_dim": 80, "rope_split": (16, 32, 32)}, "full", 1, 1, UNSUP),
