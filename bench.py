@@ -607,7 +607,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": "attn3d_fwd_kernel<D=96, QB=1, BN=64, NW=8, OCC=2, rope_q, fixed_rows>",
+                     "kernel": "attn3d_fwd_kernel<D=96, QB=1, BN=64, NW=8, OCC=2, NS=4, rope_q, fixed_rows, "
+                               "persistent>",
                      "flop_per_launch": f_full, "ms_per_launch": round(ms_launch, 4),
                      "ms_median": round(ms_med, 4), "ms_min": round(ms_min, 4)},
         "kernel_source_hash": kernel_source_hash(),

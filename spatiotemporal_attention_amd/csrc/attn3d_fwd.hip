@@ -639,8 +639,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   uint32_t unxt = ucur;
   const uint16_t* sb = nullptr;
   if constexpr (PERSIST) sb = stream_base(ucur);
-  auto issue_tile = [&](int kt, auto slot) __attribute__((always_inline)) {
-    if constexpr (PERSIST) {
+  // NEAR_END: kt may reach nkt3 (the loop's last two groups); earlier
+  // groups request the current tile's tiles only
+  auto issue_tile = [&](int kt, auto slot, auto near_end) __attribute__((always_inline)) {
+    if constexpr (PERSIST && !decltype(near_end)::value) {
+      if constexpr (TAB) {
+        if (lead) dma_tile_tab(sb, kt, kslot(slot), 0u, kt + 1);
+        else dma_tile_tab(sb, kt, vslot(slot), 0u, kt + 1);
+      } else {
+        if (lead) dma_tile(sb, kt, kslot(slot), 0u);
+        else dma_tile(sb, kt, vslot(slot), 0u);
+      }
+    } else if constexpr (PERSIST) {
       const bool nx = has_next && kt >= nkt3;
       if (has_next && kt == nkt3) sb = stream_base(unxt);
       const int kk = nx ? kt - nkt3 : kt;
@@ -834,11 +844,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   const int tu = nkt - (ragged ? 1 : 0);
   // one iteration (two phases) for tile t in slot P = t % NS; MASKED: mask
   // keys past the end (correct for any tile; used for the last groups)
-  auto iter = [&](int t, auto slot, auto masked) __attribute__((always_inline)) {
+  auto iter = [&](int t, auto slot, auto masked, auto near_end) __attribute__((always_inline)) {
     constexpr int P = decltype(slot)::value;
     m_phase(t, slot, bool_c<true>{}, bool_c<true>{}, masked);
     barrier();
-    issue_tile(t + NS - 1, int_c<(P + NS - 1) % NS>{});
+    issue_tile(t + NS - 1, int_c<(P + NS - 1) % NS>{}, near_end);
     softmax_phase(s, pb, t == 0);
     finish_tile(t + NS - 1, int_c<(P + NS - 1) % NS>{});
     loads_done();
@@ -855,11 +865,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
   auto iter_pad = [&](int t, auto slot) __attribute__((always_inline)) {
     constexpr int P = decltype(slot)::value;
     if (!kSkipPad || t < nkt) {
-      iter(t, slot, bool_c<true>{});
+      iter(t, slot, bool_c<true>{}, bool_c<true>{});
     } else {
       if (t == nkt) m_phase(t, slot, bool_c<false>{}, bool_c<true>{}, bool_c<false>{});
       barrier();
-      issue_tile(t + NS - 1, int_c<(P + NS - 1) % NS>{});
+      issue_tile(t + NS - 1, int_c<(P + NS - 1) % NS>{}, bool_c<true>{});
       finish_tile(t + NS - 1, int_c<(P + NS - 1) % NS>{});
       loads_done();
       barrier();
@@ -904,17 +914,24 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     if constexpr (TAB) tab_fetch(NS - 1);    // the first tile the loop requests
     if (!lead) barrier();
     int t = 0;
-    for (; t + NS <= tu; t += NS) {
+    auto group = [&](auto near_end) __attribute__((always_inline)) {
       for_slots([&](auto sl) __attribute__((always_inline)) {
-        iter(t + decltype(sl)::value, sl, bool_c<false>{});
+        iter(t + decltype(sl)::value, sl, bool_c<false>{}, near_end);
       }, std::make_integer_sequence<int, NS>{});
+    };
+    if constexpr (PERSIST) {
+      // the groups whose requests stay below nkt3, then at most one more
+      for (; t + 2 * NS <= tu; t += NS) group(bool_c<false>{});
+      for (; t + NS <= tu; t += NS) group(bool_c<true>{});
+    } else {
+      for (; t + NS <= tu; t += NS) group(bool_c<true>{});
     }
     // the last group: tiles past nkt - 1 only pad the group to NS slots;
     // their matrix and softmax work is skipped (uniform branches), except
     // the PV product of the last real tile
     for (; t < nkt3; t += NS) {
       for_slots([&](auto sl) __attribute__((always_inline)) {
-        if constexpr (decltype(sl)::value == 0) iter(t, sl, bool_c<true>{});
+        if constexpr (decltype(sl)::value == 0) iter(t, sl, bool_c<true>{}, bool_c<true>{});
         else iter_pad(t + decltype(sl)::value, sl);
       }, std::make_integer_sequence<int, NS>{});
     }
@@ -1083,7 +1100,10 @@ static hipError_t launch_tiles(K kern, bool persist, const AttnArgs& a, dim3 blo
 // tile loop pushes the register budget (a few spills outside the key loop)
 // and the row-table instance runs more scalar work per key tile; there
 // they ran 3-8% slower, so those launches keep one workgroup per tile.
-template <int D> constexpr bool kPersistFixed = D == 96;
+#ifndef OSP_PERSIST_ALL_D
+#define OSP_PERSIST_ALL_D 0
+#endif
+template <int D> constexpr bool kPersistFixed = OSP_PERSIST_ALL_D || D == 96;
 
 template <int D, bool RQ, bool RK, bool PK>
 static hipError_t launch_drk(const AttnArgs& a, bool persist, hipStream_t s) {
