@@ -92,7 +92,7 @@ typedef enum {
 #define OSP_FUSE_ROPE 3    /* both                                           */
 #define OSP_ONE_TILE_PER_WORKGROUP 4
                            /* launch one workgroup per query tile.  Without
-                              it, a call at head_dim 96 whose rows map to
+                              it, a call at head_dim 64 or 96 whose rows map to
                               tokens with a fixed stride (full, BLOCK,
                               SKIPARSE_SINGLE, SKIPARSE_GROUP with 64 % k ==
                               0) and with more query tiles than the GPU holds

@@ -366,11 +366,29 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
     for (int t = 0; t < C::DPW; ++t)
       tab_nx[t + 1] = row_tab[min(r0 + uint32_t(dm_row[t]), uint32_t(L - 1))];
   };
+  // The DMA descriptor's base address is the same in every lane.  Where the
+  // compiler cannot prove it, it wraps each DMA in a loop over the distinct
+  // values.  The persistent instances at head_dim 64 and 128 hold the
+  // stream base in vector registers and got such loops in the key loop;
+  // there the address is read from the first lane, which tells the
+  // compiler.  Elsewhere that read moves the address arithmetic to vector
+  // instructions and measured 1-2% slower (no such loop in their key
+  // loops), so it is left out.
+  auto wave_ptr = [](const uint16_t* p) __attribute__((always_inline)) {
+    if constexpr (PERSIST && D != 96) {
+      const uint64_t v = reinterpret_cast<uint64_t>(p);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+      return reinterpret_cast<uint16_t*>((uint64_t(hi) << 32) | lo);
+    } else {
+      return const_cast<uint16_t*>(p);
+    }
+  };
   auto dma_tile_tab = [&](const uint16_t* src, int kt, uint16_t* dst, uint32_t cj, int fetch_kt)
       __attribute__((always_inline)) {
     const uint32_t base = tab_nx[0];
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(src + int64_t(base + cj) * a_sn), (short)0, kRecords, 0x00020000);
+        wave_ptr(src + int64_t(base + cj) * a_sn), (short)0, kRecords, 0x00020000);
 #pragma unroll
     for (int t = 0; t < C::DPW; ++t) {
       int32_t off = int32_t((tab_nx[t + 1] - base) * sn2 + 16u * uint32_t(dm_col[t]));
@@ -384,7 +402,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn3d_fwd_kernel(const AttnArgs
       __attribute__((always_inline)) {
     const uint32_t i0 = tile_first(kt, jj);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(src + int64_t(i0) * a_sn), (short)0, kRecords, 0x00020000);
+        wave_ptr(src + int64_t(i0) * a_sn), (short)0, kRecords, 0x00020000);
     // lattice position of the tile's first row, and the subsequence's (jh, jw)
     const uint32_t r0 = uint32_t(kt * BN);
     const uint32_t t0 = fdiv(r0, divk.plane);
@@ -1093,17 +1111,21 @@ static hipError_t launch_tiles(K kern, bool persist, const AttnArgs& a, dim3 blo
   return hipGetLastError();
 }
 
-// Persistent launches are taken where they measured faster: head_dim 96
-// with fixed rows (full, block, Single and Group Skip with 64 % k == 0),
-// 2-4% on the 28,800-token workload's full and Skiparse k=4 attention and
-// 8% on its spatial (1,200-token) attention.  At head_dim 64 and 128 the
-// tile loop pushes the register budget (a few spills outside the key loop)
-// and the row-table instance runs more scalar work per key tile; there
-// they ran 3-8% slower, so those launches keep one workgroup per tile.
+// Persistent launches are taken where they measured faster, with fixed
+// rows (full, block, Single and Group Skip with k dividing the key tile):
+// at head_dim 96, 2-4% on the 28,800-token workload's full and Skiparse
+// k=4 attention and 8% on its spatial (1,200-token) attention; at head_dim
+// 64, 2.4% on CogVideoX's 17,776 tokens.  At head_dim 128 it measured
+// within the noise (+0.4%), and the row-table instance 1% slower than one
+// workgroup per tile: those launches keep one workgroup per tile.
 #ifndef OSP_PERSIST_ALL_D
 #define OSP_PERSIST_ALL_D 0
 #endif
-template <int D> constexpr bool kPersistFixed = OSP_PERSIST_ALL_D || D == 96;
+template <int D> constexpr bool kPersistFixed = OSP_PERSIST_ALL_D || D == 96 || D == 64;
+#ifndef OSP_PERSIST_TAB
+#define OSP_PERSIST_TAB 0
+#endif
+template <int D> constexpr bool kPersistTab = OSP_PERSIST_TAB && D == 96;
 
 template <int D, bool RQ, bool RK, bool PK>
 static hipError_t launch_drk(const AttnArgs& a, bool persist, hipStream_t s) {
@@ -1127,6 +1149,14 @@ static hipError_t launch_drk(const AttnArgs& a, bool persist, hipStream_t s) {
   if constexpr (RQ && !RK && !PK) {
     constexpr int NS = D == 96 ? OSP_TAB_NS : 3;
     const int64_t tab = int64_t(a.seq_len) * 4;
+    if constexpr (kPersistTab<D>) {
+      auto pkern = attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, NS, RQ, RK, false, PK, true, true>;
+      const int plds = static_lds_of(pkern);
+      if (persist && plds >= 0 && plds + tab <= kLdsBytes) {
+        const hipError_t e = launch_tiles(pkern, true, a, block, size_t(tab), s);
+        if (e != hipErrorNotSupported) return e;
+      }
+    }
     auto kern = attn3d_fwd_kernel<D, T::QB, T::BN, T::NW, T::OCC, NS, RQ, RK, false, PK, true, false>;
     const int lds = static_lds_of(kern);
     if (lds < 0) return hipErrorInvalidDeviceFunction;

@@ -1,15 +1,15 @@
-"""GPU tests of the persistent forward launch: a call at head_dim 96 with
-fixed-row remaps and more query tiles than the GPU holds workgroups at
-once takes one workgroup per slot, each walking its XCD's list of tiles.
+"""GPU tests of the persistent forward launch: a call at head_dim 64 or 96
+with fixed-row remaps and more query tiles than the GPU holds workgroups
+at once takes one workgroup per slot, each walking its XCD's list of tiles.
 Every case is run both ways (the default and OSP_ONE_TILE_PER_WORKGROUP)
 with O and LSE filled with NaN first, and the two results must be the same
 bits and fully written: the per-tile arithmetic is the same, only the
 launch differs.  The persistent cases cover full, block, Single and Group
 Skip, tiles left over after the XCD split (one more tile for some
 workgroups), subsequences shorter than the slot count of key tiles, and Q
-already rotated; the row-table, head_dim 64 and head_dim 128 cases take one
-tile per workgroup either way and check that the flag changes nothing
-there.  One case is also checked against the fp64 oracle on sampled rows.
+already rotated, and head_dim 64 with text tokens in front; the row-table
+and head_dim 128 cases take one tile per workgroup either way and check
+that the flag changes nothing there.  One case is also checked against the fp64 oracle on sampled rows.
 Needs an MI355X."""
 import numpy as np
 import pytest
