@@ -7,7 +7,8 @@ bits and fully written: the per-tile arithmetic is the same, only the
 launch differs.  The persistent cases cover full, block, Single and Group
 Skip, tiles left over after the XCD split (one more tile for some
 workgroups), subsequences shorter than the slot count of key tiles, and Q
-already rotated, and head_dim 64 with text tokens in front; the row-table
+already rotated, head_dim 64 with text tokens in front and with Skiparse,
+head_dim 96 with text tokens, batch 2 and a strided output; the row-table
 and head_dim 128 cases take one tile per workgroup either way and check
 that the flag changes nothing there.  One case is also checked against the fp64 oracle on sampled rows.
 Needs an MI355X."""
@@ -39,12 +40,17 @@ CASES = {
     # head_dim 64 with text tokens in front; head_dim 128
     "cogvideox_joint": ((13, 30, 45), 226, 48, 64, (16, 24, 24), "full", 1, True),
     "osp15_d128": ((16, 36, 64), 0, 24, 128, (32, 48, 48), "full", 1, True),
+    # head_dim 96 with text tokens in front (ragged last query and key tiles)
+    "d96_text": ((12, 30, 40), 77, 24, 96, (32, 32, 32), "full", 1, True),
+    # head_dim 64 Skiparse: Group Skip k=4 and Single Skip k=2 (fixed rows at 32-key tiles)
+    "d64_group_k4": ((13, 32, 44), 0, 24, 64, (16, 24, 24), "skiparse_group", 4, True),
+    "d64_single_k2": ((13, 30, 45), 0, 16, 64, (16, 24, 24), "skiparse_single", 2, True),
 }
 
 
-def _run(q, k, v, grid, n_text, mode, sk, split, fuse, one_tile):
+def _run(q, k, v, grid, n_text, mode, sk, split, fuse, one_tile, out=None):
     b, n, h, _ = q.shape
-    o = torch.full_like(q, float("nan"))
+    o = torch.full_like(q, float("nan")) if out is None else out.fill_(float("nan"))
     lse = torch.full((b, h, n), float("nan"), dtype=torch.float32, device=q.device)
     osp.osp_attn3d_fwd(q, k, v, grid=grid, n_text=n_text, mode=mode, sparse_k=sk,
                        rope_split=split, fuse_rope=fuse, out=o, lse=lse,
@@ -90,3 +96,28 @@ def test_persistent_back_to_back_calls():
     a2, la2 = _run(q, k, v, grid, 0, "full", 1, split, True, True)
     assert torch.equal(a1, a2) and torch.equal(la1, la2)
     assert torch.equal(b1, b2) and torch.equal(lb1, lb2)
+
+
+def test_persistent_batch_and_strided_output():
+    # batch 2 (the tile list spans both batches) with O written into a
+    # strided view (every other head of a wider tensor): both launches give
+    # the same bits, the untouched heads stay as they were, and sampled rows
+    # of the second batch match the oracle
+    grid, split = (12, 30, 40), (32, 32, 32)
+    shape = (2, 14400, 24, 96)
+    note(f"persistent batch 2, strided O: shape={shape}")
+    cpu, (q, k, v) = qkv_for((11, 77), shape)
+    wide = [torch.zeros((2, 14400, 48, 96), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    res = []
+    for one_tile, w in zip((False, True), wide):
+        res.append(_run(q, k, v, grid, 0, "full", 1, split, True, one_tile, out=w[:, :, 0::2]))
+    (o1, l1), (o2, l2) = res
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for w in wide:
+        assert not w[:, :, 1::2].any(), "heads outside the view were written"
+    rows = workloads.sample_rows(12, 14400, 96)
+    want_o, want_l = oracle_attn(tuple(t[1:2] for t in cpu), grid=grid, n_text=0, mode="full",
+                                 sparse_k=1, rope_split=split, rows=rows)
+    idx = torch.from_numpy(rows).cuda()
+    assert_parity(to_np(o1[1:2].index_select(1, idx)), want_o, f"batch 1 ({len(rows)} rows)")
+    assert np.abs(to_np(l1[1:2].index_select(2, idx)) - want_l).max() <= LSE_ABS
