@@ -8,7 +8,8 @@ launch differs.  The persistent cases cover full, block, Single and Group
 Skip, tiles left over after the XCD split (one more tile for some
 workgroups), subsequences shorter than the slot count of key tiles, and Q
 already rotated, head_dim 64 with text tokens in front and with Skiparse,
-head_dim 96 with text tokens, batch 2 and a strided output; the row-table
+head_dim 96 with text tokens, batch 2 and a strided output, and units of
+one query tile with fewer key tiles than prefetch slots; the row-table
 and head_dim 128 cases take one tile per workgroup either way and check
 that the flag changes nothing there.  One case is also checked against the fp64 oracle on sampled rows.
 Needs an MI355X."""
@@ -45,6 +46,12 @@ CASES = {
     # head_dim 64 Skiparse: Group Skip k=4 and Single Skip k=2 (fixed rows at 32-key tiles)
     "d64_group_k4": ((13, 32, 44), 0, 24, 64, (16, 24, 24), "skiparse_group", 4, True),
     "d64_single_k2": ((13, 30, 45), 0, 16, 64, (16, 24, 24), "skiparse_single", 2, True),
+    # one query tile per unit and fewer key tiles than the prefetch slots:
+    # 130-token windows (three key tiles, the last with 2 keys), and 65-token
+    # windows, the shortest the flash kernel takes, at head_dim 96 and 64
+    "window_130": ((10, 26, 50), 0, 24, 96, (32, 32, 32), "block", 100, True),
+    "window_65": ((5, 13, 40), 0, 48, 96, (32, 32, 32), "block", 40, True),
+    "window_65_d64": ((5, 13, 40), 0, 48, 64, (16, 24, 24), "block", 40, True),
 }
 
 
@@ -72,7 +79,7 @@ def test_persistent_equals_one_tile_per_workgroup(name):
     o2, l2 = _run(q, k, v, grid, n_text, mode, sk, split, fuse, True)
     assert torch.equal(o1, o2), "O differs between the two launches"
     assert torch.equal(l1, l2), "LSE differs between the two launches"
-    if name == "one_head_258_tiles":
+    if name in ("one_head_258_tiles", "window_130", "window_65_d64"):
         rows = workloads.sample_rows(11, n, 256)
         want_o, want_l = oracle_attn(cpu, grid=grid, n_text=n_text, mode=mode, sparse_k=sk,
                                      rope_split=split, rows=rows)
